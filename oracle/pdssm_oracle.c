@@ -1,0 +1,264 @@
+/*
+ * pdssm_oracle.c -- plain fp64 reference for the Flash PD-SSM forward scan.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark load this; the library and its kernels never
+ * do, and the two share no code.  It is deliberately slow and sequential: one
+ * time step after another, exactly as the recurrence is defined, in double
+ * precision (complex128 when the state is complex).
+ *
+ * What is computed (source: "Flash PD-SSM: Memory-Optimized Structured Sparse
+ * State-Space Models", gist.science explainer, Technical Summary):
+ *
+ *   - Methodology, "1. Novel Selection Mechanism (Hard Selection)": a
+ *     dictionary of K sparse matrices is fixed in advance; at every step the
+ *     K scores pick one matrix by argmax, and that matrix is used as is.  The
+ *     selected matrix is a one-hot column selector: column j of P holds a
+ *     single 1, in row pi[j].  We store P as the index map pi.
+ *   - Methodology, "3. Hardware-Aware Implementation", Phase A: the
+ *     recurrence within a chunk is an ordinary sequential recurrence; this
+ *     file runs it over the whole sequence.
+ *   - The transition is A_t = P_t D_t with D_t diagonal, so
+ *         x_t = P_t (d_t * x_{t-1}) + b_t,   y_t = Re( sum_i c_t[i] x_t[i] ).
+ *     The pages name the structure (P times D) but print no formula; this
+ *     form, the readout without conjugation, and the lowest-index tie-break
+ *     of the argmax are the readings this build takes.
+ *
+ * Inputs are read as the exact double value of the stored bits (fp32, bf16,
+ * int16, int32).  Outputs are double.  Index ranges are asserted: a
+ * selection outside [0,K) or a map entry outside [0,N) returns an error.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Storage kinds of the selection input. */
+enum { ORC_SEL_I32 = 0, ORC_SEL_I16 = 1, ORC_LOGITS_F32 = 2, ORC_LOGITS_BF16 = 3 };
+
+/* Error codes. */
+enum { ORC_OK = 0, ORC_BAD_SEL = -1, ORC_BAD_MAP = -2, ORC_BAD_ARG = -3 };
+
+/* bf16 is the upper half of an fp32 bit pattern. */
+static double bf16_value(uint16_t bits)
+{
+    uint32_t w = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return (double)f;
+}
+
+/* Element i of an fp32 or bf16 array, as an exact double. */
+static double load_value(const void *base, int64_t i, int is_bf16)
+{
+    if (is_bf16)
+        return bf16_value(((const uint16_t *)base)[i]);
+    return (double)((const float *)base)[i];
+}
+
+/*
+ * Hard selection for one step: index mode reads the stored index; logits
+ * mode takes the argmax over the K scores.  Ties go to the lowest index
+ * (the first maximum), -0 equals +0 under ordinary comparison, and a NaN
+ * score counts as larger than every number (the first NaN wins).
+ */
+static int64_t select_step(const void *src, int sel_kind, int64_t step, int32_t K)
+{
+    if (sel_kind == ORC_SEL_I32)
+        return ((const int32_t *)src)[step];
+    if (sel_kind == ORC_SEL_I16)
+        return ((const int16_t *)src)[step];
+    int is_bf16 = (sel_kind == ORC_LOGITS_BF16);
+    int64_t row = step * (int64_t)K;
+    int64_t best = 0;
+    double best_v = load_value(src, row, is_bf16);
+    for (int32_t k = 1; k < K; ++k) {
+        double v = load_value(src, row + k, is_bf16);
+        int take;
+        if (isnan(best_v))
+            take = 0;
+        else if (isnan(v))
+            take = 1;
+        else
+            take = v > best_v;
+        if (take) {
+            best = k;
+            best_v = v;
+        }
+    }
+    return best;
+}
+
+static void set_error(volatile int *err, int code)
+{
+    if (*err == ORC_OK)
+        *err = code;
+}
+
+/* sel_out[B,H,L] = the selected dictionary entry of every step. */
+int pdssm_oracle_select(const void *src, int sel_kind, int64_t B, int64_t H, int64_t L, int32_t K,
+                        int32_t *sel_out)
+{
+    if (!src || !sel_out || B < 0 || H < 0 || L < 0 || K < 1 || sel_kind < 0 || sel_kind > 3)
+        return ORC_BAD_ARG;
+    int64_t steps = B * H * L;
+    for (int64_t s = 0; s < steps; ++s) {
+        int64_t k = select_step(src, sel_kind, s, K);
+        if (k < 0 || k >= K)
+            return ORC_BAD_SEL;
+        sel_out[s] = (int32_t)k;
+    }
+    return ORC_OK;
+}
+
+/*
+ * The forward scan.  For every sequence (b,h), starting from x0[b,h] (zero
+ * when x0 is NULL), for t = 0..L-1:
+ *     k   = selected entry of step t
+ *     pi  = dict_idx[h,k,:]
+ *     x'  = 0;  for j = 0..N-1 (ascending):  x'[pi[j]] += diag[t,j] * x[j]
+ *     x'  += b[t,:];  x = x'
+ *     y[t] = Re( sum_{i ascending} c[t,i] * x[i] )
+ * and x_final[b,h] = x after the last step.
+ *
+ * Layouts: diag, b, c are [B,H,L,N] (real) or [B,H,L,N,2] (complex,
+ * interleaved re/im); diag, x0 are fp32, b and c are fp32 or bf16
+ * (bc_bf16).  y_out is double [B,H,L]; xfinal_out (nullable) is double
+ * [B,H,N] or [B,H,N,2].  Sequences are independent; nthreads > 0 runs that
+ * many of them at once (arithmetic unchanged).
+ */
+int pdssm_oracle_scan(const void *src, int sel_kind, const int32_t *dict_idx, const float *diag,
+                      const void *b, const void *c, const float *x0, int is_complex, int bc_bf16,
+                      int64_t B, int64_t H, int64_t L, int32_t N, int32_t K, double *y_out,
+                      double *xfinal_out, int nthreads)
+{
+    if (!src || !dict_idx || !diag || !b || !c || !y_out || B < 0 || H < 0 || L < 0 || N < 1 ||
+        K < 1 || sel_kind < 0 || sel_kind > 3)
+        return ORC_BAD_ARG;
+    const int ncomp = is_complex ? 2 : 1;
+    const int64_t BH = B * H;
+    volatile int err = ORC_OK;
+    (void)nthreads;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t s = 0; s < BH; ++s) {
+        const int64_t h = s % H;
+        double *x = (double *)calloc((size_t)N * 2, sizeof(double));   /* re, im */
+        double *xn = (double *)calloc((size_t)N * 2, sizeof(double));
+        if (!x || !xn) {
+            set_error(&err, ORC_BAD_ARG);
+            free(x);
+            free(xn);
+            continue;
+        }
+        if (x0) {
+            for (int32_t i = 0; i < N; ++i) {
+                x[2 * i] = x0[(s * N + i) * ncomp];
+                x[2 * i + 1] = is_complex ? x0[(s * N + i) * ncomp + 1] : 0.0;
+            }
+        }
+        for (int64_t t = 0; t < L && err == ORC_OK; ++t) {
+            const int64_t step = s * L + t;
+            const int64_t k = select_step(src, sel_kind, step, K);
+            if (k < 0 || k >= K) {
+                set_error(&err, ORC_BAD_SEL);
+                break;
+            }
+            const int32_t *pi = dict_idx + (h * K + k) * N;
+            const int64_t row = step * N;   /* first element of step t */
+
+            for (int32_t i = 0; i < 2 * N; ++i)
+                xn[i] = 0.0;
+            for (int32_t j = 0; j < N; ++j) {
+                const int32_t i = pi[j];
+                if (i < 0 || i >= N) {
+                    set_error(&err, ORC_BAD_MAP);
+                    break;
+                }
+                const double dr = diag[(row + j) * ncomp];
+                const double di = is_complex ? diag[(row + j) * ncomp + 1] : 0.0;
+                const double xr = x[2 * j], xi = x[2 * j + 1];
+                xn[2 * i] += dr * xr - di * xi;
+                xn[2 * i + 1] += dr * xi + di * xr;
+            }
+            for (int32_t i = 0; i < N; ++i) {
+                xn[2 * i] += load_value(b, (row + i) * ncomp, bc_bf16);
+                if (is_complex)
+                    xn[2 * i + 1] += load_value(b, (row + i) * ncomp + 1, bc_bf16);
+            }
+            double *tmp = x;
+            x = xn;
+            xn = tmp;
+
+            double acc = 0.0;
+            for (int32_t i = 0; i < N; ++i) {
+                const double cr = load_value(c, (row + i) * ncomp, bc_bf16);
+                const double ci = is_complex ? load_value(c, (row + i) * ncomp + 1, bc_bf16) : 0.0;
+                acc += cr * x[2 * i] - ci * x[2 * i + 1];
+            }
+            y_out[step] = acc;
+        }
+        if (xfinal_out) {
+            for (int32_t i = 0; i < N; ++i) {
+                xfinal_out[(s * N + i) * ncomp] = x[2 * i];
+                if (is_complex)
+                    xfinal_out[(s * N + i) * ncomp + 1] = x[2 * i + 1];
+            }
+        }
+        free(x);
+        free(xn);
+    }
+    return err;
+}
+
+/*
+ * The total transition of every sequence, A_{L-1} ... A_1 A_0, which is again
+ * a one-hot column selector times a diagonal (the product of such matrices
+ * keeps one non-zero per column).  Written per source column j: follow j
+ * through the steps,
+ *     d_total[j] = prod_t diag[t, p_t(j)],   pi_total[j] = p_L(j),
+ * where p_0(j) = j and p_{t+1}(j) = pi_t[p_t(j)].
+ * pi_out is int32 [B,H,N]; d_out is double [B,H,N] or [B,H,N,2].
+ */
+int pdssm_oracle_compose(const void *src, int sel_kind, const int32_t *dict_idx, const float *diag,
+                         int is_complex, int64_t B, int64_t H, int64_t L, int32_t N, int32_t K,
+                         int32_t *pi_out, double *d_out)
+{
+    if (!src || !dict_idx || !diag || !pi_out || !d_out || B < 0 || H < 0 || L < 0 || N < 1 ||
+        K < 1 || sel_kind < 0 || sel_kind > 3)
+        return ORC_BAD_ARG;
+    const int ncomp = is_complex ? 2 : 1;
+    const int64_t BH = B * H;
+    for (int64_t s = 0; s < BH; ++s) {
+        const int64_t h = s % H;
+        for (int32_t j = 0; j < N; ++j) {
+            int32_t p = j;
+            double dr = 1.0, di = 0.0;
+            for (int64_t t = 0; t < L; ++t) {
+                const int64_t step = s * L + t;
+                const int64_t k = select_step(src, sel_kind, step, K);
+                if (k < 0 || k >= K)
+                    return ORC_BAD_SEL;
+                const int64_t e = (step * N + p) * ncomp;
+                const double er = diag[e];
+                const double ei = is_complex ? diag[e + 1] : 0.0;
+                const double nr = er * dr - ei * di;
+                const double ni = er * di + ei * dr;
+                dr = nr;
+                di = ni;
+                p = dict_idx[(h * K + k) * N + p];
+                if (p < 0 || p >= N)
+                    return ORC_BAD_MAP;
+            }
+            pi_out[s * N + j] = p;
+            d_out[(s * N + j) * ncomp] = dr;
+            if (is_complex)
+                d_out[(s * N + j) * ncomp + 1] = di;
+        }
+    }
+    return ORC_OK;
+}
