@@ -1,0 +1,188 @@
+"""Benchmark of the Flash PD-SSM forward scan on one MI355X.
+
+One step = one pdssm_scan_fwd call over the whole batch (selection, P D
+recurrence, in-chunk composition, chunk carry, fused readout), inputs already
+resident in HBM.  The default workload is the LM-layer shape: B=8 H=32
+L=4096 N=64 K=64, bf16 router logits, complex64 diagonal, bf16 b/c/y,
+complex64 x_final.  Inputs are seeded synthetic data of that shape.
+
+Prints one JSON line with throughput (scanned tokens/s = B*H*L per second),
+the roofline of the scan kernel (algorithmic HBM bytes per call over the
+measured call time, against 8 TB/s), and the fp64 CPU oracle timed on the
+host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "scanned tokens/sec (B·H·L) and achieved HBM GB/s vs peak, N=64 L=4096"
+HBM_PEAK_GBS = 8000.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "scan_kernel_lm_counters.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "structured_sparse_state_amd", "csrc", f)
+                  for f in ("pdssm_scan.hip", "pdssm_device.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(inp, y, xf) -> int:
+    """Every input read once and every output written once."""
+    n = 0
+    for t in (inp.sel_or_logits, inp.dict_idx, inp.diag, inp.b, inp.c, inp.x0, y, xf):
+        if t is not None:
+            n += t.numel() * t.element_size()
+    return n
+
+
+def counter_traffic(bytes_per_call: int):
+    """HBM bytes per call from the committed rocprofv3 counter summary, or
+    None when the kernel sources changed since the counters were taken."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    vals = {}
+    for line in open(COUNTERS_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_call"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="lm", choices=["lm", "long", "verylong", "small", "tiny"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the scan is measured on a single MI355X.", file=sys.stderr)
+        return 2
+
+    import torch
+    import structured_sparse_state_amd as pk
+    from structured_sparse_state_amd import inputs as gen
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    inp = gen.make_inputs(args.workload, device=dev)
+    B, H, L, N, K = inp.B, inp.H, inp.L, inp.N, inp.K
+    y = torch.empty((B, H, L), device=dev, dtype=torch.bfloat16 if inp.y_bf16 else torch.float32)
+    xf = torch.empty((B, H, N, 2) if inp.complex else (B, H, N), device=dev, dtype=torch.float32)
+    ws = pk.workspace_for(inp)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        pk.scan(inp, workspace=ws, y=y, x_final=xf, stream=stream)
+
+    print(f"[bench] workload {args.workload}: B={B} H={H} L={L} N={N} K={K}; warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for s in range(args.steps):
+        step()
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call_ms = [ev[s].elapsed_time(ev[s + 1]) for s in range(args.steps)]
+    total_ms = ev[0].elapsed_time(ev[-1])
+    ms_per_step = total_ms / args.steps
+    tokens = B * H * L
+    value = tokens / (ms_per_step * 1e-3)
+    alg_bytes = algorithmic_bytes(inp, y, xf)
+    avg_call_s = sum(per_call_ms) / len(per_call_ms) * 1e-3
+    achieved = alg_bytes / avg_call_s / 1e9
+    traffic = counter_traffic(alg_bytes)
+    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (min "
+          f"{min(per_call_ms) * 1e3:.1f}), {achieved:.0f} GB/s algorithmic, wall {wall:.3f} s",
+          file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = cpu_threads()
+        host = inp.to("cpu")
+        orc = oracle.get()
+        best = None
+        for _ in range(args.cpu_reps):
+            c0 = time.perf_counter()
+            orc.scan_inputs(host, nthreads=threads)
+            dt = time.perf_counter() - c0
+            best = dt if best is None else min(best, dt)
+        cpu = {"value": tokens / best, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": f"the whole {args.workload} batch (B={B} H={H} L={L} N={N}), fp64 "
+                         f"sequential oracle, OpenMP over the {B * H} sequences, best of "
+                         f"{args.cpu_reps} runs ({best:.2f} s)"}
+        print(f"[bench] cpu oracle: {best:.2f} s on {threads} threads", file=sys.stderr, flush=True)
+
+    cfgdesc = {
+        "lm": "LM-layer scan: bf16 logits argmax over K, complex64 diag, bf16 b/c, bf16 y, "
+              "complex64 x_final",
+        "long": "time-series scan: int32 selection, permutation dictionary, complex64 "
+                "diag/b/c, fp32 y",
+        "verylong": "very long scan: int16 selection, complex64 diag, bf16 b/c/y",
+        "small": "small real scan: fp32 logits, fp32 diag/b/c/y",
+        "tiny": "tiny real scan: int32 selection, fp32 diag/b/c/y",
+    }[args.workload]
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {cfgdesc}", "B": B, "H": H, "L": L, "N": N,
+                   "K": K, "global_batch": B * H, "seq_len": L, "parallelism": "single GPU"},
+        "achieved_GBps": achieved,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_call": alg_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

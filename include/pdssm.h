@@ -1,0 +1,147 @@
+/*
+ * pdssm.h -- C ABI of the Flash PD-SSM forward recurrence scan on MI355X (gfx950).
+ *
+ * The operation (source: "Flash PD-SSM: Memory-Optimized Structured Sparse
+ * State-Space Models", gist.science explainer, Technical Summary):
+ *
+ *   Methodology, "1. Novel Selection Mechanism (Hard Selection)": a dictionary
+ *   of K sparse matrices is fixed in advance; at each step the K scores pick
+ *   one of them by argmax and it is used directly.  The picked matrix is a
+ *   one-hot column selector P (column j has its single 1 in row pi[j]) times a
+ *   diagonal D, so a step costs O(N) and no N x N matrix is ever formed.
+ *
+ *   Methodology, "3. Hardware-Aware Implementation": the sequence is cut into
+ *   chunks; recurrences run independently inside chunks, a prefix scan over
+ *   chunk aggregates gives the carry states, and the carries correct the
+ *   chunk states.  "Sequential-Parallel Duality in Prefix Scannable Models"
+ *   (fugumt.com listing, abstract) frames such models as a parallel prefix
+ *   scan with a custom associative operator; here that operator composes two
+ *   P D operators by a gather and a multiply.
+ *
+ *   For every sequence (b,h), with x_{-1} = x0[b,h] (zero when x0 is NULL):
+ *       k_t = sel[b,h,t]                      (index modes), or
+ *       k_t = argmax_k logits[b,h,t,k]        (logit modes; first maximum wins,
+ *                                               -0 == +0, NaN above all numbers,
+ *                                               first NaN wins)
+ *       pi  = dict_idx[h, k_t, :]
+ *       x_t[i] = sum_{j : pi[j] = i} diag[b,h,t,j] * x_{t-1}[j]  +  b[b,h,t,i]
+ *       y[b,h,t] = Re( sum_i c[b,h,t,i] * x_t[i] )     (no conjugation)
+ *   and x_final[b,h] = x_{L-1}.
+ *
+ * Arithmetic: fp32 (complex fp32 when PDSSM_COMPLEX), any summation order;
+ * y is rounded once to its storage type (round to nearest even).
+ *
+ * Layouts: contiguous, row-major, DEVICE pointers, each 16-byte aligned.
+ *   sel      int32 or int16          [B,H,L]
+ *   logits   fp32 or bf16            [B,H,L,K]
+ *   dict_idx int32                   [H,K,N], entries in [0,N)
+ *   diag     fp32                    [B,H,L,N], or [B,H,L,N,2] complex (re,im interleaved)
+ *   b, c     fp32 or bf16            same shape as diag
+ *   y        fp32 or bf16            [B,H,L]
+ *   x0, x_final fp32                 [B,H,N], or [B,H,N,2] complex
+ * A dictionary shared by all heads is passed replicated over H.
+ *
+ * Ownership: the caller owns every buffer, including the workspace, whose
+ * size comes from pdssm_scan_workspace_bytes and grows as O(B*H*L*N / 128),
+ * never with N*N*L.  The library allocates nothing and keeps no per-call
+ * state; the workspace may hold anything on entry (the library recognises
+ * its own header and clears the rest on first use).  Two calls in flight at
+ * once need two workspaces.
+ *
+ * Execution: asynchronous on `stream`; no host synchronisation.  Outputs are
+ * valid once the stream has reached the end of the call; inputs must stay
+ * unchanged until then.
+ *
+ * Errors: 0 on success, else a negative PDSSM_ERR_* code; every check except
+ * PDSSM_ERR_HIP runs on the host before any HIP call.  Element values are
+ * preconditions: a selection outside [0,K) or a map entry outside [0,N) is
+ * clamped into range on the device (no fault, result unspecified).
+ */
+#ifndef PDSSM_H
+#define PDSSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* flags: selection storage (2 bits) */
+#define PDSSM_SEL_I32 0x0u     /* sel int32 [B,H,L] */
+#define PDSSM_SEL_I16 0x1u     /* sel int16 [B,H,L] */
+#define PDSSM_LOGITS_F32 0x2u  /* logits fp32 [B,H,L,K] */
+#define PDSSM_LOGITS_BF16 0x3u /* logits bf16 [B,H,L,K] */
+#define PDSSM_SEL_MASK 0x3u
+/* flags: value storage */
+#define PDSSM_COMPLEX 0x4u /* diag, b, c, x0, x_final complex (re,im pairs) */
+#define PDSSM_BC_BF16 0x8u /* b and c stored as bf16 (else fp32) */
+#define PDSSM_Y_BF16 0x10u /* y stored as bf16 (else fp32) */
+#define PDSSM_FLAGS_ALL 0x1Fu
+
+/* status codes */
+#define PDSSM_OK 0
+#define PDSSM_ERR_NULL -1      /* a required pointer is NULL */
+#define PDSSM_ERR_DIM -2       /* B,H,L < 1, N not in [1,64], K not in [1,32767], or too large */
+#define PDSSM_ERR_FLAGS -3     /* unknown flag bits, or a mode the call does not take */
+#define PDSSM_ERR_ALIGN -4     /* a pointer is not 16-byte aligned */
+#define PDSSM_ERR_WORKSPACE -5 /* workspace smaller than the size function returns */
+#define PDSSM_ERR_HIP -6       /* a HIP launch failed; pdssm_strerror gives the HIP text */
+
+/*
+ * The forward scan (all five steps of the path: selection, per-step P D
+ * update, in-chunk composition, chunk carry, fused readout).
+ *   sel_or_logits  selection input, storage given by flags & PDSSM_SEL_MASK
+ *   dict_idx       dictionary index maps
+ *   diag, b, c     per-step diagonal, input and readout vectors
+ *   y              output readout
+ *   x_final        output final state, or NULL
+ *   x0             initial state, or NULL for zero
+ *   workspace      device buffer of workspace_bytes bytes (see above)
+ */
+int pdssm_scan_fwd(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
+                   const void *b, const void *c, void *y, void *x_final, int64_t B, int64_t H,
+                   int64_t L, int32_t N, int32_t K, uint32_t flags, const void *x0,
+                   void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes pdssm_scan_fwd and pdssm_compose need for these sizes and
+ * flags; 0 when the arguments are invalid. */
+size_t pdssm_scan_workspace_bytes(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K,
+                                  uint32_t flags);
+
+/*
+ * The selection step alone: sel_out[b,h,t] = the dictionary entry step t
+ * picks (Methodology, "1. Novel Selection Mechanism": argmax of the K
+ * scores; index modes copy the index).  flags: selection bits only.
+ */
+int pdssm_select(const void *sel_or_logits, int32_t *sel_out, int64_t B, int64_t H, int64_t L,
+                 int32_t K, uint32_t flags, hipStream_t stream);
+
+/*
+ * The total operator A_{L-1} ... A_0 of every sequence, which is again a
+ * one-hot column selector times a diagonal (Methodology, "1. Novel Selection
+ * Mechanism": the matrices stay sparse; the composition is the chunk
+ * aggregate of "3. Hardware-Aware Implementation", Phase B, over the whole
+ * sequence).  Column j of the product has d_out[b,h,j] in row pi_out[b,h,j].
+ *   pi_out  int32 [B,H,N]
+ *   d_out   fp32  [B,H,N], or [B,H,N,2] with PDSSM_COMPLEX
+ * flags: selection bits and PDSSM_COMPLEX.  The workspace is sized by
+ * pdssm_scan_workspace_bytes with the same arguments.
+ */
+int pdssm_compose(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
+                  int32_t *pi_out, void *d_out, int64_t B, int64_t H, int64_t L, int32_t N,
+                  int32_t K, uint32_t flags, void *workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+
+/* Text for a status code; for PDSSM_ERR_HIP, the HIP error of the failing
+ * call on this thread.  The string stays valid until the next call on this
+ * thread. */
+const char *pdssm_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PDSSM_H */

@@ -1,0 +1,204 @@
+"""Flash PD-SSM forward recurrence scan for AMD MI355X (gfx950).
+
+The compute path is the C-ABI library ``libpdssm.so`` (hand-written HIP
+kernels, declared in ``include/pdssm.h``).  This module is a thin ctypes
+binding with the same function names: it only turns torch tensors into
+device pointers and the current HIP stream into a ``hipStream_t``.  Every
+step of the scan runs in the library's kernels; there is no fallback, and a
+missing library raises.
+
+Higher-level helpers (``scan``, ``select``, ``compose``) allocate outputs and
+the workspace with torch and call the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libpdssm.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "pdssm.h")
+
+# Flag and status values of include/pdssm.h (tests check they agree).
+PDSSM_SEL_I32 = 0x0
+PDSSM_SEL_I16 = 0x1
+PDSSM_LOGITS_F32 = 0x2
+PDSSM_LOGITS_BF16 = 0x3
+PDSSM_SEL_MASK = 0x3
+PDSSM_COMPLEX = 0x4
+PDSSM_BC_BF16 = 0x8
+PDSSM_Y_BF16 = 0x10
+PDSSM_FLAGS_ALL = 0x1F
+
+PDSSM_OK = 0
+PDSSM_ERR_NULL = -1
+PDSSM_ERR_DIM = -2
+PDSSM_ERR_FLAGS = -3
+PDSSM_ERR_ALIGN = -4
+PDSSM_ERR_WORKSPACE = -5
+PDSSM_ERR_HIP = -6
+
+SEL_FLAG = {"sel_i32": PDSSM_SEL_I32, "sel_i16": PDSSM_SEL_I16,
+            "logits_f32": PDSSM_LOGITS_F32, "logits_bf16": PDSSM_LOGITS_BF16}
+
+_LIB = None
+
+
+class PdssmError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"pdssm status {status}: {text}")
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(f"{LIBRARY} is missing: build it with __graft_entry__.build() "
+                               "(hipcc --offload-arch=gfx950); there is no fallback path")
+        lib = ctypes.CDLL(LIBRARY)
+        P, I64, I32, U32, SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32,
+                                ctypes.c_size_t)
+        lib.pdssm_scan_fwd.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, U32, P, P, SZ, P]
+        lib.pdssm_scan_fwd.restype = ctypes.c_int
+        lib.pdssm_scan_workspace_bytes.argtypes = [I64, I64, I64, I32, I32, U32]
+        lib.pdssm_scan_workspace_bytes.restype = SZ
+        lib.pdssm_select.argtypes = [P, P, I64, I64, I64, I32, U32, P]
+        lib.pdssm_select.restype = ctypes.c_int
+        lib.pdssm_compose.argtypes = [P, P, P, P, P, I64, I64, I64, I32, I32, U32, P, SZ, P]
+        lib.pdssm_compose.restype = ctypes.c_int
+        lib.pdssm_strerror.argtypes = [ctypes.c_int]
+        lib.pdssm_strerror.restype = ctypes.c_char_p
+        _LIB = lib
+    return _LIB
+
+
+def header_functions() -> list:
+    """Names of the functions include/pdssm.h declares."""
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(pdssm_[a-z_]+)\s*\(", text)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# The C entry points, same names and argument order.  Tensors (or raw
+# addresses) in, status code out.
+# ---------------------------------------------------------------------------
+
+def pdssm_scan_fwd(sel_or_logits, dict_idx, diag, b, c, y, x_final, B, H, L, N, K, flags, x0,
+                   workspace, workspace_bytes, stream=None) -> int:
+    return library().pdssm_scan_fwd(_ptr(sel_or_logits), _ptr(dict_idx), _ptr(diag), _ptr(b),
+                                    _ptr(c), _ptr(y), _ptr(x_final), B, H, L, N, K, flags,
+                                    _ptr(x0), _ptr(workspace), workspace_bytes, _stream(stream))
+
+
+def pdssm_scan_workspace_bytes(B, H, L, N, K, flags) -> int:
+    return library().pdssm_scan_workspace_bytes(B, H, L, N, K, flags)
+
+
+def pdssm_select(sel_or_logits, sel_out, B, H, L, K, flags, stream=None) -> int:
+    return library().pdssm_select(_ptr(sel_or_logits), _ptr(sel_out), B, H, L, K, flags,
+                                  _stream(stream))
+
+
+def pdssm_compose(sel_or_logits, dict_idx, diag, pi_out, d_out, B, H, L, N, K, flags, workspace,
+                  workspace_bytes, stream=None) -> int:
+    return library().pdssm_compose(_ptr(sel_or_logits), _ptr(dict_idx), _ptr(diag), _ptr(pi_out),
+                                   _ptr(d_out), B, H, L, N, K, flags, _ptr(workspace),
+                                   workspace_bytes, _stream(stream))
+
+
+def pdssm_strerror(status: int) -> str:
+    return library().pdssm_strerror(status).decode()
+
+
+def check(status: int) -> None:
+    if status != PDSSM_OK:
+        raise PdssmError(status, pdssm_strerror(status))
+
+
+# ---------------------------------------------------------------------------
+# Convenience layer over ScanInputs-like objects (fields: sel_mode,
+# sel_or_logits, dict_idx, diag, b, c, x0, complex, bc_bf16, y_bf16, B, H,
+# L, N, K), all tensors on the GPU.
+# ---------------------------------------------------------------------------
+
+def flags_of(inp) -> int:
+    f = SEL_FLAG[inp.sel_mode]
+    if inp.complex:
+        f |= PDSSM_COMPLEX
+    if inp.bc_bf16:
+        f |= PDSSM_BC_BF16
+    if inp.y_bf16:
+        f |= PDSSM_Y_BF16
+    return f
+
+
+def workspace_for(inp, device=None) -> torch.Tensor:
+    n = pdssm_scan_workspace_bytes(inp.B, inp.H, inp.L, inp.N, inp.K, flags_of(inp))
+    if n == 0:
+        raise PdssmError(PDSSM_ERR_DIM, "invalid sizes")
+    return torch.empty(n, dtype=torch.uint8, device=device or inp.diag.device)
+
+
+def scan(inp, *, workspace: Optional[torch.Tensor] = None, want_x_final: bool = True,
+         y: Optional[torch.Tensor] = None, x_final: Optional[torch.Tensor] = None, stream=None,
+         x0="from_inputs"):
+    """Run pdssm_scan_fwd on a batch; returns (y, x_final or None)."""
+    dev = inp.diag.device
+    if y is None:
+        y = torch.empty((inp.B, inp.H, inp.L), device=dev,
+                        dtype=torch.bfloat16 if inp.y_bf16 else torch.float32)
+    if want_x_final and x_final is None:
+        shape = (inp.B, inp.H, inp.N, 2) if inp.complex else (inp.B, inp.H, inp.N)
+        x_final = torch.empty(shape, device=dev, dtype=torch.float32)
+    if workspace is None:
+        workspace = workspace_for(inp)
+    x0t = inp.x0 if isinstance(x0, str) else x0
+    check(pdssm_scan_fwd(inp.sel_or_logits, inp.dict_idx, inp.diag, inp.b, inp.c, y,
+                         x_final if want_x_final else None, inp.B, inp.H, inp.L, inp.N, inp.K,
+                         flags_of(inp), x0t, workspace, workspace.numel(), stream))
+    return y, (x_final if want_x_final else None)
+
+
+def select(sel_or_logits, sel_mode: str, K: int, stream=None) -> torch.Tensor:
+    shape = sel_or_logits.shape if sel_mode.startswith("sel") else sel_or_logits.shape[:-1]
+    B, H, L = shape
+    out = torch.empty((B, H, L), dtype=torch.int32, device=sel_or_logits.device)
+    check(pdssm_select(sel_or_logits, out, B, H, L, K, SEL_FLAG[sel_mode], stream))
+    return out
+
+
+def compose(inp, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Total operator of every sequence: (pi int32 [B,H,N], d fp32 [B,H,N(,2)])."""
+    dev = inp.diag.device
+    flags = SEL_FLAG[inp.sel_mode] | (PDSSM_COMPLEX if inp.complex else 0)
+    pi = torch.empty((inp.B, inp.H, inp.N), dtype=torch.int32, device=dev)
+    d = torch.empty((inp.B, inp.H, inp.N, 2) if inp.complex else (inp.B, inp.H, inp.N),
+                    dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = workspace_for(inp)
+    check(pdssm_compose(inp.sel_or_logits, inp.dict_idx, inp.diag, pi, d, inp.B, inp.H, inp.L,
+                        inp.N, inp.K, flags, workspace, workspace.numel(), stream))
+    return pi, d

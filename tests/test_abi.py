@@ -1,0 +1,93 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments on the host before any HIP call.  No call here reaches
+a kernel launch."""
+import ctypes
+import re
+
+import pytest
+
+import structured_sparse_state_amd as pk
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pk.library()
+
+
+def test_exports_every_declared_function(lib):
+    names = pk.header_functions()
+    assert set(names) == {"pdssm_scan_fwd", "pdssm_scan_workspace_bytes", "pdssm_select",
+                          "pdssm_compose", "pdssm_strerror"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_constants_match_binding():
+    text = open(pk.HEADER).read()
+    defs = dict(re.findall(r"#define\s+(PDSSM_[A-Z0-9_]+)\s+(-?0x[0-9A-Fa-f]+u?|-?\d+)", text))
+    assert defs
+    for name, val in defs.items():
+        v = int(val.rstrip("u"), 0)
+        assert getattr(pk, name) == v, name
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6, 42):
+        assert pk.pdssm_strerror(code)
+
+
+FAKE = 1 << 20          # an aligned, never-dereferenced address
+
+
+def _scan(**kw):
+    args = dict(sel=FAKE, dict_idx=FAKE, diag=FAKE, b=FAKE, c=FAKE, y=FAKE, x_final=None,
+                B=2, H=3, L=100, N=16, K=8, flags=pk.PDSSM_LOGITS_BF16, x0=None, ws=FAKE,
+                ws_bytes=1 << 40)
+    args.update(kw)
+    return pk.pdssm_scan_fwd(args["sel"], args["dict_idx"], args["diag"], args["b"], args["c"],
+                             args["y"], args["x_final"], args["B"], args["H"], args["L"], args["N"],
+                             args["K"], args["flags"], args["x0"], args["ws"], args["ws_bytes"], 0)
+
+
+def test_scan_argument_errors(lib):
+    for name in ("sel", "dict_idx", "diag", "b", "c", "y", "ws"):
+        assert _scan(**{name: None}) == pk.PDSSM_ERR_NULL, name
+    for bad in (dict(B=0), dict(H=-1), dict(L=0), dict(N=0), dict(N=65), dict(K=0),
+                dict(K=32768), dict(B=1 << 40, H=1 << 20)):
+        assert _scan(**bad) == pk.PDSSM_ERR_DIM, bad
+    assert _scan(flags=0x20) == pk.PDSSM_ERR_FLAGS
+    for name in ("sel", "dict_idx", "diag", "b", "c", "y", "ws", "x0", "x_final"):
+        assert _scan(**{name: FAKE + 4}) == pk.PDSSM_ERR_ALIGN, name
+    need = pk.pdssm_scan_workspace_bytes(2, 3, 100, 16, 8, pk.PDSSM_LOGITS_BF16)
+    assert _scan(ws_bytes=need - 1) == pk.PDSSM_ERR_WORKSPACE
+
+
+def test_select_and_compose_argument_errors(lib):
+    assert pk.pdssm_select(None, FAKE, 1, 1, 1, 4, 0, 0) == pk.PDSSM_ERR_NULL
+    assert pk.pdssm_select(FAKE, FAKE, 1, 1, 0, 4, 0, 0) == pk.PDSSM_ERR_DIM
+    assert pk.pdssm_select(FAKE, FAKE, 1, 1, 1, 4, pk.PDSSM_COMPLEX, 0) == pk.PDSSM_ERR_FLAGS
+    assert pk.pdssm_select(FAKE + 2, FAKE, 1, 1, 1, 4, 0, 0) == pk.PDSSM_ERR_ALIGN
+    c = pk.pdssm_compose
+    assert c(FAKE, FAKE, FAKE, None, FAKE, 1, 1, 8, 4, 2, 0, FAKE, 1 << 30, 0) == pk.PDSSM_ERR_NULL
+    assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 70, 2, 0, FAKE, 1 << 30, 0) == pk.PDSSM_ERR_DIM
+    assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 4, 2, pk.PDSSM_Y_BF16, FAKE, 1 << 30,
+             0) == pk.PDSSM_ERR_FLAGS
+    assert c(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 8, 4, 2, 0, FAKE, 16, 0) == pk.PDSSM_ERR_WORKSPACE
+
+
+def test_workspace_is_linear_in_length_not_quadratic_in_state(lib):
+    """O(L N) memory (Methodology, "1. Novel Selection Mechanism": the
+    selected matrices are never dense, so memory drops from O(L N^2) to
+    O(L N)): the workspace grows linearly in L and B*H, at most linearly in
+    N, and is a small fraction of the inputs."""
+    f = pk.PDSSM_LOGITS_BF16 | pk.PDSSM_COMPLEX | pk.PDSSM_BC_BF16 | pk.PDSSM_Y_BF16
+    ws = lambda B, H, L, N: pk.pdssm_scan_workspace_bytes(B, H, L, N, 64, f)
+    base = ws(8, 32, 4096, 64)
+    assert 0 < base
+    assert ws(8, 32, 8192, 64) - 256 <= 2 * (base - 256) + 1
+    assert ws(16, 32, 4096, 64) - 256 <= 2 * (base - 256) + 1
+    assert ws(8, 32, 4096, 32) <= base
+    inputs = 8 * 32 * 4096 * (64 * 8 + 64 * 4 * 2 + 64 * 2)
+    assert base < 0.03 * inputs
+    assert pk.pdssm_scan_workspace_bytes(0, 1, 1, 1, 1, 0) == 0
+    assert pk.pdssm_scan_workspace_bytes(1, 1, 1, 1, 1, 0x40) == 0

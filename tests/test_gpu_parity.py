@@ -1,0 +1,270 @@
+"""GPU parity: the HIP path (through the C-ABI) against the fp64 oracle.
+
+Floating outputs must be within the per-sequence relative tolerance
+(1e-4 with fp32 I/O, 2e-2 with bf16 b/c/y); selections, composed index maps
+and automaton states must be bit-exact.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import structured_sparse_state_amd as pk
+from structured_sparse_state_amd import inputs as gen
+from tests.gpu_common import seq_rel_err, tol_of, x_to_np, y_to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def run_and_compare(orc, inp, label, x0="from_inputs"):
+    say(f"[case] {label}: B={inp.B} H={inp.H} L={inp.L} N={inp.N} K={inp.K} "
+        f"mode={inp.sel_mode} cplx={inp.complex} bf16={inp.bc_bf16}/{inp.y_bf16}")
+    g = inp.to(DEV)
+    y, xf = pk.scan(g, x0=x0 if isinstance(x0, str) else (None if x0 is None else x0.to(DEV)))
+    torch.cuda.synchronize()
+    y_ref, xf_ref = orc.scan_inputs(inp, nthreads=8, x0=x0)
+    tol = tol_of(inp)
+    ey = seq_rel_err(y_to_np(y), y_ref)
+    ex = seq_rel_err(x_to_np(xf, inp.complex), xf_ref)
+    assert np.all(np.isfinite(y_to_np(y)))
+    assert ey <= tol, f"{label}: y error {ey:.3e} > {tol}"
+    assert ex <= tol, f"{label}: x_final error {ex:.3e} > {tol}"
+    return ey, ex
+
+
+# ---------------------------------------------------------------------------
+# The five workloads, at oracle-friendly sizes (full L, several tiles, ragged
+# tails) ...
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,B,H,L", [
+    ("tiny", 1, 1, 256),
+    ("small", 2, 3, 2048),
+    ("long", 1, 2, 18000),
+    ("lm", 1, 3, 4096),
+    ("verylong", 1, 1, 131072),
+])
+def test_workload_scaled(orc, name, B, H, L):
+    inp = gen.make_inputs(name, B=B, H=H, L=L)
+    run_and_compare(orc, inp, f"{name} scaled")
+    inp = gen.make_inputs(name, B=B, H=H, L=min(L, 3000) - 7, with_x0=True, seed=77)
+    run_and_compare(orc, inp, f"{name} scaled with x0, ragged L")
+
+
+# ... and at their full sizes, in the bench's launch configuration, checked
+# on sampled sequences.
+@pytest.mark.parametrize("name,samples", [("small", 6), ("long", 4), ("lm", 6), ("verylong", 3)])
+def test_workload_full_size_sampled(orc, name, samples):
+    cfg = gen.CONFIGS[name]
+    say(f"[case] {name} full size B={cfg['B']} H={cfg['H']} L={cfg['L']}")
+    g = gen.make_inputs(name, device=DEV)
+    y, xf = pk.scan(g)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    picks = {(0, 0), (cfg["B"] - 1, cfg["H"] - 1)}
+    while len(picks) < samples:
+        picks.add((int(rng.integers(cfg["B"])), int(rng.integers(cfg["H"]))))
+    tol = tol_of(g)
+    for (bi, hi) in sorted(picks):
+        one = g.sequence(bi, hi).to("cpu")
+        y_ref, xf_ref = orc.scan_inputs(one, nthreads=1)
+        ey = seq_rel_err(y_to_np(y[bi:bi + 1, hi:hi + 1]), y_ref)
+        ex = seq_rel_err(x_to_np(xf[bi:bi + 1, hi:hi + 1], g.complex), xf_ref)
+        say(f"  seq ({bi},{hi}): y err {ey:.2e}, x_final err {ex:.2e}")
+        assert ey <= tol and ex <= tol, (bi, hi, ey, ex)
+    del g, y, xf
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# Shapes: every padded state width, ragged N and L, small and odd K.
+# ---------------------------------------------------------------------------
+
+SHAPES = [
+    # N, L, K, sel_mode, complex, bc_bf16, y_bf16
+    (1, 1, 1, gen.SEL_I32, False, False, False),
+    (1, 77, 3, gen.LOGITS_F32, True, False, False),
+    (3, 31, 5, gen.LOGITS_BF16, False, True, True),
+    (5, 33, 7, gen.SEL_I16, True, True, False),
+    (8, 129, 4, gen.LOGITS_F32, False, False, False),
+    (13, 1000, 200, gen.LOGITS_BF16, True, True, True),
+    (16, 513, 16, gen.SEL_I32, True, False, False),
+    (17, 300, 9, gen.LOGITS_BF16, False, False, True),
+    (31, 257, 32, gen.LOGITS_F32, True, False, False),
+    (32, 1025, 64, gen.SEL_I16, False, True, False),
+    (33, 129, 12, gen.LOGITS_BF16, True, True, True),
+    (47, 2000, 33, gen.SEL_I32, True, False, False),
+    (63, 95, 8, gen.LOGITS_F32, False, False, False),
+    (64, 1, 64, gen.LOGITS_BF16, True, True, True),
+    (64, 127, 2, gen.SEL_I32, False, False, False),
+    (64, 5000, 128, gen.LOGITS_BF16, True, True, True),
+]
+
+
+@pytest.mark.parametrize("N,L,K,mode,cplx,bcbf,ybf", SHAPES)
+def test_shapes(orc, N, L, K, mode, cplx, bcbf, ybf):
+    for with_x0 in (False, True):
+        inp = gen.make_inputs("tiny", B=2, H=2, L=L, N=N, K=K, sel_mode=mode, complex=cplx,
+                              bc_bf16=bcbf, y_bf16=ybf, dmin=0.8, dmax=1.0, with_x0=with_x0,
+                              seed=1000 + N * 7 + L)
+        run_and_compare(orc, inp, f"shape N={N} L={L} K={K} x0={with_x0}")
+
+
+# ---------------------------------------------------------------------------
+# Automata: D = I, one-hot or count states -- every value is an exact small
+# integer, so the GPU must match bit for bit (Proposition 1 of the pages: one
+# layer of state size N represents any N-state automaton).
+# ---------------------------------------------------------------------------
+
+FSA = [
+    ("parity", 2, False, gen.SEL_I32, False, 8, 256),
+    ("parity", 2, False, gen.LOGITS_BF16, True, 8, 5000),
+    ("modcount", 5, False, gen.SEL_I16, False, 8, 3001),
+    ("modcount", 7, False, gen.LOGITS_F32, True, 16, 777),
+    ("cycle", 6, False, gen.SEL_I32, True, 32, 4096),
+    ("cycle", 12, False, gen.LOGITS_BF16, False, 64, 9000),
+    ("reset", 5, True, gen.SEL_I32, False, 8, 2048),
+    ("reset", 6, True, gen.LOGITS_F32, True, 64, 1500),
+]
+
+
+@pytest.mark.parametrize("kind,m,count,mode,cplx,N,L", FSA)
+def test_automata_bit_exact(orc, kind, m, count, mode, cplx, N, L):
+    inp = gen.make_fsa_inputs(kind, B=2, H=3, L=L, N=N, m=m, count_state=count, sel_mode=mode,
+                              complex=cplx, seed=50 + m + L, start_state=1 % m)
+    say(f"[case] fsa {kind} m={m} N={N} L={L} mode={mode} cplx={cplx}")
+    g = inp.to(DEV)
+    y, xf = pk.scan(g)
+    torch.cuda.synchronize()
+    y_ref, xf_ref = orc.scan_inputs(inp)
+    assert np.array_equal(y_to_np(y), y_ref)
+    assert np.array_equal(x_to_np(xf, cplx), xf_ref)
+
+
+# ---------------------------------------------------------------------------
+# Selection alone (bit-exact) and the composed total operator.
+# ---------------------------------------------------------------------------
+
+def test_select_bit_exact(orc):
+    g = torch.Generator().manual_seed(9)
+    cases = []
+    for K in (1, 3, 8, 16, 64, 100, 128):
+        v = torch.randint(-4, 5, (2, 3, 333, K), generator=g).float() * 0.25
+        v[torch.rand(v.shape, generator=g) < 0.05] = -0.0
+        cases.append(("logits_bf16", v.to(torch.bfloat16), K))
+        cases.append(("logits_f32", v, K))
+    lg = torch.randn((4, 8, 1024, 64), generator=g).to(torch.bfloat16)
+    cases.append(("logits_bf16", lg, 64))
+    nanl = torch.randn((1, 2, 64, 16), generator=g)
+    nanl[0, 0, 3, 9] = float("nan")
+    nanl[0, 1, 5, 0] = float("nan")
+    nanl[0, 1, 5, 7] = float("nan")
+    nanl[0, 1, 6, 2] = float("inf")
+    cases.append(("logits_f32", nanl, 16))
+    cases.append(("logits_bf16", nanl.to(torch.bfloat16), 16))
+    s = torch.randint(0, 50, (3, 2, 1000), generator=g, dtype=torch.int32)
+    cases.append(("sel_i32", s, 50))
+    cases.append(("sel_i16", s.to(torch.int16), 50))
+    for mode, src, K in cases:
+        got = pk.select(src.to(DEV), mode, K).cpu().numpy()
+        want = orc.select(src, mode, K)
+        assert np.array_equal(got, want), (mode, K)
+
+
+@pytest.mark.parametrize("name,B,H,L", [("tiny", 1, 1, 256), ("small", 2, 2, 2048),
+                                        ("long", 1, 2, 18000), ("lm", 2, 2, 4096),
+                                        ("lm", 1, 1, 333)])
+def test_compose(orc, name, B, H, L):
+    inp = gen.make_inputs(name, B=B, H=H, L=L)
+    pi, d = pk.compose(inp.to(DEV))
+    torch.cuda.synchronize()
+    pi_ref, d_ref = orc.compose_inputs(inp)
+    assert np.array_equal(pi.cpu().numpy(), pi_ref)
+    dg = x_to_np(d, inp.complex)
+    rtol = 4e-7 * L + 1e-5
+    assert np.all(np.abs(dg - d_ref) <= rtol * np.abs(d_ref) + 1e-30), name
+
+
+def test_compose_automaton_exact(orc):
+    inp = gen.make_fsa_inputs("cycle", B=2, H=2, L=4000, N=16, m=9, seed=5)
+    pi, d = pk.compose(inp.to(DEV))
+    pi_ref, d_ref = orc.compose_inputs(inp)
+    assert np.array_equal(pi.cpu().numpy(), pi_ref)
+    assert np.array_equal(d.cpu().numpy().astype(np.float64), d_ref)
+
+
+# ---------------------------------------------------------------------------
+# Workspace handling and chaining.
+# ---------------------------------------------------------------------------
+
+def test_workspace_reuse_and_garbage(orc):
+    big = gen.make_inputs("lm", B=2, H=2, L=3000, seed=3)
+    small = gen.make_inputs("long", B=1, H=3, L=1000, seed=4)
+    n = max(pk.workspace_for(big.to(DEV)).numel(), pk.workspace_for(small.to(DEV)).numel())
+    ws = torch.randint(0, 256, (n,), dtype=torch.uint8, device=DEV)   # garbage on entry
+    for rep in range(3):
+        for inp, label in ((big, "lm"), (small, "long"), (big, "lm")):
+            say(f"[case] workspace reuse {rep} {label}")
+            y, xf = pk.scan(inp.to(DEV), workspace=ws)
+            torch.cuda.synchronize()
+            y_ref, xf_ref = orc.scan_inputs(inp, nthreads=8)
+            assert seq_rel_err(y_to_np(y), y_ref) <= tol_of(inp)
+            assert seq_rel_err(x_to_np(xf, inp.complex), xf_ref) <= tol_of(inp)
+
+
+def test_segment_chaining(orc):
+    """Scanning [0, L) equals [0, L1) then [L1, L) started from x_final."""
+    inp = gen.make_inputs("long", B=2, H=2, L=5000, seed=8)
+    g = inp.to(DEV)
+    y, xf = pk.scan(g)
+    L1 = 2333
+    first = gen.ScanInputs(**{**g.__dict__})
+    for f in ("sel_or_logits", "diag", "b", "c"):
+        setattr(first, f, getattr(g, f)[:, :, :L1].contiguous())
+    first.L = L1
+    y1, x1 = pk.scan(first)
+    second = gen.ScanInputs(**{**g.__dict__})
+    for f in ("sel_or_logits", "diag", "b", "c"):
+        setattr(second, f, getattr(g, f)[:, :, L1:].contiguous())
+    second.L = inp.L - L1
+    y2, x2 = pk.scan(second, x0=x1)
+    torch.cuda.synchronize()
+    yc = torch.cat([y1, y2], dim=-1)
+    assert seq_rel_err(y_to_np(yc), y_to_np(y)) <= 1e-4
+    assert seq_rel_err(x_to_np(x2, True), x_to_np(xf, True)) <= 1e-4
+
+
+def test_no_x_final_pointer(orc):
+    inp = gen.make_inputs("lm", B=1, H=2, L=1000)
+    y, xf = pk.scan(inp.to(DEV), want_x_final=False)
+    assert xf is None
+    y_ref, _ = orc.scan_inputs(inp)
+    assert seq_rel_err(y_to_np(y), y_ref) <= tol_of(inp)
+
+
+def test_stream_argument(orc):
+    inp = gen.make_inputs("small", B=1, H=2, L=900)
+    s = torch.cuda.Stream()
+    g = inp.to(DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        y, xf = pk.scan(g, stream=s)
+    s.synchronize()
+    y_ref, _ = orc.scan_inputs(inp)
+    assert seq_rel_err(y_to_np(y), y_ref) <= tol_of(inp)
