@@ -137,6 +137,337 @@ __device__ __forceinline__ int select_step(const void *__restrict__ src, uint32_
 }
 
 // ---------------------------------------------------------------------------
+// Cross-lane moves inside a wavefront.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bperm(float v, int src_lane)
+{
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(v)));
+}
+__device__ __forceinline__ int bperm(int v, int src_lane)
+{
+    return __builtin_amdgcn_ds_bpermute(src_lane << 2, v);
+}
+__device__ __forceinline__ uint32_t bperm(uint32_t v, int src_lane)
+{
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane << 2, (int)v);
+}
+
+// DPP lane moves inside rows of 16 lanes.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8
+constexpr int kDppRowRor8 = 0x128;    // lane i <- (i+8) mod 16 within each row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// The partner value across lane bit b (used only as a summation partner:
+// for b = 2 the partner is the mirror lane 7-i, which differs in bit 2 and
+// keeps bits >= 3, enough for a reduction that later sums bits 1 and 0).
+template <int BIT>
+__device__ __forceinline__ float across_bit(float v)
+{
+    if constexpr (BIT == 3)
+        return dpp<kDppRowRor8>(v);
+    else if constexpr (BIT == 2)
+        return dpp<kDppHalfMirror>(v);
+    else if constexpr (BIT == 1)
+        return dpp<kDppXor2>(v);
+    else
+        return dpp<kDppXor1>(v);
+}
+
+// Sum of the two values held across lane bit BIT (5: lanes l and l^32,
+// 4: l and l^16): the permlane swaps of gfx950 exchange half-waves / odd
+// and even rows between two registers in one instruction.
+template <int BIT>
+__device__ __forceinline__ void swap_halves(float &lo_keep, float &hi_keep)
+{
+    // After the swap, lanes with BIT clear hold (lo[l], lo[partner]) in the
+    // two registers and lanes with BIT set hold (hi[partner], hi[l]).
+    if constexpr (BIT == 5) {
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo_keep), __float_as_uint(hi_keep),
+                                                  false, false);
+        lo_keep = __uint_as_float(r[0]);
+        hi_keep = __uint_as_float(r[1]);
+    } else {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo_keep), __float_as_uint(hi_keep),
+                                                  false, false);
+        lo_keep = __uint_as_float(r[0]);
+        hi_keep = __uint_as_float(r[1]);
+    }
+}
+
+// Transposed butterfly sum inside groups of NP lanes.  On entry every lane
+// holds v[t] for T steps; on exit register r of lane i (group-local index)
+// holds the group sum of step  r + RF * (i >> NPLAIN), with RF and NPLAIN
+// below, and every lane whose low NPLAIN bits are zero owns its steps.
+template <int NP, int T>
+struct Butterfly {
+    static constexpr int LOG = NP == 8 ? 3 : NP == 16 ? 4 : NP == 32 ? 5 : 6;
+    static constexpr int LT = T == 1 ? 0 : T == 2 ? 1 : T == 4 ? 2 : T == 8 ? 3 : T == 16 ? 4 : T == 32 ? 5 : 6;
+    static constexpr int NH = LT < LOG ? LT : LOG;   // halving levels
+    static constexpr int NPLAIN = LOG - NH;          // plain levels
+    static constexpr int RF = T >> NH;               // registers left
+};
+
+template <int BIT, int R>
+__device__ __forceinline__ void butterfly_level(float *v, int i)
+{
+    if constexpr (R > 1) {
+        constexpr int H = R / 2;
+        const bool hi = (i >> BIT) & 1;
+#pragma unroll
+        for (int r = 0; r < H; ++r) {
+            if constexpr (BIT >= 4) {
+                float a = v[r], b = v[r + H];
+                swap_halves<BIT>(a, b);
+                v[r] = a + b;
+            } else {
+                const float send = hi ? v[r] : v[r + H];
+                const float keep = hi ? v[r + H] : v[r];
+                v[r] = keep + across_bit<BIT>(send);
+            }
+        }
+    } else {
+        if constexpr (BIT >= 4) {
+            float a = v[0], b = v[0];
+            swap_halves<BIT>(a, b);
+            v[0] = a + b;
+        } else {
+            v[0] = v[0] + across_bit<BIT>(v[0]);
+        }
+    }
+}
+
+template <int BIT, int R>
+__device__ __forceinline__ void butterfly_from(float *v, int i)
+{
+    butterfly_level<BIT, R>(v, i);
+    if constexpr (BIT > 0)
+        butterfly_from<BIT - 1, (R > 1 ? R / 2 : 1)>(v, i);
+}
+
+template <int NP, int T>
+__device__ __forceinline__ void group_transpose_sum(float (&v)[T], int i)
+{
+    butterfly_from<Butterfly<NP, T>::LOG - 1, T>(v, i);
+}
+
+// ---------------------------------------------------------------------------
+// Cooperative hard selection for SPW consecutive steps of one sequence by
+// one wave.  With SPW <= 64, 64/SPW lanes share a step: each takes a slice of
+// the K scores (coalesced, 16-byte loads when aligned), then the slices
+// combine across lanes.  Writes k to out[q] for q < SPW (0 past the end).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool better(float v2, int k2, float v1, int k1)
+{
+    const bool n1 = v1 != v1, n2 = v2 != v2;
+    if (n2)
+        return !n1 || k2 < k1;
+    return !n1 && (v2 > v1 || (v2 == v1 && k2 < k1));
+}
+
+__device__ __forceinline__ void slice_argmax(const void *__restrict__ src, uint32_t mode,
+                                             int64_t step, int K, int k0, int k1, float &bv, int &bk)
+{
+    if (mode == PDSSM_LOGITS_F32) {
+        const float *row = reinterpret_cast<const float *>(src) + step * (int64_t)K;
+        if (((K | k0 | k1) & 3) == 0) {
+            for (int q = k0; q < k1; q += 4) {
+                const float4 v = *reinterpret_cast<const float4 *>(row + q);
+                if (better(v.x, q, bv, bk)) { bv = v.x; bk = q; }
+                if (better(v.y, q + 1, bv, bk)) { bv = v.y; bk = q + 1; }
+                if (better(v.z, q + 2, bv, bk)) { bv = v.z; bk = q + 2; }
+                if (better(v.w, q + 3, bv, bk)) { bv = v.w; bk = q + 3; }
+            }
+        } else {
+            for (int q = k0; q < k1; ++q) {
+                const float v = row[q];
+                if (better(v, q, bv, bk)) { bv = v; bk = q; }
+            }
+        }
+    } else {
+        const uint16_t *row = reinterpret_cast<const uint16_t *>(src) + step * (int64_t)K;
+        if (((K | k0 | k1) & 7) == 0) {
+            for (int q = k0; q < k1; q += 8) {
+                const uint4 w = *reinterpret_cast<const uint4 *>(row + q);
+                const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float lo = bf16_lo(ws[m]), hi = bf16_hi(ws[m]);
+                    if (better(lo, q + 2 * m, bv, bk)) { bv = lo; bk = q + 2 * m; }
+                    if (better(hi, q + 2 * m + 1, bv, bk)) { bv = hi; bk = q + 2 * m + 1; }
+                }
+            }
+        } else {
+            for (int q = k0; q < k1; ++q) {
+                const float v = bf16_lo(row[q]);
+                if (better(v, q, bv, bk)) { bv = v; bk = q; }
+            }
+        }
+    }
+}
+
+template <int SPW>
+__device__ __forceinline__ void wave_select(const void *__restrict__ src, uint32_t mode, int K,
+                                            int64_t L, int64_t seq_row, int64_t t_first,
+                                            int16_t *out, int lane)
+{
+    constexpr int LPS = SPW >= 64 ? 1 : 64 / SPW;   // lanes per step
+    constexpr int SPL = SPW >= 64 ? SPW / 64 : 1;   // steps per lane
+    const bool index_mode = (mode == PDSSM_SEL_I32 || mode == PDSSM_SEL_I16);
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) {
+        const int q = SPW >= 64 ? s * 64 + lane : lane / LPS;
+        const int part = SPW >= 64 ? 0 : lane % LPS;
+        const int64_t t = t_first + q;
+        const bool live = t < L;
+        int k = 0;
+        if (index_mode) {
+            if (live && part == 0)
+                k = (mode == PDSSM_SEL_I32) ? reinterpret_cast<const int32_t *>(src)[seq_row + t]
+                                            : reinterpret_cast<const int16_t *>(src)[seq_row + t];
+        } else {
+            // Slice of the K scores for this lane, a multiple of 8 wide when
+            // K is, so every slice stays 16-byte aligned.
+            int seg = (K + LPS - 1) / LPS;
+            if ((K & 7) == 0)
+                seg = (seg + 7) & ~7;
+            const int k0 = min(part * seg, K), k1 = min(k0 + seg, K);
+            float bv = -__builtin_inff();
+            int bk = K;
+            if (live && k0 < k1)
+                slice_argmax(src, mode, seq_row + t, K, k0, k1, bv, bk);
+#pragma unroll
+            for (int m = 1; m < LPS; m <<= 1) {
+                const float ov = __shfl_xor(bv, m);
+                const int ok = __shfl_xor(bk, m);
+                if (better(ov, ok, bv, bk)) { bv = ov; bk = ok; }
+            }
+            k = bk;
+        }
+        k = (int)min((unsigned)k, (unsigned)(K - 1));
+        if (part == 0)
+            out[q] = (int16_t)(live ? k : 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Split form of the cooperative selection for the common case: one step per
+// lane group of LPS = 64/SPW lanes, K a multiple of 8 (bf16) or 4 (fp32), and
+// a slice of at most 64 bytes per lane.  select_issue() starts the loads (all
+// addresses clamped in range, so they are unconditional); select_finish()
+// reduces them once they have arrived.
+// ---------------------------------------------------------------------------
+struct ScoreSlice {
+    uint4 v[4];
+};
+
+template <int SPW>
+__host__ __device__ constexpr int lanes_per_step() { return SPW >= 64 ? 1 : 64 / SPW; }
+
+__host__ __device__ inline bool select_fast_ok(uint32_t mode, int K, int LPS, int SPW)
+{
+    if (SPW > 64)
+        return false;
+    if (mode == PDSSM_LOGITS_BF16)
+        return (K & 7) == 0 && (((K + LPS - 1) / LPS + 7) & ~7) <= 32;
+    if (mode == PDSSM_LOGITS_F32)
+        return (K & 3) == 0 && (((K + LPS - 1) / LPS + 3) & ~3) <= 16;
+    return true;   // index modes
+}
+
+template <int SPW>
+__device__ __forceinline__ void select_slice(uint32_t mode, int K, int lane, int &k0, int &k1)
+{
+    constexpr int LPS = lanes_per_step<SPW>();
+    const int part = lane % LPS;
+    int seg = (K + LPS - 1) / LPS;
+    seg = (mode == PDSSM_LOGITS_BF16) ? ((seg + 7) & ~7) : ((seg + 3) & ~3);
+    k0 = min(part * seg, K);
+    k1 = min(k0 + seg, K);
+}
+
+template <int SPW>
+__device__ __forceinline__ ScoreSlice select_issue(const void *__restrict__ src, uint32_t mode, int K,
+                                                   int64_t L, int64_t seq_row, int64_t t_first, int lane)
+{
+    constexpr int LPS = lanes_per_step<SPW>();
+    ScoreSlice s;
+    const int q = lane / LPS;
+    const int64_t t = min(t_first + q, L - 1);
+    if (mode == PDSSM_SEL_I32 || mode == PDSSM_SEL_I16) {
+        const int v = (mode == PDSSM_SEL_I32) ? reinterpret_cast<const int32_t *>(src)[seq_row + t]
+                                              : reinterpret_cast<const int16_t *>(src)[seq_row + t];
+        s.v[0].x = (uint32_t)v;
+        return s;
+    }
+    int k0, k1;
+    select_slice<SPW>(mode, K, lane, k0, k1);
+    const int esz = (mode == PDSSM_LOGITS_BF16) ? 2 : 4;
+    const int per = 16 / esz;   // elements per 16-byte vector
+    const char *row = reinterpret_cast<const char *>(src) + (seq_row + t) * (int64_t)K * esz;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int e = min(k0 + v * per, K - per);
+        s.v[v] = *reinterpret_cast<const uint4 *>(row + (int64_t)e * esz);
+    }
+    return s;
+}
+
+template <int SPW>
+__device__ __forceinline__ void select_finish(const ScoreSlice &s, uint32_t mode, int K, int64_t L,
+                                              int64_t t_first, int16_t *out, int lane)
+{
+    constexpr int LPS = lanes_per_step<SPW>();
+    const int q = lane / LPS, part = lane % LPS;
+    const bool live = t_first + q < L;
+    int k;
+    if (mode == PDSSM_SEL_I32 || mode == PDSSM_SEL_I16) {
+        k = (int)s.v[0].x;
+    } else {
+        int k0, k1;
+        select_slice<SPW>(mode, K, lane, k0, k1);
+        float bv = -__builtin_inff();
+        int bk = K;
+        const bool bf = (mode == PDSSM_LOGITS_BF16);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const uint32_t w[4] = {s.v[v].x, s.v[v].y, s.v[v].z, s.v[v].w};
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int kk = bf ? k0 + v * 8 + m : k0 + v * 4 + (m & 3);
+                if (!bf && m >= 4)
+                    continue;
+                const float val = bf ? ((m & 1) ? bf16_hi(w[m >> 1]) : bf16_lo(w[m >> 1]))
+                                     : __uint_as_float(w[m]);
+                if (kk < k1 && better(val, kk, bv, bk)) {
+                    bv = val;
+                    bk = kk;
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 1; m < LPS; m <<= 1) {
+            const float ov = __shfl_xor(bv, m);
+            const int ok = __shfl_xor(bk, m);
+            if (better(ov, ok, bv, bk)) {
+                bv = ov;
+                bk = ok;
+            }
+        }
+        k = bk;
+    }
+    k = (int)min((unsigned)k, (unsigned)(K - 1));
+    if (part == 0)
+        out[q] = (int16_t)(live ? k : 0);
+}
+
+// ---------------------------------------------------------------------------
 // Scatter-add through the wave's LDS scratch:  out[i] = add[i] +
 // sum_{j : pi[j] = i} v[j], over the NP lanes of one group.  `base` is the
 // group's first slot.  Every lane of the wave must call it (convergent).
@@ -174,13 +505,17 @@ __device__ __forceinline__ bool get_word(const uint64_t *p, uint32_t epoch, uint
     return (uint32_t)(w >> 32) == epoch;
 }
 
-// Workspace header (first 256 bytes).
+// Workspace header (first 256 bytes).  The ticket counter has a 128-byte
+// line to itself: every workgroup reads the epoch, and sharing a line with
+// those reads would slow each ticket increment several-fold.
 struct Header {
     uint64_t magic;
     uint32_t epoch;
+    uint32_t reserved0[29];
     uint32_t ticket;
-    uint32_t reserved[60];
+    uint32_t reserved1[31];
 };
+static_assert(sizeof(Header) == 256, "workspace header is 256 bytes");
 // The upper half is an epoch value the library never uses (epochs restart
 // below 0xFFFFFFF0), so no record word can look like the magic.
 constexpr uint64_t kMagic = 0xFFFFFFFF5D55A7B1ull;
