@@ -80,6 +80,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="lm", choices=["lm", "long", "verylong", "small", "tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy (known bytes) so that "
+                         "rocprofv3 byte counters can be scaled")
     ap.add_argument("--cpu-reps", type=int, default=3)
     args = ap.parse_args()
 
@@ -132,22 +135,34 @@ def main() -> int:
           f"{min(per_call_ms) * 1e3:.1f}), {achieved:.0f} GB/s algorithmic, wall {wall:.3f} s",
           file=sys.stderr, flush=True)
 
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 3 x {src.numel()} bytes copied", file=sys.stderr, flush=True)
+        del src, dst
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         threads = cpu_threads()
         host = inp.to("cpu")
         orc = oracle.get()
-        best = None
-        for _ in range(args.cpu_reps):
+        times = []
+        t_start = time.perf_counter()
+        while len(times) < args.cpu_reps or time.perf_counter() - t_start < 2.0:
             c0 = time.perf_counter()
             orc.scan_inputs(host, nthreads=threads)
-            dt = time.perf_counter() - c0
-            best = dt if best is None else min(best, dt)
-        cpu = {"value": tokens / best, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            times.append(time.perf_counter() - c0)
+        times.sort()
+        med = times[len(times) // 2]
+        cpu = {"value": tokens / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
                "sample": f"the whole {args.workload} batch (B={B} H={H} L={L} N={N}), fp64 "
-                         f"sequential oracle, OpenMP over the {B * H} sequences, best of "
-                         f"{args.cpu_reps} runs ({best:.2f} s)"}
+                         f"sequential oracle, OpenMP over the {B * H} sequences, median of "
+                         f"{len(times)} runs ({med:.3f} s each)"}
+        best = med
         print(f"[bench] cpu oracle: {best:.2f} s on {threads} threads", file=sys.stderr, flush=True)
 
     cfgdesc = {
