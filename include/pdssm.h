@@ -84,7 +84,7 @@ extern "C" {
 /* status codes */
 #define PDSSM_OK 0
 #define PDSSM_ERR_NULL -1      /* a required pointer is NULL */
-#define PDSSM_ERR_DIM -2       /* B,H,L < 1, N not in [1,64], K not in [1,32767], or too large */
+#define PDSSM_ERR_DIM -2       /* B,H,L < 1, L > 2^30, N not in [1,64], K not in [1,32767], or too large */
 #define PDSSM_ERR_FLAGS -3     /* unknown flag bits, or a mode the call does not take */
 #define PDSSM_ERR_ALIGN -4     /* a pointer is not 16-byte aligned */
 #define PDSSM_ERR_WORKSPACE -5 /* workspace smaller than the size function returns */

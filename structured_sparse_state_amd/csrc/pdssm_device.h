@@ -30,6 +30,32 @@ __device__ __forceinline__ cf cmul(cf a, cf b)
 // the order.
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
+// Materialise two values here: the compiler may neither sink their
+// computation towards a distant use (which would keep every input of it
+// alive instead of the result) nor recompute them later.
+__device__ __forceinline__ void keep_here(float &a, float &b) { asm volatile("" : "+v"(a), "+v"(b)); }
+
+// A copy of v that the compiler cannot see through: everything derived from
+// it is computed after this point.  Inside a loop this keeps lane-derived
+// constants from being hoisted out and held in registers across the loop.
+__device__ __forceinline__ int opaque(int v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// The same for a wave-uniform value (kept in a scalar register).
+__device__ __forceinline__ int opaque_s(int v)
+{
+    asm volatile("" : "+s"(v));
+    return v;
+}
+__device__ __forceinline__ uint32_t opaque_s(uint32_t v)
+{
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
 // bf16 <-> fp32.  bf16 is the upper half of an fp32 bit pattern.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -257,6 +283,82 @@ __device__ __forceinline__ void group_transpose_sum(float (&v)[T], int i)
     butterfly_from<Butterfly<NP, T>::LOG - 1, T>(v, i);
 }
 
+// The same sum taken in two stages, so that only four per-step registers
+// are live at a time: every four consecutive steps first fold over the two
+// top lane bits of the group (group_fold4, one register out), and the T/4
+// folded registers then finish over the remaining bits (group_finish).
+// Afterwards register r of lane i holds the group sum of step
+//   4 * (r + RF * ((i >> NPLAIN) & (2^NH - 1))) + ((i >> (LOG - 2)) & 3)
+// and every lane whose low NPLAIN bits are zero owns its RF steps.
+template <int NP, int T>
+struct GroupedButterfly {
+    static_assert(T % 4 == 0 && T >= 4, "steps come in groups of four");
+    static constexpr int LOG = Butterfly<NP, T>::LOG;
+    static constexpr int LT4 = Butterfly<NP, T / 4>::LT;
+    static constexpr int NH = LT4 < LOG - 2 ? LT4 : LOG - 2;
+    static constexpr int NPLAIN = LOG - 2 - NH;
+    static constexpr int RF = (T / 4) >> NH;
+
+    __device__ static int step_of(int r, int i)
+    {
+        return 4 * (r + RF * ((i >> NPLAIN) & ((1 << NH) - 1))) + ((i >> (LOG - 2)) & 3);
+    }
+};
+
+template <int NP>
+__device__ __forceinline__ float group_fold4(float (&v)[4], int i)
+{
+    constexpr int LOG = Butterfly<NP, 4>::LOG;
+    butterfly_level<LOG - 1, 4>(v, i);
+    butterfly_level<LOG - 2, 2>(v, i);
+    return v[0];
+}
+
+template <int NP, int R>
+__device__ __forceinline__ void group_finish(float (&w)[R], int i)
+{
+    constexpr int LOG = Butterfly<NP, 4>::LOG;
+    if constexpr (LOG >= 3)
+        butterfly_from<LOG - 3, R>(w, i);
+}
+
+// ds_bpermute with the source given as a byte address (4 * lane).
+__device__ __forceinline__ float bperm_a(float v, int addr)
+{
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v)));
+}
+__device__ __forceinline__ uint32_t bperm_a(uint32_t v, int addr)
+{
+    return (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v);
+}
+
+// Raw buffer access: a wave-uniform base in scalar registers, a per-lane
+// byte offset and a wave-uniform byte offset, so stepping through rows costs
+// no vector arithmetic.  Callers keep every access inside `bytes`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint64_t bytes)
+{
+    const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)n, 0x00020000);
+}
+
+template <typename V>
+__device__ __forceinline__ V bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    V out;
+    if constexpr (sizeof(V) == 8) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        __builtin_memcpy(&out, &v, 8);
+    } else if constexpr (sizeof(V) == 4) {
+        const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+        __builtin_memcpy(&out, &v, 4);
+    } else {
+        static_assert(sizeof(V) == 2, "2, 4 or 8 bytes");
+        const uint16_t v = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+        __builtin_memcpy(&out, &v, 2);
+    }
+    return out;
+}
+
 // ---------------------------------------------------------------------------
 // Cooperative hard selection for SPW consecutive steps of one sequence by
 // one wave.  With SPW <= 64, 64/SPW lanes share a step: each takes a slice of
@@ -338,14 +440,15 @@ __device__ __forceinline__ void wave_select(const void *__restrict__ src, uint32
             if ((K & 7) == 0)
                 seg = (seg + 7) & ~7;
             const int k0 = min(part * seg, K), k1 = min(k0 + seg, K);
-            float bv = -__builtin_inff();
+            float bv = __int_as_float(opaque((int)0xFF800000u));   // -inf, made here
             int bk = K;
             if (live && k0 < k1)
                 slice_argmax(src, mode, seq_row + t, K, k0, k1, bv, bk);
 #pragma unroll
             for (int m = 1; m < LPS; m <<= 1) {
-                const float ov = __shfl_xor(bv, m);
-                const int ok = __shfl_xor(bk, m);
+                const int from = (lane ^ m) << 2;
+                const float ov = bperm_a(bv, from);
+                const int ok = (int)bperm_a((uint32_t)bk, from);
                 if (better(ov, ok, bv, bk)) { bv = ov; bk = ok; }
             }
             k = bk;
@@ -359,25 +462,28 @@ __device__ __forceinline__ void wave_select(const void *__restrict__ src, uint32
 // ---------------------------------------------------------------------------
 // Split form of the cooperative selection for the common case: one step per
 // lane group of LPS = 64/SPW lanes, K a multiple of 8 (bf16) or 4 (fp32), and
-// a slice of at most 64 bytes per lane.  select_issue() starts the loads (all
+// a slice of at most NV 16-byte vectors per lane.  select_issue() starts the loads (all
 // addresses clamped in range, so they are unconditional); select_finish()
 // reduces them once they have arrived.
 // ---------------------------------------------------------------------------
+template <int NV>
 struct ScoreSlice {
-    uint4 v[4];
+    uint4 v[NV];
 };
 
 template <int SPW>
 __host__ __device__ constexpr int lanes_per_step() { return SPW >= 64 ? 1 : 64 / SPW; }
 
-__host__ __device__ inline bool select_fast_ok(uint32_t mode, int K, int LPS, int SPW)
+// The cooperative path needs every lane's slice of a step's K scores to fit
+// NV 16-byte vectors (and K a multiple of the vector width).
+__host__ __device__ inline bool select_fast_ok(uint32_t mode, int K, int LPS, int SPW, int NV)
 {
     if (SPW > 64)
         return false;
     if (mode == PDSSM_LOGITS_BF16)
-        return (K & 7) == 0 && (((K + LPS - 1) / LPS + 7) & ~7) <= 32;
+        return (K & 7) == 0 && (((K + LPS - 1) / LPS + 7) & ~7) <= 8 * NV;
     if (mode == PDSSM_LOGITS_F32)
-        return (K & 3) == 0 && (((K + LPS - 1) / LPS + 3) & ~3) <= 16;
+        return (K & 3) == 0 && (((K + LPS - 1) / LPS + 3) & ~3) <= 4 * NV;
     return true;   // index modes
 }
 
@@ -392,12 +498,12 @@ __device__ __forceinline__ void select_slice(uint32_t mode, int K, int lane, int
     k1 = min(k0 + seg, K);
 }
 
-template <int SPW>
-__device__ __forceinline__ ScoreSlice select_issue(const void *__restrict__ src, uint32_t mode, int K,
-                                                   int64_t L, int64_t seq_row, int64_t t_first, int lane)
+template <int SPW, int NV>
+__device__ __forceinline__ ScoreSlice<NV> select_issue(const void *__restrict__ src, uint32_t mode, int K,
+                                                       int64_t L, int64_t seq_row, int64_t t_first, int lane)
 {
     constexpr int LPS = lanes_per_step<SPW>();
-    ScoreSlice s;
+    ScoreSlice<NV> s = {};
     const int q = lane / LPS;
     const int64_t t = min(t_first + q, L - 1);
     if (mode == PDSSM_SEL_I32 || mode == PDSSM_SEL_I16) {
@@ -412,15 +518,15 @@ __device__ __forceinline__ ScoreSlice select_issue(const void *__restrict__ src,
     const int per = 16 / esz;   // elements per 16-byte vector
     const char *row = reinterpret_cast<const char *>(src) + (seq_row + t) * (int64_t)K * esz;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < NV; ++v) {
         const int e = min(k0 + v * per, K - per);
         s.v[v] = *reinterpret_cast<const uint4 *>(row + (int64_t)e * esz);
     }
     return s;
 }
 
-template <int SPW>
-__device__ __forceinline__ void select_finish(const ScoreSlice &s, uint32_t mode, int K, int64_t L,
+template <int SPW, int NV>
+__device__ __forceinline__ void select_finish(const ScoreSlice<NV> &s, uint32_t mode, int K, int64_t L,
                                               int64_t t_first, int16_t *out, int lane)
 {
     constexpr int LPS = lanes_per_step<SPW>();
@@ -432,11 +538,11 @@ __device__ __forceinline__ void select_finish(const ScoreSlice &s, uint32_t mode
     } else {
         int k0, k1;
         select_slice<SPW>(mode, K, lane, k0, k1);
-        float bv = -__builtin_inff();
+        float bv = __int_as_float(opaque((int)0xFF800000u));   // -inf, made here
         int bk = K;
         const bool bf = (mode == PDSSM_LOGITS_BF16);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
+        for (int v = 0; v < NV; ++v) {
             const uint32_t w[4] = {s.v[v].x, s.v[v].y, s.v[v].z, s.v[v].w};
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
@@ -453,8 +559,19 @@ __device__ __forceinline__ void select_finish(const ScoreSlice &s, uint32_t mode
         }
 #pragma unroll
         for (int m = 1; m < LPS; m <<= 1) {
-            const float ov = __shfl_xor(bv, m);
-            const int ok = __shfl_xor(bk, m);
+            float ov;
+            int ok;
+            if (m == 1) {
+                ov = dpp<kDppXor1>(bv);
+                ok = __float_as_int(dpp<kDppXor1>(__int_as_float(bk)));
+            } else if (m == 2) {
+                ov = dpp<kDppXor2>(bv);
+                ok = __float_as_int(dpp<kDppXor2>(__int_as_float(bk)));
+            } else {
+                const int src = (lane ^ m) << 2;
+                ov = bperm_a(bv, src);
+                ok = (int)bperm_a((uint32_t)bk, src);
+            }
             if (better(ov, ok, bv, bk)) {
                 bv = ov;
                 bk = ok;

@@ -46,11 +46,12 @@ struct ScanArgs {
     uint64_t *agg;
     uint64_t *incl;
     int64_t H, L, S, n_tiles;
+    uint32_t total;   // tiles in the call: n_tiles * S
     int N, K;
     uint32_t sel_mode;
     int y_bf16;
     int dict_lds;   // the head's entry table fits in LDS
-    const uint32_t *tab;   // [H][K][NP]: pi | rank << 8 | indegree << 16 (see prep_kernel)
+    const uint32_t *tab;   // [H][K][NP]: scatter slot | 4 * pi << 16 (see prep_kernel)
 };
 
 // Scan tiling: a chunk is kScanT steps of one group of NP lanes; a wave holds
@@ -62,16 +63,19 @@ struct ScanArgs {
 #define PDSSM_SCAN_W 7
 #endif
 #ifndef PDSSM_SCAN_D
-#define PDSSM_SCAN_D 8
-#endif
-#ifndef PDSSM_SCAN_WAVES_PER_EU
-#define PDSSM_SCAN_WAVES_PER_EU 1
+#define PDSSM_SCAN_D 4
 #endif
 constexpr int kScanT = PDSSM_SCAN_T;
 constexpr int kScanW = PDSSM_SCAN_W;
 constexpr int kScanD = PDSSM_SCAN_D;   // steps of inputs in flight per lane (register ring)
+static_assert(kScanW >= 1 && kScanW <= 32, "chunk waves post into a 32-bit mask");
 constexpr int kDictLdsMax = 32768;   // bytes of the head's entry table kept in LDS
-constexpr int kRegions = 4;          // collision-free scatter regions (ranks 0..3)
+#ifndef PDSSM_SCAN_REGIONS
+#define PDSSM_SCAN_REGIONS 3
+#endif
+constexpr int kRegions = PDSSM_SCAN_REGIONS;   // collision-free scatter regions (ranks 0..kRegions-1)
+constexpr int kRegionBytes = 64 * 8;           // one region: 64 complex slots
+static_assert((kRegions + 1) * kRegionBytes <= 4096, "slot offsets are 12-bit");
 
 __host__ __device__ constexpr int scan_tile_steps(int NP) { return kScanW * (64 / NP) * kScanT; }
 
@@ -124,6 +128,17 @@ __device__ __forceinline__ typename RawVec<CPLX, BCBF>::type zero_raw()
 }
 
 template <bool CPLX, bool BCBF>
+__device__ __forceinline__ typename RawVec<CPLX, BCBF>::type bperm_raw_a(typename RawVec<CPLX, BCBF>::type v, int addr)
+{
+    if constexpr (BCBF)
+        return bperm_a((uint32_t)v, addr);
+    else if constexpr (CPLX)
+        return make_float2(bperm_a(v.x, addr), bperm_a(v.y, addr));
+    else
+        return bperm_a(v, addr);
+}
+
+template <bool CPLX, bool BCBF>
 __device__ __forceinline__ typename RawVec<CPLX, BCBF>::type bperm_raw(typename RawVec<CPLX, BCBF>::type v, int src)
 {
     if constexpr (BCBF)
@@ -135,47 +150,57 @@ __device__ __forceinline__ typename RawVec<CPLX, BCBF>::type bperm_raw(typename 
 }
 
 // ---------------------------------------------------------------------------
-// a4: the carry of one tile, run by wave 0 with lane = state (lanes >= NP
-// idle but convergent).  (api, ad, ae) is the tile's inclusive operator;
-// returns the carry into the tile and publishes the carry out of it.
+// a4: the carry between tiles, run by the carry wave with lane = state
+// (lanes >= NP idle but convergent).  Tile records (decoupled look-back,
+// Merrill & Garland's single-pass scan): AGG = the tile's operator (pi, d,
+// e), INCL = the state after the tile.
+//
+// LookBack gathers the carry into a tile: (bpi, bd, be) = tiles j+1 ..
+// tile-1 composed (latest last); it ends at the first INCL found.  Each
+// poll reads one word of tile j's INCL (lane 0) and of its AGG (lane 1); a
+// record is read whole only once that word is from this call, and read
+// again if any of its words is not yet.
 // ---------------------------------------------------------------------------
 template <int NP, bool CPLX>
-__device__ cf tile_carry(const ScanArgs &a, int64_t tile, int64_t seq, uint32_t epoch, int api,
-                         cf ad, cf ae, cf *scr)
-{
-    constexpr int NC = CPLX ? 2 : 1;
-    constexpr int AW = agg_words<NP, CPLX>(), IW = incl_words<NP, CPLX>();
-    const int lane = threadIdx.x & 63;
-    const bool act = lane < NP;
-    cf xin = {0.f, 0.f};
+struct LookBack {
+    static constexpr int NC = CPLX ? 2 : 1;
+    static constexpr int AW = agg_words<NP, CPLX>(), IW = incl_words<NP, CPLX>();
+    int64_t j = 0, seq = 0;
+    int bpi = 0;
+    cf bd = {1.f, 0.f}, be = {0.f, 0.f}, xin = {0.f, 0.f};
+    bool done = false;
 
-    if (tile == 0) {
-        if (a.x0 && lane < a.N) {
-            const int64_t e = seq * a.N + lane;
-            xin = load_diag<CPLX>(a.x0, e);
-        }
-    } else {
-        // Publish this tile's aggregate so later tiles need not wait for the carry.
-        uint64_t *aw = a.agg + (tile * a.S + seq) * AW;
-        if (act) {
-            put_word(aw + lane, (uint32_t)api, epoch);
-            put_word(aw + NP + lane * NC, __float_as_uint(ad.r), epoch);
-            put_word(aw + NP + NP * NC + lane * NC, __float_as_uint(ae.r), epoch);
-            if constexpr (CPLX) {
-                put_word(aw + NP + lane * NC + 1, __float_as_uint(ad.i), epoch);
-                put_word(aw + NP + NP * NC + lane * NC + 1, __float_as_uint(ae.i), epoch);
-            }
-        }
-        // Look back: (bpi, bd, be) = tiles j+1 .. tile-1 composed, latest last.
-        int bpi = lane;
-        cf bd = {1.f, 0.f}, be = {0.f, 0.f};
-        int64_t j = tile - 1;
-        while (true) {
-            const int64_t rj = j * a.S + seq;
+    __device__ void start(const ScanArgs &a, int64_t tile, int64_t sq, int lane)
+    {
+        seq = sq;
+        bpi = lane;
+        bd = {1.f, 0.f};
+        be = {0.f, 0.f};
+        xin = {0.f, 0.f};
+        j = tile - 1;
+        done = tile == 0;
+        if (done && a.x0 && lane < a.N)
+            xin = load_diag<CPLX>(a.x0, sq * a.N + lane);
+    }
+
+    // One poll; true when it made progress (found the INCL or took an AGG).
+    __device__ bool step(const ScanArgs &a, uint32_t epoch, int lane, cf *scr)
+    {
+        const bool act = lane < NP;
+        const int64_t rj = j * a.S + seq;
+        const uint64_t *iw = a.incl + rj * IW;
+        const uint64_t *w = a.agg + rj * AW;
+        uint32_t pw = 0;
+        bool pok = false;
+        if (lane == 0)
+            pok = get_word(iw, epoch, pw);
+        else if (lane == 1 && j > 0)
+            pok = get_word(w, epoch, pw);
+        const uint64_t ready = __ballot(pok);
+        if (ready & 1) {
             bool ok = true;
             cf X = {0.f, 0.f};
             if (act) {
-                const uint64_t *iw = a.incl + rj * IW;
                 uint32_t u0 = 0, u1 = 0;
                 ok = get_word(iw + lane * NC, epoch, u0);
                 if constexpr (CPLX)
@@ -184,47 +209,72 @@ __device__ cf tile_carry(const ScanArgs &a, int64_t tile, int64_t seq, uint32_t 
             }
             if (__all(ok)) {
                 xin = scatter_add<CPLX>(scr, lane, 0, bpi, cmul(bd, X), be);
-                break;
+                done = true;
+                return true;
             }
-            if (j > 0) {
-                ok = true;
-                int p = lane;
-                cf d = {1.f, 0.f}, e = {0.f, 0.f};
-                if (act) {
-                    const uint64_t *w = a.agg + rj * AW;
-                    uint32_t up = 0, dr = 0, di = 0, er = 0, ei = 0;
-                    ok = get_word(w + lane, epoch, up);
-                    ok = get_word(w + NP + lane * NC, epoch, dr) && ok;
-                    ok = get_word(w + NP + NP * NC + lane * NC, epoch, er) && ok;
-                    if constexpr (CPLX) {
-                        ok = get_word(w + NP + lane * NC + 1, epoch, di) && ok;
-                        ok = get_word(w + NP + NP * NC + lane * NC + 1, epoch, ei) && ok;
-                    }
-                    p = (int)min(up, (uint32_t)(NP - 1));
-                    d = {__uint_as_float(dr), __uint_as_float(di)};
-                    e = {__uint_as_float(er), __uint_as_float(ei)};
+        } else if (ready & 2) {
+            bool ok = true;
+            int p = lane;
+            cf d = {1.f, 0.f}, e = {0.f, 0.f};
+            if (act) {
+                uint32_t up = 0, dr = 0, di = 0, er = 0, ei = 0;
+                ok = get_word(w + lane, epoch, up);
+                ok = get_word(w + NP + lane * NC, epoch, dr) && ok;
+                ok = get_word(w + NP + NP * NC + lane * NC, epoch, er) && ok;
+                if constexpr (CPLX) {
+                    ok = get_word(w + NP + lane * NC + 1, epoch, di) && ok;
+                    ok = get_word(w + NP + NP * NC + lane * NC + 1, epoch, ei) && ok;
                 }
-                if (__all(ok)) {
-                    // acc <- acc o agg_j  (acc is later in time)
-                    const int npi = bperm(bpi, p);
-                    cf gd;
-                    gd.r = bperm(bd.r, p);
-                    gd.i = CPLX ? bperm(bd.i, p) : 0.f;
-                    const cf ne = scatter_add<CPLX>(scr, lane, 0, bpi, cmul(bd, e), be);
-                    bpi = npi;
-                    bd = cmul(gd, d);
-                    be = ne;
-                    --j;
-                    continue;
-                }
+                p = (int)min(up, (uint32_t)(NP - 1));
+                d = {__uint_as_float(dr), __uint_as_float(di)};
+                e = {__uint_as_float(er), __uint_as_float(ei)};
             }
-            __builtin_amdgcn_s_sleep(2);
+            if (__all(ok)) {
+                // acc <- acc o agg_j  (acc is later in time)
+                const int npi = bperm(bpi, p);
+                cf gd;
+                gd.r = bperm(bd.r, p);
+                gd.i = CPLX ? bperm(bd.i, p) : 0.f;
+                const cf ne = scatter_add<CPLX>(scr, lane, 0, bpi, cmul(bd, e), be);
+                bpi = npi;
+                bd = cmul(gd, d);
+                be = ne;
+                --j;
+                return true;
+            }
+        }
+        return false;
+    }
+};
+
+// Publish a tile's AGG record (tile > 0 only; tile 0 knows its carry).
+template <int NP, bool CPLX>
+__device__ void publish_agg(const ScanArgs &a, int64_t tile, int64_t seq, uint32_t epoch, int lane, int api,
+                            cf ad, cf ae)
+{
+    constexpr int NC = CPLX ? 2 : 1;
+    uint64_t *aw = a.agg + (tile * a.S + seq) * agg_words<NP, CPLX>();
+    if (lane < NP) {
+        put_word(aw + lane, (uint32_t)api, epoch);
+        put_word(aw + NP + lane * NC, __float_as_uint(ad.r), epoch);
+        put_word(aw + NP + NP * NC + lane * NC, __float_as_uint(ae.r), epoch);
+        if constexpr (CPLX) {
+            put_word(aw + NP + lane * NC + 1, __float_as_uint(ad.i), epoch);
+            put_word(aw + NP + NP * NC + lane * NC + 1, __float_as_uint(ae.i), epoch);
         }
     }
+}
 
+// The state after the tile from its carry-in: publish INCL, and x_final
+// after the last tile.
+template <int NP, bool CPLX>
+__device__ void publish_incl(const ScanArgs &a, int64_t tile, int64_t seq, uint32_t epoch, int lane, int api,
+                             cf ad, cf ae, cf xin, cf *scr)
+{
+    constexpr int NC = CPLX ? 2 : 1;
     const cf xout = scatter_add<CPLX>(scr, lane, 0, api, cmul(ad, xin), ae);
-    if (act) {
-        uint64_t *iw = a.incl + (tile * a.S + seq) * IW;
+    if (lane < NP) {
+        uint64_t *iw = a.incl + (tile * a.S + seq) * incl_words<NP, CPLX>();
         put_word(iw + lane * NC, __float_as_uint(xout.r), epoch);
         if constexpr (CPLX)
             put_word(iw + lane * NC + 1, __float_as_uint(xout.i), epoch);
@@ -235,307 +285,544 @@ __device__ cf tile_carry(const ScanArgs &a, int64_t tile, int64_t seq, uint32_t 
         if constexpr (CPLX)
             a.xfinal[e + 1] = xout.i;
     }
-    return xin;
 }
 
 // ---------------------------------------------------------------------------
-// The fused scan kernel: one workgroup per tile.  Workgroups take tiles from
-// an atomic ticket in tile-major order (index u = tile * S + seq), so every
-// tile waits only on tiles that hold a smaller ticket -- tiles that are
-// already running or done -- and the look-back cannot deadlock.
+// The fused scan kernel.  Persistent workgroups take tiles from an atomic
+// ticket in tile-major order (u = tile * S + seq) and run them one after
+// another.  A workgroup holds at most two tickets, its current tile and the
+// next one, and starts the next only once the current tile's carry is out.
+// So the smallest unfinished ticket always belongs to a current tile, whose
+// look-back waits only on smaller tickets -- all finished: no deadlock.
 //
-// Waves 0..W-1 ("chunk waves") each own G chunks of T steps.  Wave W (the
-// "carry wave") stages the dictionary table, chains the chunk operators of
-// the tile and runs the look-back.  The two roles run on separate
-// wave-uniform paths that meet only at barriers, so the chunk waves'
-// per-step readout state never has to share registers with the carry code.
+// Waves 0..W-1 ("chunk waves") each own G chunks of T steps of the tile.
+// Wave W (the "carry wave") takes the tickets, stages the dictionary table,
+// chains the chunk operators and runs the look-back (while the chunk waves
+// are busy: the carry into a tile depends only on earlier tiles).  Per tile:
+//
+//   chunk waves:  local pass, post operator       (B) start the next tile's loads (C) readout (D) ... next selection
+//   carry wave:   next ticket, chain as
+//                 operators come, look-back       (B) next table, previous y,
+//                                                     publish                     (C)         (D)
+//
+// so the next tile's router scores and first input steps are in flight
+// while the carry of the current one is worked out.  The two roles run on
+// separate wave-uniform paths that meet only at barriers.
 // ---------------------------------------------------------------------------
+// Waves per SIMD the scan kernel is compiled for: six (three 8-wave
+// workgroups per CU) where the register allocator fits that without
+// spilling, else no constraint.
 template <int NP, bool CPLX, bool BCBF>
-__global__ void __launch_bounds__((kScanW + 1) * 64) __attribute__((amdgpu_waves_per_eu(PDSSM_SCAN_WAVES_PER_EU))) scan_kernel(ScanArgs a)
+constexpr int scan_waves_per_eu()
+{
+#ifdef PDSSM_SCAN_WAVES_PER_EU
+    return PDSSM_SCAN_WAVES_PER_EU;
+#else
+    return (!CPLX || (BCBF && NP == 64)) ? 6 : 1;
+#endif
+}
+
+template <int NP, bool CPLX, bool BCBF>
+__global__ void __launch_bounds__((kScanW + 1) * 64)
+__attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_kernel(ScanArgs a)
 {
     constexpr int W = kScanW, T = kScanT, G = 64 / NP, C = W * G, TILE = C * T, SLOTS = W * 64;
+    constexpr int NV = (G == 1) ? 2 : 4;   // 16-byte score vectors per lane in the fast selection
     using Raw = typename RawVec<CPLX, BCBF>::type;
     using DRaw = typename std::conditional<CPLX, float2, float>::type;
     using Stored = typename std::conditional<BCBF, typename std::conditional<CPLX, uint32_t, uint16_t>::type, Raw>::type;
-    // Entry table: the head's [K][NP] (pi | rank << 8 | indegree << 16) when
-    // it fits, else this tile's entries per (wave, step, lane).
+    // Entry table: the head's [K][NP] (scatter slot | 4 * pi << 16) when it
+    // fits, else the tile's entries per (wave, step, lane).
     extern __shared__ __attribute__((aligned(16))) uint32_t s_tab[];
     __shared__ int16_t s_sel[W][G * T];
-    __shared__ cf s_reg[W][kRegions + 1][64];   // scatter regions; the last one takes ranks >= kRegions
+    __shared__ __attribute__((aligned(16))) cf s_reg[W][kRegions + 1][64];   // scatter regions, plus a spare one for ranks >= kRegions
     __shared__ cf s_scr[W + 1][64];
     __shared__ int s_pi[SLOTS];   // chunk operators, then their inclusive prefixes
     __shared__ cf s_d[SLOTS];
     __shared__ cf s_e[SLOTS];
     __shared__ cf s_xin[64];
-    __shared__ uint32_t s_ticket;
+    __shared__ float s_y[TILE];   // a finished tile's outputs, stored by the carry wave
+    __shared__ float s_q[TILE];   // per step: sum_j Re(c_t[j] x_loc_t[j]), until the correction
+    __shared__ uint32_t s_next;   // ticket published by the carry wave
+    __shared__ uint32_t s_ready;  // bit w: chunk wave w has posted its operators
 
     // Tile indices, sequences and heads fit 32 bits (the host checks).
-    const uint32_t S32 = (uint32_t)a.S, H32 = (uint32_t)a.H;
+    const uint32_t S32 = (uint32_t)a.S, H32 = (uint32_t)a.H, total = a.total;
     const int N = a.N, K = a.K;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    if (tid == 0)
-        s_ticket = atomicAdd(&a.hdr->ticket, 1u);
-    __syncthreads();
-    const uint32_t u = s_ticket;
-    const uint32_t tile = u / S32, seq = u - tile * S32;
-    const uint32_t h = seq % H32;
-    const int64_t tile_t0 = (int64_t)tile * TILE;
-    const int64_t seq_row = (int64_t)seq * a.L;
-    const uint32_t *tab_h = a.tab + h * (int64_t)K * NP;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
 
     if (wave == W) {
         // ================= carry wave =================
+        auto take_ticket = [&]() -> uint32_t {
+            uint32_t t = 0;
+            if (lane == 0)
+                t = atomicAdd(&a.hdr->ticket, 1u);
+            return __builtin_amdgcn_readfirstlane(t);
+        };
         // The head's entry table straight to LDS (16 bytes per lane per
-        // instruction, no registers involved).
-        if (a.dict_lds) {
+        // instruction, no registers involved); waited for before (C).
+        auto stage_table = [&](uint32_t u) {
+            if (!a.dict_lds)
+                return;
+            const uint32_t h = __builtin_amdgcn_readfirstlane((u % S32) % H32);
+            const uint4 *src = reinterpret_cast<const uint4 *>(a.tab + h * (int64_t)K * NP);
             const int tab_vecs = (K * NP) >> 2;   // 4 entries per 16 bytes
-            const uint4 *src = reinterpret_cast<const uint4 *>(tab_h);
             for (int w0 = 0; w0 < tab_vecs; w0 += 64) {
                 const int w = min(w0 + lane, tab_vecs - 1);
                 __builtin_amdgcn_global_load_lds(
                     src + w, (__attribute__((address_space(3))) void *)(reinterpret_cast<uint8_t *>(s_tab) + w0 * 16),
                     16, 0, 0);
             }
+        };
+        uint32_t cur = take_ticket();
+        if (lane == 0) {
+            s_next = cur;
+            s_ready = 0;
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the copy has landed
         const uint32_t epoch = a.hdr->epoch;
-        __syncthreads();   // (1) table ready
-        __syncthreads();   // (2) chunk operators ready
+        __syncthreads();   // (P) first ticket published
+        if (cur >= total)
+            return;
+        stage_table(cur);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();   // (Q) first table and selections ready
 
-        // ---- a3: chain the C chunk operators in time order; slot c then
-        // holds the operator of chunks 0..c of the tile.  Lane = state;
-        // lanes >= NP carry an identity that touches only their own slot.
+        // The outputs of tile u, staged in s_y by the chunk waves.
+        auto store_y = [&](uint32_t u) {
+            const uint32_t tile = __builtin_amdgcn_readfirstlane(u / S32), seq = u - tile * S32;
+            const int64_t t0 = (int64_t)tile * TILE;
+            const int64_t y0 = (int64_t)seq * a.L + t0;
+            for (int k = lane; k < TILE; k += 64) {
+                if (t0 + k < a.L) {
+                    if (a.y_bf16)
+                        reinterpret_cast<uint16_t *>(a.y)[y0 + k] = f32_to_bf16_rne(s_y[k]);
+                    else
+                        reinterpret_cast<float *>(a.y)[y0 + k] = s_y[k];
+                }
+            }
+        };
         const bool act = lane < NP;
         const int l = act ? lane : 0;
-        int ppi = act ? lane : 0;
-        cf pd = {1.f, 0.f}, pe = {0.f, 0.f};
         cf *scr = s_scr[W];
-        for (int c = 0; c < C; ++c) {
-            const int base = c * NP;
-            const int cpi = act ? s_pi[base + l] : lane;
-            const cf cd = act ? s_d[base + l] : cf{1.f, 0.f};
-            const cf ce = act ? s_e[base + l] : cf{0.f, 0.f};
-            // (op_c o prefix): pi[j] = cpi[ppi[j]], d[j] = cd[ppi[j]] * pd[j],
-            // e = P_c D_c pe + ce.
-            const int npi = s_pi[base + ppi];
-            const cf gd = s_d[base + ppi];
-            const cf ne = scatter_add<CPLX>(scr, lane, 0, cpi, act ? cmul(cd, pe) : cf{0.f, 0.f}, ce);
-            if (act) {
-                ppi = npi;
-                pd = cmul(gd, pd);
-                pe = ne;
-                s_pi[base + lane] = ppi;
-                s_d[base + lane] = pd;
-                s_e[base + lane] = pe;
+        bool have_prev = false;
+        uint32_t prev = 0;
+        LookBack<NP, CPLX> lb;
+        while (true) {
+            const uint32_t nxt = take_ticket();
+            if (lane == 0)
+                s_next = nxt;
+            const uint32_t tile = __builtin_amdgcn_readfirstlane(cur / S32), seq = cur - tile * S32;
+            lb.start(a, tile, seq, lane);
+
+            // ---- a3 + a4 while the chunk waves run their local pass: chain
+            // the C chunk operators in time order as their waves post them
+            // (slot c then holds the operator of chunks 0..c of the tile;
+            // lane = state, lanes >= NP carry an identity; the index and
+            // factor gathers are lane moves, only the scatter of e goes
+            // through LDS), and in between look back for the carry into
+            // this tile, which depends only on earlier tiles.
+            int ppi = lane;
+            cf pd = {1.f, 0.f}, pe = {0.f, 0.f};
+            int wnext = 0;   // next chunk wave whose operators to take
+            while (wnext < W) {
+                const uint32_t posted = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile uint32_t *>(&s_ready));
+                if ((posted >> wnext) & 1u) {
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+                    for (int k = 0; k < G; ++k) {
+                        const int base = (wnext * G + k) * NP;
+                        const int cpi = act ? s_pi[base + l] : lane;
+                        const cf cd = act ? s_d[base + l] : cf{1.f, 0.f};
+                        const cf ce = act ? s_e[base + l] : cf{0.f, 0.f};
+                        // (op_c o prefix): pi[j] = cpi[ppi[j]], d[j] = cd[ppi[j]] * pd[j],
+                        // e = P_c D_c pe + ce.
+                        const int src = ppi * 4;
+                        const int npi = (int)bperm_a((uint32_t)cpi, src);
+                        cf gd;
+                        gd.r = bperm_a(cd.r, src);
+                        gd.i = CPLX ? bperm_a(cd.i, src) : 0.f;
+                        pe = scatter_add<CPLX>(scr, lane, 0, cpi, cmul(cd, pe), ce);
+                        ppi = npi;
+                        pd = cmul(gd, pd);
+                        if (act) {
+                            s_pi[base + lane] = ppi;
+                            s_d[base + lane] = pd;
+                            s_e[base + lane] = pe;
+                        }
+                    }
+                    ++wnext;
+                    continue;
+                }
+                if (!lb.done && lb.step(a, epoch, lane, scr))
+                    continue;
+                __builtin_amdgcn_s_sleep(1);
             }
-            lds_order();
+            __syncthreads();   // (B) all chunk operators taken, next ticket published
+            if (lane == 0)
+                s_ready = 0;
+            const bool more = nxt < total;
+            if (more)
+                stage_table(nxt);
+            // The previous tile's outputs: the chunk waves staged them in s_y
+            // after its (D), before this (B).
+            if (have_prev)
+                store_y(prev);
+            // ---- a4, second part: publish the tile's aggregate if the carry
+            // is still unknown (so later tiles need not wait for it), then the
+            // state after the tile.
+            if (!lb.done) {
+                publish_agg<NP, CPLX>(a, tile, seq, epoch, lane, ppi, pd, pe);
+                while (!lb.done)
+                    if (!lb.step(a, epoch, lane, scr))
+                        __builtin_amdgcn_s_sleep(2);
+            }
+            publish_incl<NP, CPLX>(a, tile, seq, epoch, lane, ppi, pd, pe, lb.xin, scr);
+            s_xin[lane] = lb.xin;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next table has landed
+            __syncthreads();   // (C) carry ready, next table staged
+            __syncthreads();   // (D) chunk waves have read the prefixes and the carry
+            if (!more)
+                return;
+            prev = cur;
+            have_prev = true;
+            cur = nxt;
         }
-        // ---- a4: carry into / out of the tile.
-        s_xin[lane] = tile_carry<NP, CPLX>(a, (int64_t)tile, (int64_t)seq, epoch, act ? ppi : lane,
-                                           act ? pd : cf{1.f, 0.f}, act ? pe : cf{0.f, 0.f}, scr);
-        __syncthreads();   // (3) carry ready
-        return;
     }
 
     // ================= chunk waves =================
-    const int g = lane / NP, i = lane % NP, chunk = wave * G + g, gbase = g * NP;
-    const int icl = min(i, N - 1);
-    const bool sel_fast = select_fast_ok(a.sel_mode, K, lanes_per_step<G * T>(), G * T);
-
-    // ---- Router-score slice of this wave's steps first (the selection
-    // needs it before any step can run) ...
-    ScoreSlice sc;
-    if (sel_fast)
-        sc = select_issue<G * T>(a.sel, a.sel_mode, K, a.L, seq_row, tile_t0 + (int64_t)wave * G * T, lane);
-    // ... then the chunk's step inputs, streamed through a ring of D
-    // register slots: the first D steps now, step t + D once step t is used.
-    // Addresses are clamped in range (steps past the end reload the last
-    // row), so every load is unconditional.
+    // Lane roles: group g of NP lanes runs chunk wave * G + g; lane i of the
+    // group holds state i.  Every phase below derives them from its own
+    // opaque copy of the lane index, so that per-lane constants are made
+    // where they are used instead of being held across the whole loop.
+    struct Lanes {
+        int ln, g, i, gbase, icl;
+        bool row_ok;   // padding rows (i >= N) hold no state
+    };
+    auto lanes = [&]() {
+        Lanes q;
+        q.ln = opaque(lane);
+        q.g = (G == 1) ? 0 : q.ln / NP;
+        q.i = (G == 1) ? q.ln : q.ln % NP;
+        q.gbase = q.g * NP;
+        q.icl = min(q.i, N - 1);
+        q.row_ok = q.i < N;
+        return q;
+    };
+    const bool sel_fast = select_fast_ok(a.sel_mode, K, lanes_per_step<G * T>(), G * T, NV);
     constexpr int D = kScanD < T ? kScanD : T;
-    const int64_t tc0 = tile_t0 + (int64_t)chunk * T;
-    const int64_t row0 = seq_row + (tc0 < a.L ? tc0 : a.L - 1);
-    const int last = tc0 < a.L ? (int)min((int64_t)(T - 1), a.L - 1 - tc0) : 0;
-    const DRaw *dbase = reinterpret_cast<const DRaw *>(a.diag) + row0 * N;
-    const Stored *bbase = reinterpret_cast<const Stored *>(a.b) + row0 * N;
-    const Stored *cbase = reinterpret_cast<const Stored *>(a.c) + row0 * N;
+
+    // ---- Streaming state of the tile whose loads are in flight: the
+    // router-score slice of the wave's steps (the selection needs it first)
+    // and the chunk's step inputs, streamed through a ring of D register
+    // slots: the first D steps at issue, step t + D once step t is used.
+    // Buffer resources start at the wave's first row.  Rows past the end of
+    // the sequence are clamped to the last one, so every load is in range;
+    // with one chunk per wave the row offset is wave-uniform (scalar), and in
+    // a whole wave a lane's offset is fixed while the row offset steps.
+    ScoreSlice<NV> sc;
+    __amdgpu_buffer_rsrc_t rsd, rsb, rsc;
+    const int L = (int)a.L;   // steps fit 31 bits (the host checks)
+    int64_t row0 = 0;         // index of the sequence's first step
+    int tw0 = 0, wrow = 0;    // the wave's first step; the first buffer row
+    bool full = false;        // every chunk of the wave lies inside the sequence
+    uint32_t h = 0;
     DRaw dv[D];
     Raw bv[D], cv[D];
-    auto fetch = [&](int tt) {
-        const int off = min(tt, last) * N + icl;
-        dv[tt % D] = dbase[off];
-        bv[tt % D] = (Raw)bbase[off];
-        cv[tt % D] = (Raw)cbase[off];
-    };
-#pragma unroll
-    for (int tt = 0; tt < D; ++tt)
-        fetch(tt);
-    const int64_t tw0 = tile_t0 + (int64_t)wave * G * T;   // first step of the wave
-
-    // ---- a1: selection of this wave's G*T consecutive steps.
-    if (sel_fast)
-        select_finish<G * T>(sc, a.sel_mode, K, a.L, tw0, s_sel[wave], lane);
-    else
-        wave_select<G * T>(a.sel, a.sel_mode, K, a.L, seq_row, tw0, s_sel[wave], lane);
-
-    // ---- When the head's entry table does not fit in LDS, this wave's
-    // entries straight from the table in memory.
-    if (!a.dict_lds) {
-        lds_order();
-        for (int tt = 0; tt < T; ++tt) {
-            const int k = s_sel[wave][g * T + tt];
-            s_tab[(wave * T + tt) * 64 + lane] = tab_h[(int64_t)k * NP + i];
+    auto fetch = [&](const Lanes &q, int tt) {
+        uint32_t el, row_el;
+        if (G == 1 || full) {
+            el = (uint32_t)(q.g * T * N + q.icl);
+            row_el = (uint32_t)((min(tw0 + tt, L - 1) - wrow) * N);   // == tt * N in a whole wave
+        } else {
+            el = (uint32_t)((min(tw0 + q.g * T + tt, L - 1) - wrow) * N + q.icl);
+            row_el = 0;
         }
-    }
-    __syncthreads();   // (1) table ready
-
-    // ---- a2 + chunk-local a3: recurrence from zero state, and the prefix
-    // operator of the chunk (source j sits at pacc[j] with factor dacc[j]).
-    cf *scr = s_scr[wave];
-    cf x = {0.f, 0.f};
-    int pacc = i;
-    cf dacc = {1.f, 0.f};
-    float q[T], gr[T], gi[T];
-    Raw craw_prev = zero_raw<CPLX, BCBF>();
-    // With one chunk per wave the step's selection is wave-uniform: keep
-    // the chunk's selections in one register and broadcast them per step.
-    int selv = 0;
-    if constexpr (G == 1)
-        selv = s_sel[wave][lane % T];
-    auto entry = [&](int tt) {
-        if (!a.dict_lds)
-            return s_tab[(wave * T + tt) * 64 + lane];
-        const int k = (G == 1) ? __builtin_amdgcn_readlane(selv, tt) : (int)s_sel[wave][g * T + tt];
-        return s_tab[k * NP + i];
+        dv[tt % D] = bload<DRaw>(rsd, el * (uint32_t)sizeof(DRaw), row_el * (uint32_t)sizeof(DRaw));
+        bv[tt % D] = (Raw)bload<Stored>(rsb, el * (uint32_t)sizeof(Stored), row_el * (uint32_t)sizeof(Stored));
+        cv[tt % D] = (Raw)bload<Stored>(rsc, el * (uint32_t)sizeof(Stored), row_el * (uint32_t)sizeof(Stored));
     };
-    uint32_t ent_next = entry(0);
+    // Two parts: the router scores (and the tile's geometry), then the
+    // first D input steps.
+    auto issue_scores = [&](uint32_t u) {
+        const Lanes q = lanes();
+        const uint32_t tile = __builtin_amdgcn_readfirstlane(u / S32);
+        const uint32_t seq = u - tile * S32;
+        h = __builtin_amdgcn_readfirstlane(seq % H32);
+        row0 = (int64_t)seq * a.L;
+        tw0 = (int)tile * TILE + wave * G * T;
+        full = tw0 + G * T <= L;
+        // Assigned on every path, so no older value is kept around the loop.
+        sc = sel_fast ? select_issue<G * T, NV>(a.sel, opaque_s(a.sel_mode), opaque_s(K), a.L, row0, tw0, q.ln)
+                      : ScoreSlice<NV>{};
+    };
+    auto issue_inputs = [&]() {
+        const Lanes q = lanes();
+        wrow = min(tw0, L - 1);
+        const uint64_t rem = (uint64_t)(L - wrow) * (uint64_t)N;   // elements to the end of the sequence
+        const int64_t e0 = (row0 + wrow) * N;
+        rsd = make_rsrc(reinterpret_cast<const DRaw *>(a.diag) + e0, rem * sizeof(DRaw));
+        rsb = make_rsrc(reinterpret_cast<const Stored *>(a.b) + e0, rem * sizeof(Stored));
+        rsc = make_rsrc(reinterpret_cast<const Stored *>(a.c) + e0, rem * sizeof(Stored));
 #pragma unroll
-    for (int tt = 0; tt < T; ++tt) {
-        const bool valid = (tc0 + tt < a.L) && (i < N);
-        const uint32_t ent = ent_next;
-        if (tt + 1 < T)
-            ent_next = entry(tt + 1);
-        const int p = valid ? (int)(ent & 0xFF) : i;
-        const int rank = valid ? (int)((ent >> 8) & 0xFF) : 0;
-        const int deg = valid ? (int)((ent >> 16) & 0xFF) : 1;
-        const int sl = tt % D;
-        cf d;
-        if constexpr (CPLX)
-            d = valid ? cf{dv[sl].x, dv[sl].y} : cf{1.f, 0.f};
+        for (int tt = 0; tt < D; ++tt)
+            fetch(q, tt);
+    };
+    // ---- a1: selection of the wave's G*T consecutive steps of the tile
+    // whose loads are in flight (and, when the head's entry table does not
+    // fit in LDS, the wave's entries straight from the table in memory).
+    auto select = [&]() {
+        const Lanes q = lanes();
+        const int Kq = opaque_s(K);
+        const uint32_t mode = opaque_s(a.sel_mode);
+        if (sel_fast)
+            select_finish<G * T, NV>(sc, mode, Kq, a.L, tw0, s_sel[wave], q.ln);
         else
-            d = valid ? cf{dv[sl], 0.f} : cf{1.f, 0.f};
-        const cf b = valid ? unpack_raw<CPLX, BCBF>(bv[sl]) : cf{0.f, 0.f};
-        const Raw craw = valid ? cv[sl] : zero_raw<CPLX, BCBF>();
-        const cf c = unpack_raw<CPLX, BCBF>(craw);
-        if (tt + D < T)
-            fetch(tt + D);
-        // x_t = P_t (d_t * x_{t-1}) + b_t.  Source j goes to region rank(j)
-        // at row pi(j): within a region every row has at most one source, so
-        // plain stores suffice.  Row i then reads the regions below its
-        // in-degree -- exactly the slots written in this step, so stale
-        // slots are never read and nothing needs clearing.  Sources of rank
-        // >= kRegions (rare) add atomically into the last region.
-        {
-            const cf v = cmul(d, x);
-            const int ri = rank < kRegions ? rank : kRegions;
-            s_reg[wave][ri][gbase + p] = v;
+            wave_select<G * T>(a.sel, mode, Kq, a.L, row0, tw0, s_sel[wave], q.ln);
+        if (!a.dict_lds) {
             lds_order();
-            if (__any(rank >= kRegions)) {
-                if (rank >= kRegions) {
-                    atomicAdd(&s_reg[wave][kRegions - 1][gbase + p].r, v.r);
-                    if constexpr (CPLX)
-                        atomicAdd(&s_reg[wave][kRegions - 1][gbase + p].i, v.i);
-                }
+            const uint32_t *tab_h = a.tab + h * (int64_t)K * NP;
+            uint32_t *tb = s_tab + wave * T * 64 + q.ln;
+            for (int tt = 0; tt < T; ++tt) {
+                const int k = s_sel[wave][q.g * T + tt];
+                tb[tt * 64] = tab_h[k * NP + q.i];
+            }
+        }
+        lds_order();
+    };
+
+    __syncthreads();   // (P) first ticket published
+    uint32_t cur = __builtin_amdgcn_readfirstlane(s_next);
+    if (cur >= total)
+        return;
+    issue_scores(cur);
+    issue_inputs();
+    select();
+    // The scatter regions start cleared; every step clears what it reads.
+#pragma unroll
+    for (int r = 0; r < kRegions; ++r)
+        s_reg[wave][r][lane] = cf{0.f, 0.f};
+    __syncthreads();   // (Q) first table and selections ready
+
+    while (true) {
+        const Lanes q = lanes();
+        // ---- a2 + chunk-local a3: recurrence from zero state, and the
+        // prefix operator of the chunk: source j of the chunk start sits at
+        // lane pa4 / 4 (a byte address, as ds_bpermute takes it) with factor
+        // dacc[j].  Steps past the end of the sequence are skipped (the
+        // identity).  Padding rows only ever exchange values among
+        // themselves; they are kept out of the two sums over rows (the
+        // readout and its correction).
+        // (issue() moves tw0 and row0 on to the next tile before the readout.)
+        const int cw0 = tw0;                // the wave's first step
+        const int tc0 = cw0 + q.g * T;      // first step of the chunk
+        const int64_t y0 = row0 + cw0;      // y index of the wave's first step
+        const int nvalid = max(0, min(T, L - tc0));
+        char *const regp = reinterpret_cast<char *>(&s_reg[wave][0][0]) + q.gbase * (int)sizeof(cf);
+        const uint32_t *const tb = s_tab + (a.dict_lds ? q.i : wave * T * 64 + q.ln);
+        cf x = {0.f, 0.f};
+        int pa4 = q.ln * 4;
+        cf dacc = {1.f, 0.f};
+        float qg[4], w[T / 4], gr[T], gi[T];
+        Raw craw_prev = zero_raw<CPLX, BCBF>();
+        // With one chunk per wave the step's selection is wave-uniform: keep
+        // the chunk's selections in one register and broadcast them per step.
+        int selv = 0;
+        if constexpr (G == 1)
+            selv = s_sel[wave][q.ln % T];
+        auto entry = [&](int tt) -> uint32_t {
+            if (a.dict_lds) {
+                const int k = (G == 1) ? __builtin_amdgcn_readlane(selv, tt) : (int)s_sel[wave][q.g * T + tt];
+                return tb[k * NP];
+            }
+            return tb[tt * 64];
+        };
+        uint32_t ent_next = entry(0);
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+            const uint32_t ent = ent_next;
+            if (tt + 1 < T)
+                ent_next = entry(tt + 1);
+            const int sl = tt % D;
+            cf d;
+            if constexpr (CPLX)
+                d = {dv[sl].x, dv[sl].y};
+            else
+                d = {dv[sl], 0.f};
+            const cf b = unpack_raw<CPLX, BCBF>(bv[sl]);
+            const Raw craw = cv[sl];
+            const cf c = unpack_raw<CPLX, BCBF>(craw);
+            if (tt + D < T)
+                fetch(q, tt + D);
+            // Readout weight of step t-1, through the prefix operator before
+            // step t:  Re(c_{t-1} . P D X) = Re(sum_j g_{t-1}[j] X[j]) with
+            // g_{t-1}[j] = c_{t-1}[pacc_{t-1}[j]] * dacc_{t-1}[j].
+            if (tt > 0) {
+                const cf gg = cmul(unpack_raw<CPLX, BCBF>(bperm_raw_a<CPLX, BCBF>(craw_prev, pa4)), dacc);
+                gr[tt - 1] = gg.r;
+                gi[tt - 1] = gg.i;
+                keep_here(gr[tt - 1], gi[tt - 1]);
+            }
+            if (tt < nvalid) {
+                // x_t = P_t (d_t * x_{t-1}) + b_t.  Source j stores into the
+                // slot its entry names: region rank(j) at row pi(j), so within
+                // a region every row has at most one source and plain stores
+                // suffice.  Sources of rank >= kRegions (rare) go to a spare
+                // region and then add atomically into the last one.  Row i
+                // sums its slots of all regions and clears them; slots no
+                // source wrote stay zero.
+                const cf v = cmul(d, x);
+                const uint32_t slot = ent & 0xFFFu;
+                *static_cast<float2 *>(__builtin_assume_aligned(regp + slot, 8)) = make_float2(v.r, v.i);
                 lds_order();
-            }
-            // All regions are read back to back (one LDS round trip); rows
-            // keep only the regions below their in-degree.
-            cf uu[kRegions];
+                if (__any(slot >= (uint32_t)(kRegions * kRegionBytes))) {
+                    if (slot >= (uint32_t)(kRegions * kRegionBytes)) {
+                        cf *o = reinterpret_cast<cf *>(regp + slot - kRegionBytes);
+                        atomicAdd(&o->r, v.r);
+                        if constexpr (CPLX)
+                            atomicAdd(&o->i, v.i);
+                    }
+                    lds_order();
+                }
+                cf uu[kRegions];
 #pragma unroll
-            for (int r = 0; r < kRegions; ++r)
-                uu[r] = s_reg[wave][r][lane];
-            lds_order();
-            cf sum = b;
+                for (int r = 0; r < kRegions; ++r)
+                    uu[r] = s_reg[wave][r][q.ln];
+                lds_order();
 #pragma unroll
-            for (int r = 0; r < kRegions; ++r) {
-                sum.r += deg > r ? uu[r].r : 0.f;
-                sum.i += deg > r ? uu[r].i : 0.f;
+                for (int r = 0; r < kRegions; ++r)
+                    s_reg[wave][r][q.ln] = cf{0.f, 0.f};
+                lds_order();
+                cf sum = b;
+#pragma unroll
+                for (int r = 0; r < kRegions; ++r) {
+                    sum.r += uu[r].r;
+                    sum.i += uu[r].i;
+                }
+                x = sum;
+                const float qv = c.r * x.r - c.i * x.i;
+                qg[tt & 3] = q.row_ok ? qv : 0.f;
+                // Extend the prefix operator by step t.
+                const uint32_t pe = bperm_a(ent, pa4);
+                cf dd;
+                dd.r = bperm_a(d.r, pa4);
+                dd.i = CPLX ? bperm_a(d.i, pa4) : 0.f;
+                dacc = cmul(dd, dacc);
+                pa4 = (int)(pe >> 16) + q.gbase * 4;
             }
-            x = sum;
+            craw_prev = craw;
+            if ((tt & 3) == 3)
+                w[tt >> 2] = group_fold4<NP>(qg, q.i);
         }
-        q[tt] = c.r * x.r - c.i * x.i;
-        // Extend the prefix operator by step t (source j sits at pacc[j]
-        // with factor dacc[j]); the same gather also brings the readout
-        // weight of step t-1:  Re(c_{t-1} . P D X) = Re(sum_j g_{t-1}[j] X[j])
-        // with g_{t-1}[j] = c_{t-1}[pacc_{t-1}[j]] * dacc_{t-1}[j].
-        const int src = gbase + pacc;
-        const int npacc = bperm(p, src);
-        cf dd;
-        dd.r = bperm(d.r, src);
-        dd.i = CPLX ? bperm(d.i, src) : 0.f;
-        if (tt > 0) {
-            const cf gg = cmul(unpack_raw<CPLX, BCBF>(bperm_raw<CPLX, BCBF>(craw_prev, src)), dacc);
-            gr[tt - 1] = gg.r;
-            gi[tt - 1] = gg.i;
+        {
+            const cf gg = cmul(unpack_raw<CPLX, BCBF>(bperm_raw_a<CPLX, BCBF>(craw_prev, pa4)), dacc);
+            gr[T - 1] = gg.r;
+            gi[T - 1] = gg.i;
+            keep_here(gr[T - 1], gi[T - 1]);
         }
-        dacc = cmul(dd, dacc);
-        pacc = npacc;
-        craw_prev = craw;
-    }
-    {
-        const cf gg = cmul(unpack_raw<CPLX, BCBF>(bperm_raw<CPLX, BCBF>(craw_prev, gbase + pacc)), dacc);
-        gr[T - 1] = gg.r;
-        gi[T - 1] = gg.i;
-    }
 
-    // ---- The chunk's operator (pi, d, e) = (pacc, dacc, x) for the carry wave.
-    s_pi[tid] = pacc;
-    s_d[tid] = dacc;
-    s_e[tid] = x;
-    __syncthreads();   // (2) chunk operators ready
-    __syncthreads();   // (3) carry ready
+        // ---- The chunk's operator (pi, d, e) = (pacc, dacc, x) for the carry wave.
+        // The local part of the readout, summed over the group's rows now
+        // (the sum is linear, so the carry's part is summed on its own).
+        using GB = GroupedButterfly<NP, T>;
+        group_finish<NP, T / 4>(w, q.i);
+        if ((q.i & ((1 << GB::NPLAIN) - 1)) == 0) {
+#pragma unroll
+            for (int rr = 0; rr < GB::RF; ++rr)
+                s_q[wave * G * T + q.g * T + GB::step_of(rr, q.i)] = w[rr];
+        }
+        int opi = (pa4 >> 2) - q.gbase;
+        {
+            const int slot = wave * 64 + q.ln;
+            s_pi[slot] = opi;
+            s_d[slot] = dacc;
+            s_e[slot] = x;
+        }
+        // Post them: the carry wave chains them while other waves finish.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        if (q.ln == 0)
+            atomicOr(&s_ready, 1u << wave);
+        __syncthreads();   // (B) all chunk operators taken, next ticket published
+        const uint32_t nxt = __builtin_amdgcn_readfirstlane(s_next);
+        const bool more = nxt < total;
+        // Issued unconditionally (the workgroup's last tile reloads its own
+        // rows, which are in range): a load under a condition would keep its
+        // registers live around the whole loop.
+        issue_scores(more ? nxt : cur);
+#ifndef PDSSM_SCAN_LATE_INPUTS
+        issue_inputs();
+#endif
+        __syncthreads();   // (C) carry ready, next table staged
 
-    // ---- a5: carry into this chunk, then the readout
-    //   y_t = sum_j ( Re(c_t[j] x_loc_t[j]) + Re(g_t[j] X_chunk[j]) ).
-    const cf xt = s_xin[i];
-    int ppi = i;
-    cf pd = {1.f, 0.f}, pe = {0.f, 0.f};
-    if (chunk > 0) {
-        ppi = s_pi[tid - NP];
-        pd = s_d[tid - NP];
-        pe = s_e[tid - NP];
-    }
-    const cf xc = scatter_add<CPLX>(scr, lane, gbase, ppi, cmul(pd, xt), pe);
+        // ---- a5: carry into this chunk, then the readout
+        //   y_t = sum_j ( Re(c_t[j] x_loc_t[j]) + Re(g_t[j] X_chunk[j]) ).
+        {
+            const Lanes r = lanes();
+            const int chunk = wave * G + r.g, slot = wave * 64 + r.ln;
+            cf *scr = s_scr[wave];
+            const cf xt = s_xin[r.i];
+            int ppi = r.i;
+            cf pd = {1.f, 0.f}, pe = {0.f, 0.f};
+            if (chunk > 0) {
+                ppi = s_pi[slot - NP];
+                pd = s_d[slot - NP];
+                pe = s_e[slot - NP];
+            }
+            // The previous wave's slots are rewritten with its next operator
+            // once it has left this barrier.
+            __syncthreads();   // (D) prefixes and carry read
+            const cf xc = scatter_add<CPLX>(scr, r.ln, r.gbase, ppi, cmul(pd, xt), pe);
+            float wc[T / 4];
 #pragma unroll
-    for (int tt = 0; tt < T; ++tt) {
-        q[tt] += gr[tt] * xc.r;
-        if constexpr (CPLX)
-            q[tt] -= gi[tt] * xc.i;
-    }
-    group_transpose_sum<NP, T>(q, i);
-    using BF = Butterfly<NP, T>;
-    if ((i & ((1 << BF::NPLAIN) - 1)) == 0) {
+            for (int m = 0; m < T / 4; ++m) {
+                float c4[4];
 #pragma unroll
-        for (int r = 0; r < BF::RF; ++r) {
-            const int tt = r + BF::RF * (i >> BF::NPLAIN);
-            const int64_t t = tc0 + tt;
-            if (t < a.L) {
-                if (a.y_bf16)
-                    reinterpret_cast<uint16_t *>(a.y)[seq_row + t] = f32_to_bf16_rne(q[r]);
-                else
-                    reinterpret_cast<float *>(a.y)[seq_row + t] = q[r];
+                for (int k = 0; k < 4; ++k) {
+                    float v = gr[4 * m + k] * xc.r;
+                    if constexpr (CPLX)
+                        v -= gi[4 * m + k] * xc.i;
+                    c4[k] = r.row_ok ? v : 0.f;
+                }
+                wc[m] = group_fold4<NP>(c4, r.i);
+            }
+            group_finish<NP, T / 4>(wc, r.i);
+            // Outputs go through s_y to the carry wave, which stores them
+            // after the next (B), so no store stands between this wave and
+            // its next loads; the workgroup's last tile stores them here.
+            if ((r.i & ((1 << GB::NPLAIN) - 1)) == 0) {
+#pragma unroll
+                for (int rr = 0; rr < GB::RF; ++rr) {
+                    const int tt = r.g * T + GB::step_of(rr, r.i);   // step within the wave
+                    const float yv = s_q[wave * G * T + tt] + wc[rr];
+                    if (more) {
+                        s_y[wave * G * T + tt] = yv;
+                    } else if (cw0 + tt < L) {
+                        if (a.y_bf16)
+                            (reinterpret_cast<uint16_t *>(a.y) + y0)[tt] = f32_to_bf16_rne(yv);
+                        else
+                            (reinterpret_cast<float *>(a.y) + y0)[tt] = yv;
+                    }
+                }
             }
         }
+        if (!more)
+            return;
+#ifdef PDSSM_SCAN_LATE_INPUTS
+        issue_inputs();
+#endif
+        select();
+        cur = nxt;
     }
 }
 
 // ---------------------------------------------------------------------------
 // Per-call preparation.
 //  * Blocks >= 1, one wave per dictionary entry (h, k): the entry table
-//    tab[h][k][j] = pi(j) | rank(j) << 8 | deg(j) << 16, where rank(j)
-//    counts the sources j' < j with the same destination and deg(j) is the
-//    number of sources whose destination is j.  Padding sources j >= N map
-//    to themselves with rank 0 and in-degree 1.
+//    tab[h][k][j] = slot(j) | (4 * pi(j)) << 16 for source j, where slot(j)
+//    is the byte offset, inside a wave's scatter regions, of row pi(j) in
+//    region min(rank(j), kRegions), and rank(j) counts the sources j' < j
+//    with the same destination.  Padding sources j >= N map to themselves
+//    with rank 0.
 //  * Block 0: new epoch and ticket reset; on first use (or after the epoch
 //    wraps) clear every carry record.
 // ---------------------------------------------------------------------------
@@ -551,15 +838,13 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(Header *hdr, uint4 *
         if (e >= entries || lane >= NP)
             return;
         const int pi = lane < N ? (int)min((unsigned)dict[e * N + lane], (unsigned)(N - 1)) : lane;
-        int rank = 0, deg = 0;
+        int rank = 0;
         for (int jj = 0; jj < N; ++jj) {
             const int pj = __builtin_amdgcn_readlane(pi, jj);
             rank += (jj < lane && pj == pi) ? 1 : 0;
-            deg += (pj == lane) ? 1 : 0;
         }
-        if (lane >= N)
-            deg = 1;   // padding rows hold their own (zero) state
-        tab[e * NP + lane] = (uint32_t)pi | ((uint32_t)min(rank, 255) << 8) | ((uint32_t)deg << 16);
+        const uint32_t slot = (uint32_t)(min(rank, kRegions) * kRegionBytes + pi * (int)sizeof(cf));
+        tab[e * NP + lane] = slot | ((uint32_t)(pi * 4) << 16);
         return;
     }
     __shared__ int s_fresh;
@@ -733,13 +1018,17 @@ __global__ void __launch_bounds__(64) compose_final_kernel(ComposeArgs a)
 // ---------------------------------------------------------------------------
 static thread_local std::string g_err;
 
+// Step indices inside a sequence are 32-bit on the device (with room for a
+// tile past the end).
+constexpr int64_t kMaxL = (int64_t)1 << 30;
+
 static int pad_states(int N) { return N <= 8 ? 8 : N <= 16 ? 16 : N <= 32 ? 32 : 64; }
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 static int check_dims(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K)
 {
-    if (B < 1 || H < 1 || L < 1 || N < 1 || N > 64 || K < 1 || K > 32767)
+    if (B < 1 || H < 1 || L < 1 || L > kMaxL || N < 1 || N > 64 || K < 1 || K > 32767)
         return PDSSM_ERR_DIM;
     // Element counts must fit int64 and tile tickets a uint32.
     const double steps = (double)B * (double)H * (double)L;
@@ -784,13 +1073,36 @@ static int hip_status(hipError_t e)
     return PDSSM_ERR_HIP;
 }
 
+// Persistent grid: as many workgroups as the device holds at once (they
+// loop over the tiles), never more than there are tiles.
 template <int NP, bool CPLX, bool BCBF>
 static hipError_t launch_scan(const ScanArgs &a, hipStream_t st)
 {
-    const size_t dyn = a.dict_lds ? (((size_t)a.K * NP * 4 + 15) & ~(size_t)15)
+    // The table is staged in rows of 64 lanes x 16 bytes: whole rows fit.
+    const size_t dyn = a.dict_lds ? (((size_t)a.K * NP * 4 + 1023) & ~(size_t)1023)
                                   : (size_t)kScanW * kScanT * 64 * 4;
-    hipLaunchKernelGGL((scan_kernel<NP, CPLX, BCBF>), dim3((unsigned)(a.n_tiles * a.S)),
-                       dim3((kScanW + 1) * 64), dyn, st, a);
+    const int block = (kScanW + 1) * 64;
+    // Resident workgroups per device, cached per (device, LDS size).
+    static thread_local int c_dev = -1, c_wgs = 0;
+    static thread_local size_t c_dyn = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev != c_dev || dyn != c_dyn) {
+        int per_cu = 0, cus = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, scan_kernel<NP, CPLX, BCBF>, block, dyn);
+        if (e != hipSuccess)
+            return e;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess)
+            return e;
+        c_wgs = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+        c_dev = dev;
+        c_dyn = dyn;
+    }
+    const unsigned grid = (unsigned)((int64_t)a.total < c_wgs ? (int64_t)a.total : c_wgs);
+    hipLaunchKernelGGL((scan_kernel<NP, CPLX, BCBF>), dim3(grid), dim3(block), dyn, st, a);
     return hipSuccess;
 }
 
@@ -866,6 +1178,7 @@ extern "C" int pdssm_scan_fwd(const void *sel_or_logits, const int32_t *dict_idx
     a.L = L;
     a.S = lo.S;
     a.n_tiles = lo.n_tiles;
+    a.total = (uint32_t)(lo.n_tiles * lo.S);
     a.N = N;
     a.K = K;
     a.sel_mode = flags & PDSSM_SEL_MASK;
