@@ -84,6 +84,8 @@ def main() -> int:
                     help="also run a plain 1 GiB device-to-device copy (known bytes) so that "
                          "rocprofv3 byte counters can be scaled")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the oracle over the batch for at least this long")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -152,7 +154,7 @@ def main() -> int:
         orc = oracle.get()
         times = []
         t_start = time.perf_counter()
-        while len(times) < args.cpu_reps or time.perf_counter() - t_start < 2.0:
+        while len(times) < args.cpu_reps or time.perf_counter() - t_start < args.cpu_seconds:
             c0 = time.perf_counter()
             orc.scan_inputs(host, nthreads=threads)
             times.append(time.perf_counter() - c0)

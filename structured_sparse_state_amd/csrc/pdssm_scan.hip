@@ -51,7 +51,7 @@ struct ScanArgs {
     uint32_t sel_mode;
     int y_bf16;
     int dict_lds;   // the head's entry table fits in LDS
-    const uint32_t *tab;   // [H][K][NP]: scatter slot | 4 * pi << 16 (see prep_kernel)
+    const uint32_t *tab;   // [H][K][NP]: scatter slot | in-degree << 12 | 4 * pi << 16 (see prep_kernel)
 };
 
 // Scan tiling: a chunk is kScanT steps of one group of NP lanes; a wave holds
@@ -70,12 +70,25 @@ constexpr int kScanW = PDSSM_SCAN_W;
 constexpr int kScanD = PDSSM_SCAN_D;   // steps of inputs in flight per lane (register ring)
 static_assert(kScanW >= 1 && kScanW <= 32, "chunk waves post into a 32-bit mask");
 constexpr int kDictLdsMax = 32768;   // bytes of the head's entry table kept in LDS
+#ifndef PDSSM_POLL_TICKS
+#define PDSSM_POLL_TICKS 80
+#endif
+constexpr uint64_t kPollTicks = PDSSM_POLL_TICKS;   // look-back loads are used this long (realtime ticks, 10 ns) after issue
+// The carry wave's nap between polls (s_sleep units of 64 clocks): it shares
+// its SIMD with chunk waves, so it should not spin.
+#ifndef PDSSM_CARRY_NAP
+#define PDSSM_CARRY_NAP 4
+#endif
+#ifndef PDSSM_CARRY_PRIO
+#define PDSSM_CARRY_PRIO 2   // s_setprio level of the carry wave (chunk waves stay at 0)
+#endif
 #ifndef PDSSM_SCAN_REGIONS
 #define PDSSM_SCAN_REGIONS 3
 #endif
 constexpr int kRegions = PDSSM_SCAN_REGIONS;   // collision-free scatter regions (ranks 0..kRegions-1)
 constexpr int kRegionBytes = 64 * 8;           // one region: 64 complex slots
 static_assert((kRegions + 1) * kRegionBytes <= 4096, "slot offsets are 12-bit");
+static_assert(kRegions <= 3, "in-degrees are stored clamped to 2 bits");
 
 __host__ __device__ constexpr int scan_tile_steps(int NP) { return kScanW * (64 / NP) * kScanT; }
 
@@ -169,6 +182,11 @@ struct LookBack {
     int bpi = 0;
     cf bd = {1.f, 0.f}, be = {0.f, 0.f}, xin = {0.f, 0.f};
     bool done = false;
+    // Loads in flight: 0 none, 1 the two poll words, 2 tile j's INCL, 3 its
+    // AGG; they are used once kPollTicks have passed (or when asked to wait).
+    int phase = 0;
+    uint64_t t_issue = 0;
+    uint64_t w[1 + 2 * NC];
 
     __device__ void start(const ScanArgs &a, int64_t tile, int64_t sq, int lane)
     {
@@ -179,69 +197,111 @@ struct LookBack {
         xin = {0.f, 0.f};
         j = tile - 1;
         done = tile == 0;
+        phase = 0;
         if (done && a.x0 && lane < a.N)
             xin = load_diag<CPLX>(a.x0, sq * a.N + lane);
     }
 
-    // One poll; true when it made progress (found the INCL or took an AGG).
-    __device__ bool step(const ScanArgs &a, uint32_t epoch, int lane, cf *scr)
+    __device__ static uint64_t load(const uint64_t *p)
     {
+        return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ static bool from(uint64_t word, uint32_t epoch) { return (uint32_t)(word >> 32) == epoch; }
+
+    // Advance by at most one action; true when it made progress (found the
+    // INCL or took an AGG).  With wait == false it never waits on a load.
+    __device__ bool poll(const ScanArgs &a, uint32_t epoch, int lane, cf *scr, bool wait)
+    {
+        if (done)
+            return false;
         const bool act = lane < NP;
         const int64_t rj = j * a.S + seq;
         const uint64_t *iw = a.incl + rj * IW;
-        const uint64_t *w = a.agg + rj * AW;
-        uint32_t pw = 0;
-        bool pok = false;
-        if (lane == 0)
-            pok = get_word(iw, epoch, pw);
-        else if (lane == 1 && j > 0)
-            pok = get_word(w, epoch, pw);
-        const uint64_t ready = __ballot(pok);
-        if (ready & 1) {
+        const uint64_t *aw = a.agg + rj * AW;
+        if (phase == 0) {
+            // One word of tile j's INCL (lane 0) and of its AGG (lane 1).
+            w[0] = 0;
+            if (lane == 0)
+                w[0] = load(iw);
+            else if (lane == 1 && j > 0)
+                w[0] = load(aw);
+            phase = 1;
+            t_issue = __builtin_amdgcn_s_memrealtime();
+            return false;
+        }
+        if (!wait && __builtin_amdgcn_s_memrealtime() - t_issue < kPollTicks)
+            return false;
+        if (phase == 1) {
+            const uint64_t ready = __ballot((lane == 0 || (lane == 1 && j > 0)) && from(w[0], epoch));
+            if (ready & 1) {
+                // The whole INCL record.
+                if (act) {
+                    w[0] = load(iw + lane * NC);
+                    if constexpr (CPLX)
+                        w[1] = load(iw + lane * NC + 1);
+                }
+                phase = 2;
+            } else if (ready & 2) {
+                // The whole AGG record.
+                if (act) {
+                    w[0] = load(aw + lane);
+                    w[1] = load(aw + NP + lane * NC);
+                    w[2] = load(aw + NP + NP * NC + lane * NC);
+                    if constexpr (CPLX) {
+                        w[3] = load(aw + NP + lane * NC + 1);
+                        w[4] = load(aw + NP + NP * NC + lane * NC + 1);
+                    }
+                }
+                phase = 3;
+            } else {
+                phase = 0;
+                return false;
+            }
+            t_issue = __builtin_amdgcn_s_memrealtime();
+            return false;
+        }
+        if (phase == 2) {
             bool ok = true;
             cf X = {0.f, 0.f};
             if (act) {
-                uint32_t u0 = 0, u1 = 0;
-                ok = get_word(iw + lane * NC, epoch, u0);
+                ok = from(w[0], epoch);
                 if constexpr (CPLX)
-                    ok = get_word(iw + lane * NC + 1, epoch, u1) && ok;
-                X = {__uint_as_float(u0), __uint_as_float(u1)};
+                    ok = ok && from(w[1], epoch);
+                X = {__uint_as_float((uint32_t)w[0]), CPLX ? __uint_as_float((uint32_t)w[1]) : 0.f};
             }
+            phase = 0;
             if (__all(ok)) {
                 xin = scatter_add<CPLX>(scr, lane, 0, bpi, cmul(bd, X), be);
                 done = true;
                 return true;
             }
-        } else if (ready & 2) {
-            bool ok = true;
-            int p = lane;
-            cf d = {1.f, 0.f}, e = {0.f, 0.f};
-            if (act) {
-                uint32_t up = 0, dr = 0, di = 0, er = 0, ei = 0;
-                ok = get_word(w + lane, epoch, up);
-                ok = get_word(w + NP + lane * NC, epoch, dr) && ok;
-                ok = get_word(w + NP + NP * NC + lane * NC, epoch, er) && ok;
-                if constexpr (CPLX) {
-                    ok = get_word(w + NP + lane * NC + 1, epoch, di) && ok;
-                    ok = get_word(w + NP + NP * NC + lane * NC + 1, epoch, ei) && ok;
-                }
-                p = (int)min(up, (uint32_t)(NP - 1));
-                d = {__uint_as_float(dr), __uint_as_float(di)};
-                e = {__uint_as_float(er), __uint_as_float(ei)};
-            }
-            if (__all(ok)) {
-                // acc <- acc o agg_j  (acc is later in time)
-                const int npi = bperm(bpi, p);
-                cf gd;
-                gd.r = bperm(bd.r, p);
-                gd.i = CPLX ? bperm(bd.i, p) : 0.f;
-                const cf ne = scatter_add<CPLX>(scr, lane, 0, bpi, cmul(bd, e), be);
-                bpi = npi;
-                bd = cmul(gd, d);
-                be = ne;
-                --j;
-                return true;
-            }
+            return false;
+        }
+        // phase == 3: an AGG record
+        bool ok = true;
+        int p = lane;
+        cf d = {1.f, 0.f}, e = {0.f, 0.f};
+        if (act) {
+            ok = from(w[0], epoch) && from(w[1], epoch) && from(w[2], epoch);
+            if constexpr (CPLX)
+                ok = ok && from(w[3], epoch) && from(w[4], epoch);
+            p = (int)min((uint32_t)w[0], (uint32_t)(NP - 1));
+            d = {__uint_as_float((uint32_t)w[1]), CPLX ? __uint_as_float((uint32_t)w[3]) : 0.f};
+            e = {__uint_as_float((uint32_t)w[2]), CPLX ? __uint_as_float((uint32_t)w[4]) : 0.f};
+        }
+        phase = 0;
+        if (__all(ok)) {
+            // acc <- acc o agg_j  (acc is later in time)
+            const int npi = bperm(bpi, p);
+            cf gd;
+            gd.r = bperm(bd.r, p);
+            gd.i = CPLX ? bperm(bd.i, p) : 0.f;
+            const cf ne = scatter_add<CPLX>(scr, lane, 0, bpi, cmul(bd, e), be);
+            bpi = npi;
+            bd = cmul(gd, d);
+            be = ne;
+            --j;
+            return true;
         }
         return false;
     }
@@ -300,7 +360,7 @@ __device__ void publish_incl(const ScanArgs &a, int64_t tile, int64_t seq, uint3
 // chains the chunk operators and runs the look-back (while the chunk waves
 // are busy: the carry into a tile depends only on earlier tiles).  Per tile:
 //
-//   chunk waves:  local pass, post operator       (B) start the next tile's loads (C) readout (D) ... next selection
+//   chunk waves:  local pass, post operator       (B) next tile's scores          (C) readout (D) ... next inputs, selection
 //   carry wave:   next ticket, chain as
 //                 operators come, look-back       (B) next table, previous y,
 //                                                     publish                     (C)         (D)
@@ -316,7 +376,7 @@ template <int NP, bool CPLX, bool BCBF>
 constexpr int scan_waves_per_eu()
 {
 #ifdef PDSSM_SCAN_WAVES_PER_EU
-    return PDSSM_SCAN_WAVES_PER_EU;
+    return (!CPLX || (BCBF && NP == 64)) ? PDSSM_SCAN_WAVES_PER_EU : 1;
 #else
     return (!CPLX || (BCBF && NP == 64)) ? 6 : 1;
 #endif
@@ -331,12 +391,12 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
     using Raw = typename RawVec<CPLX, BCBF>::type;
     using DRaw = typename std::conditional<CPLX, float2, float>::type;
     using Stored = typename std::conditional<BCBF, typename std::conditional<CPLX, uint32_t, uint16_t>::type, Raw>::type;
-    // Entry table: the head's [K][NP] (scatter slot | 4 * pi << 16) when it
-    // fits, else the tile's entries per (wave, step, lane).
+    // Entry table: the head's [K][NP] (scatter slot | in-degree << 12 |
+    // 4 * pi << 16) when it fits, else the tile's entries per (wave, step, lane).
     extern __shared__ __attribute__((aligned(16))) uint32_t s_tab[];
     __shared__ int16_t s_sel[W][G * T];
     __shared__ __attribute__((aligned(16))) cf s_reg[W][kRegions + 1][64];   // scatter regions, plus a spare one for ranks >= kRegions
-    __shared__ cf s_scr[W + 1][64];
+    __shared__ cf s_cscr[64];   // the carry wave's scatter scratch
     __shared__ int s_pi[SLOTS];   // chunk operators, then their inclusive prefixes
     __shared__ cf s_d[SLOTS];
     __shared__ cf s_e[SLOTS];
@@ -354,6 +414,8 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
 
     if (wave == W) {
         // ================= carry wave =================
+        // Its work is on every tile's critical path: issue it first.
+        __builtin_amdgcn_s_setprio(PDSSM_CARRY_PRIO);
         auto take_ticket = [&]() -> uint32_t {
             uint32_t t = 0;
             if (lane == 0)
@@ -404,14 +466,15 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         };
         const bool act = lane < NP;
         const int l = act ? lane : 0;
-        cf *scr = s_scr[W];
+        cf *scr = s_cscr;
         bool have_prev = false;
         uint32_t prev = 0;
         LookBack<NP, CPLX> lb;
         while (true) {
-            const uint32_t nxt = take_ticket();
+            // The next ticket; its value is needed only at (B).
+            uint32_t tk = 0;
             if (lane == 0)
-                s_next = nxt;
+                tk = atomicAdd(&a.hdr->ticket, 1u);
             const uint32_t tile = __builtin_amdgcn_readfirstlane(cur / S32), seq = cur - tile * S32;
             lb.start(a, tile, seq, lane);
 
@@ -454,10 +517,14 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                     ++wnext;
                     continue;
                 }
-                if (!lb.done && lb.step(a, epoch, lane, scr))
+                // Nothing to chain yet: a look-back action that does not wait.
+                if (lb.poll(a, epoch, lane, scr, false))
                     continue;
-                __builtin_amdgcn_s_sleep(1);
+                __builtin_amdgcn_s_sleep(PDSSM_CARRY_NAP);
             }
+            const uint32_t nxt = __builtin_amdgcn_readfirstlane(tk);
+            if (lane == 0)
+                s_next = nxt;
             __syncthreads();   // (B) all chunk operators taken, next ticket published
             if (lane == 0)
                 s_ready = 0;
@@ -474,8 +541,8 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             if (!lb.done) {
                 publish_agg<NP, CPLX>(a, tile, seq, epoch, lane, ppi, pd, pe);
                 while (!lb.done)
-                    if (!lb.step(a, epoch, lane, scr))
-                        __builtin_amdgcn_s_sleep(2);
+                    if (!lb.poll(a, epoch, lane, scr, true) && lb.phase == 0)
+                        __builtin_amdgcn_s_sleep(PDSSM_CARRY_NAP);
             }
             publish_incl<NP, CPLX>(a, tile, seq, epoch, lane, ppi, pd, pe, lb.xin, scr);
             s_xin[lane] = lb.xin;
@@ -598,10 +665,6 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
     issue_scores(cur);
     issue_inputs();
     select();
-    // The scatter regions start cleared; every step clears what it reads.
-#pragma unroll
-    for (int r = 0; r < kRegions; ++r)
-        s_reg[wave][r][lane] = cf{0.f, 0.f};
     __syncthreads();   // (Q) first table and selections ready
 
     while (true) {
@@ -669,8 +732,8 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                 // a region every row has at most one source and plain stores
                 // suffice.  Sources of rank >= kRegions (rare) go to a spare
                 // region and then add atomically into the last one.  Row i
-                // sums its slots of all regions and clears them; slots no
-                // source wrote stay zero.
+                // reads all regions and keeps those below its in-degree:
+                // exactly the slots written in this step.
                 const cf v = cmul(d, x);
                 const uint32_t slot = ent & 0xFFFu;
                 *static_cast<float2 *>(__builtin_assume_aligned(regp + slot, 8)) = make_float2(v.r, v.i);
@@ -689,15 +752,12 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                 for (int r = 0; r < kRegions; ++r)
                     uu[r] = s_reg[wave][r][q.ln];
                 lds_order();
-#pragma unroll
-                for (int r = 0; r < kRegions; ++r)
-                    s_reg[wave][r][q.ln] = cf{0.f, 0.f};
-                lds_order();
+                const int deg = (int)((ent >> 12) & 3u);
                 cf sum = b;
 #pragma unroll
                 for (int r = 0; r < kRegions; ++r) {
-                    sum.r += uu[r].r;
-                    sum.i += uu[r].i;
+                    sum.r += deg > r ? uu[r].r : 0.f;
+                    sum.i += deg > r ? uu[r].i : 0.f;
                 }
                 x = sum;
                 const float qv = c.r * x.r - c.i * x.i;
@@ -749,9 +809,6 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         // rows, which are in range): a load under a condition would keep its
         // registers live around the whole loop.
         issue_scores(more ? nxt : cur);
-#ifndef PDSSM_SCAN_LATE_INPUTS
-        issue_inputs();
-#endif
         __syncthreads();   // (C) carry ready, next table staged
 
         // ---- a5: carry into this chunk, then the readout
@@ -759,7 +816,9 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         {
             const Lanes r = lanes();
             const int chunk = wave * G + r.g, slot = wave * 64 + r.ln;
-            cf *scr = s_scr[wave];
+            // Scratch for the scatter: the wave's first scatter region, which
+            // the local pass rewrites before it reads it.
+            cf *scr = &s_reg[wave][0][0];
             const cf xt = s_xin[r.i];
             int ppi = r.i;
             cf pd = {1.f, 0.f}, pe = {0.f, 0.f};
@@ -807,9 +866,10 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         }
         if (!more)
             return;
-#ifdef PDSSM_SCAN_LATE_INPUTS
+        // The next tile's first input steps (its scores have been in flight
+        // since (B)); issuing them only now keeps their registers free
+        // through the readout.
         issue_inputs();
-#endif
         select();
         cur = nxt;
     }
@@ -818,11 +878,12 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
 // ---------------------------------------------------------------------------
 // Per-call preparation.
 //  * Blocks >= 1, one wave per dictionary entry (h, k): the entry table
-//    tab[h][k][j] = slot(j) | (4 * pi(j)) << 16 for source j, where slot(j)
-//    is the byte offset, inside a wave's scatter regions, of row pi(j) in
-//    region min(rank(j), kRegions), and rank(j) counts the sources j' < j
-//    with the same destination.  Padding sources j >= N map to themselves
-//    with rank 0.
+//    tab[h][k][j] = slot(j) | min(deg(j), kRegions) << 12 | (4 * pi(j)) << 16
+//    where slot(j) is the byte offset, inside a wave's scatter regions, of
+//    row pi(j) in region min(rank(j), kRegions), rank(j) counts the sources
+//    j' < j with the same destination and deg(j) the sources whose
+//    destination is j.  Padding sources j >= N map to themselves with rank
+//    0 and in-degree 1.
 //  * Block 0: new epoch and ticket reset; on first use (or after the epoch
 //    wraps) clear every carry record.
 // ---------------------------------------------------------------------------
@@ -838,13 +899,16 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(Header *hdr, uint4 *
         if (e >= entries || lane >= NP)
             return;
         const int pi = lane < N ? (int)min((unsigned)dict[e * N + lane], (unsigned)(N - 1)) : lane;
-        int rank = 0;
+        int rank = 0, deg = 0;
         for (int jj = 0; jj < N; ++jj) {
             const int pj = __builtin_amdgcn_readlane(pi, jj);
             rank += (jj < lane && pj == pi) ? 1 : 0;
+            deg += (pj == lane) ? 1 : 0;
         }
+        if (lane >= N)
+            deg = 1;   // padding rows hold their own (zero) state
         const uint32_t slot = (uint32_t)(min(rank, kRegions) * kRegionBytes + pi * (int)sizeof(cf));
-        tab[e * NP + lane] = slot | ((uint32_t)(pi * 4) << 16);
+        tab[e * NP + lane] = slot | ((uint32_t)min(deg, kRegions) << 12) | ((uint32_t)(pi * 4) << 16);
         return;
     }
     __shared__ int s_fresh;
