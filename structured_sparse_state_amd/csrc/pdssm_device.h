@@ -589,18 +589,41 @@ __device__ __forceinline__ void select_finish(const ScoreSlice<NV> &s, uint32_t 
 // sum_{j : pi[j] = i} v[j], over the NP lanes of one group.  `base` is the
 // group's first slot.  Every lane of the wave must call it (convergent).
 // ---------------------------------------------------------------------------
+// Float add into LDS (no ordering wider than the workgroup is needed).
+__device__ __forceinline__ void lds_add(float *p, float v)
+{
+    (void)__hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Byte offset of an LDS object (the low half of its generic address).
+template <typename P>
+__device__ __forceinline__ uint32_t lds_addr(P *p)
+{
+    return (uint32_t)(uintptr_t)p;
+}
+
+// The adds and the read-back form one asm block that waits for its own LDS
+// operations.  Written as C++, the compiler makes LDS atomics wait for every
+// global-to-LDS copy still in flight, since it cannot tell that they touch
+// other bytes; the wave that stages the entry table must not stall on it.
 template <bool CPLX>
 __device__ __forceinline__ cf scatter_add(cf *scr, int lane, int base, int pi, cf v, cf add)
 {
     scr[lane] = add;
-    lds_order();
-    atomicAdd(&scr[base + pi].r, v.r);
+    const uint32_t to = lds_addr(&scr[base + pi]);
+    const uint32_t from = lds_addr(&scr[lane]);
+    float2 out;
     if constexpr (CPLX)
-        atomicAdd(&scr[base + pi].i, v.i);
-    lds_order();
-    const cf out = scr[lane];
-    lds_order();
-    return out;
+        asm volatile("ds_add_f32 %1, %3\n\tds_add_f32 %1, %4 offset:4\n\tds_read_b64 %0, %2\n\ts_waitcnt lgkmcnt(0)"
+                     : "=v"(out)
+                     : "v"(to), "v"(from), "v"(v.r), "v"(v.i)
+                     : "memory");
+    else
+        asm volatile("ds_add_f32 %1, %3\n\tds_read_b64 %0, %2\n\ts_waitcnt lgkmcnt(0)"
+                     : "=v"(out)
+                     : "v"(to), "v"(from), "v"(v.r)
+                     : "memory");
+    return {out.x, out.y};
 }
 
 // ---------------------------------------------------------------------------

@@ -9,8 +9,9 @@
 //   a2  P D step       x' = P (d * x) + b as an LDS scatter-add, lane = state.
 //   a3  composition    each chunk's operator (pi, d, e) = A_last ... A_first
 //                      applied to zero state, composed in O(N) by a gather and
-//                      a multiply; chunks of a tile combine in log2 levels
-//                      (Hillis-Steele over LDS).
+//                      a multiply; the chunk waves of a tile chain their
+//                      operators into inclusive prefixes, in time order,
+//                      through LDS.
 //   a4  carry          tiles of one sequence chain through a carry record in
 //                      the workspace: decoupled look-back over tile aggregates
 //                      (Merrill & Garland's single-pass scan), with an atomic
@@ -47,11 +48,15 @@ struct ScanArgs {
     uint64_t *incl;
     int64_t H, L, S, n_tiles;
     uint32_t total;   // tiles in the call: n_tiles * S
+    // Per-head tickets (null: one shared stream): workgroup w serves head
+    // w % H and takes its tiles from ctr[32 * h], total_head = n_tiles * B.
+    uint32_t *ctr;
+    uint32_t total_head;
     int N, K;
     uint32_t sel_mode;
     int y_bf16;
     int dict_lds;   // the head's entry table fits in LDS
-    const uint32_t *tab;   // [H][K][NP]: scatter slot | in-degree << 12 | 4 * pi << 16 (see prep_kernel)
+    const uint32_t *tab;   // [H][K][NP]: scatter slot | row read offset << 12 | 4 * pi << 24 (see prep_kernel)
 };
 
 // Scan tiling: a chunk is kScanT steps of one group of NP lanes; a wave holds
@@ -86,11 +91,41 @@ constexpr uint64_t kPollTicks = PDSSM_POLL_TICKS;   // look-back loads are used 
 #define PDSSM_SCAN_REGIONS 3
 #endif
 constexpr int kRegions = PDSSM_SCAN_REGIONS;   // collision-free scatter regions (ranks 0..kRegions-1)
-constexpr int kRegionBytes = 64 * 8;           // one region: 64 complex slots
-static_assert((kRegions + 1) * kRegionBytes <= 4096, "slot offsets are 12-bit");
-static_assert(kRegions <= 3, "in-degrees are stored clamped to 2 bits");
+constexpr int kRegionBytes = 64 * 8;           // one block: 64 complex slots
+// A chunk wave's scatter area, in blocks:  0 .. R-1 hold regions R-1 .. 0
+// (region r at block R-1-r), R .. 2R-1 are always zero, 2R is the spare
+// for sources of rank >= R.  A row of in-degree d reads the R blocks from
+// block R-d on: its d regions, then zeros -- no per-region test.
+constexpr int kBlocks = 2 * kRegions + 1;
+constexpr uint32_t kSpareOff = 2 * kRegions * kRegionBytes;
+static_assert(kBlocks * kRegionBytes <= 4096, "scatter slots are 12-bit");
+static_assert(kRegions * kRegionBytes + 63 * 8 < 2048, "row read offsets are 11-bit");
 
 __host__ __device__ constexpr int scan_tile_steps(int NP) { return kScanW * (64 / NP) * kScanT; }
+
+// Which chunk wave runs the tile's p-th group of chunks.  The carry wave
+// chains the groups in time order as their waves finish, so the order
+// follows the order in which the waves of a workgroup tend to finish their
+// local pass (measured for seven chunk waves: the waves sharing a SIMD with
+// an older wave of the workgroup finish last).  Any order is correct.
+__host__ __device__ constexpr int wave_at(int p)
+{
+    constexpr int order7[7] = {1, 2, 3, 0, 5, 6, 4};
+    return (kScanW == 7) ? order7[p] : p;
+}
+__host__ __device__ constexpr int chunk_pos(int w)
+{
+    constexpr int pos7[7] = {3, 0, 1, 2, 6, 4, 5};
+    return (kScanW == 7) ? pos7[w] : w;
+}
+constexpr bool chunk_order_ok()
+{
+    for (int p = 0; p < kScanW; ++p)
+        if (wave_at(p) < 0 || wave_at(p) >= kScanW || chunk_pos(wave_at(p)) != p)
+            return false;
+    return true;
+}
+static_assert(chunk_order_ok(), "wave_at and chunk_pos must be inverse permutations");
 
 template <int NP, bool CPLX>
 __host__ __device__ constexpr int agg_words() { return NP * (1 + 2 * (CPLX ? 2 : 1)); }
@@ -349,20 +384,21 @@ __device__ void publish_incl(const ScanArgs &a, int64_t tile, int64_t seq, uint3
 
 // ---------------------------------------------------------------------------
 // The fused scan kernel.  Persistent workgroups take tiles from an atomic
-// ticket in tile-major order (u = tile * S + seq) and run them one after
-// another.  A workgroup holds at most two tickets, its current tile and the
-// next one, and starts the next only once the current tile's carry is out.
-// So the smallest unfinished ticket always belongs to a current tile, whose
-// look-back waits only on smaller tickets -- all finished: no deadlock.
+// ticket in tile-major order (u = tile * S + seq, or, with one ticket stream
+// per head, u = tile * B + b) and run them one after another.  A workgroup
+// holds at most two tickets, its current tile and the next one, and starts
+// the next only once the current tile's carry is out.  So the smallest
+// unfinished ticket of a stream always belongs to a current tile, whose
+// look-back waits only on smaller tickets of the same stream -- all
+// finished: no deadlock.
 //
 // Waves 0..W-1 ("chunk waves") each own G chunks of T steps of the tile.
-// Wave W (the "carry wave") takes the tickets, stages the dictionary table,
-// chains the chunk operators and runs the look-back (while the chunk waves
-// are busy: the carry into a tile depends only on earlier tiles).  Per tile:
+// Wave W (the "carry wave") takes the tickets, stages the dictionary table
+// and runs the look-back while the chunk waves are busy (the carry into a
+// tile depends only on earlier tiles).  Per tile:
 //
-//   chunk waves:  local pass, post operator       (B) next tile's scores          (C) readout (D) ... next inputs, selection
-//   carry wave:   next ticket, chain as
-//                 operators come, look-back       (B) next table, previous y,
+//   chunk waves:  local pass, chain prefixes      (B) next tile's scores          (C) readout (D) ... next inputs, selection
+//   carry wave:   next ticket, look-back          (B) next table, previous y,
 //                                                     publish                     (C)         (D)
 //
 // so the next tile's router scores and first input steps are in flight
@@ -391,11 +427,11 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
     using Raw = typename RawVec<CPLX, BCBF>::type;
     using DRaw = typename std::conditional<CPLX, float2, float>::type;
     using Stored = typename std::conditional<BCBF, typename std::conditional<CPLX, uint32_t, uint16_t>::type, Raw>::type;
-    // Entry table: the head's [K][NP] (scatter slot | in-degree << 12 |
-    // 4 * pi << 16) when it fits, else the tile's entries per (wave, step, lane).
+    // Entry table: the head's [K][NP] (scatter slot | row read offset << 12
+    // | 4 * pi << 24) when it fits, else the tile's entries per (wave, step, lane).
     extern __shared__ __attribute__((aligned(16))) uint32_t s_tab[];
     __shared__ int16_t s_sel[W][G * T];
-    __shared__ __attribute__((aligned(16))) cf s_reg[W][kRegions + 1][64];   // scatter regions, plus a spare one for ranks >= kRegions
+    __shared__ __attribute__((aligned(16))) cf s_reg[W][kBlocks][64];   // scatter regions, zero blocks, spare
     __shared__ cf s_cscr[64];   // the carry wave's scatter scratch
     __shared__ int s_pi[SLOTS];   // chunk operators, then their inclusive prefixes
     __shared__ cf s_d[SLOTS];
@@ -404,10 +440,21 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
     __shared__ float s_y[TILE];   // a finished tile's outputs, stored by the carry wave
     __shared__ float s_q[TILE];   // per step: sum_j Re(c_t[j] x_loc_t[j]), until the correction
     __shared__ uint32_t s_next;   // ticket published by the carry wave
-    __shared__ uint32_t s_ready;  // bit w: chunk wave w has posted its operators
+    __shared__ uint32_t s_ready;  // bit w: chunk wave w has posted its inclusive prefixes
 
     // Tile indices, sequences and heads fit 32 bits (the host checks).
-    const uint32_t S32 = (uint32_t)a.S, H32 = (uint32_t)a.H, total = a.total;
+    const uint32_t S32 = (uint32_t)a.S, H32 = (uint32_t)a.H;
+    // Ticket u -> (tile, sequence): tile-major over all sequences, or, with
+    // per-head tickets, over the sequences b * H + hp of this workgroup's head.
+    const bool pinned = a.ctr != nullptr;
+    const uint32_t hp = pinned ? (uint32_t)blockIdx.x % H32 : 0u;
+    const uint32_t per = pinned ? S32 / H32 : S32;
+    const uint32_t total = pinned ? a.total_head : a.total;
+    auto decode = [&](uint32_t u, uint32_t &tile, uint32_t &seq) {
+        tile = __builtin_amdgcn_readfirstlane(u / per);
+        const uint32_t r = u - tile * per;
+        seq = pinned ? r * H32 + hp : r;
+    };
     const int N = a.N, K = a.K;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -419,7 +466,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         auto take_ticket = [&]() -> uint32_t {
             uint32_t t = 0;
             if (lane == 0)
-                t = atomicAdd(&a.hdr->ticket, 1u);
+                t = atomicAdd(pinned ? a.ctr + 32 * hp : &a.hdr->ticket, 1u);
             return __builtin_amdgcn_readfirstlane(t);
         };
         // The head's entry table straight to LDS (16 bytes per lane per
@@ -427,7 +474,9 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         auto stage_table = [&](uint32_t u) {
             if (!a.dict_lds)
                 return;
-            const uint32_t h = __builtin_amdgcn_readfirstlane((u % S32) % H32);
+            uint32_t tile, seq;
+            decode(u, tile, seq);
+            const uint32_t h = __builtin_amdgcn_readfirstlane(seq % H32);
             const uint4 *src = reinterpret_cast<const uint4 *>(a.tab + h * (int64_t)K * NP);
             const int tab_vecs = (K * NP) >> 2;   // 4 entries per 16 bytes
             for (int w0 = 0; w0 < tab_vecs; w0 += 64) {
@@ -450,77 +499,41 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();   // (Q) first table and selections ready
 
-        // The outputs of tile u, staged in s_y by the chunk waves.
-        auto store_y = [&](uint32_t u) {
-            const uint32_t tile = __builtin_amdgcn_readfirstlane(u / S32), seq = u - tile * S32;
-            const int64_t t0 = (int64_t)tile * TILE;
-            const int64_t y0 = (int64_t)seq * a.L + t0;
-            for (int k = lane; k < TILE; k += 64) {
-                if (t0 + k < a.L) {
-                    if (a.y_bf16)
-                        reinterpret_cast<uint16_t *>(a.y)[y0 + k] = f32_to_bf16_rne(s_y[k]);
-                    else
-                        reinterpret_cast<float *>(a.y)[y0 + k] = s_y[k];
-                }
+        // Store output v of the previous tile, which chunk wave w staged in
+        // s_y (lane = step of the wave's chunks).
+        int64_t py0 = 0, pt0 = 0;   // the previous tile: y index and step of its first output
+        auto store_y = [&](int w, float v) {
+            const int k = chunk_pos(w) * G * T + lane;   // step within the tile
+            if (lane < G * T && pt0 + k < a.L) {
+                if (a.y_bf16)
+                    reinterpret_cast<uint16_t *>(a.y)[py0 + k] = f32_to_bf16_rne(v);
+                else
+                    reinterpret_cast<float *>(a.y)[py0 + k] = v;
             }
         };
         const bool act = lane < NP;
-        const int l = act ? lane : 0;
         cf *scr = s_cscr;
         bool have_prev = false;
-        uint32_t prev = 0;
         LookBack<NP, CPLX> lb;
         while (true) {
             // The next ticket; its value is needed only at (B).
             uint32_t tk = 0;
             if (lane == 0)
-                tk = atomicAdd(&a.hdr->ticket, 1u);
-            const uint32_t tile = __builtin_amdgcn_readfirstlane(cur / S32), seq = cur - tile * S32;
+                tk = atomicAdd(pinned ? a.ctr + 32 * hp : &a.hdr->ticket, 1u);
+            uint32_t tile, seq;
+            decode(cur, tile, seq);
             lb.start(a, tile, seq, lane);
 
-            // ---- a3 + a4 while the chunk waves run their local pass: chain
-            // the C chunk operators in time order as their waves post them
-            // (slot c then holds the operator of chunks 0..c of the tile;
-            // lane = state, lanes >= NP carry an identity; the index and
-            // factor gathers are lane moves, only the scatter of e goes
-            // through LDS), and in between look back for the carry into
-            // this tile, which depends only on earlier tiles.
-            int ppi = lane;
-            cf pd = {1.f, 0.f}, pe = {0.f, 0.f};
-            int wnext = 0;   // next chunk wave whose operators to take
-            while (wnext < W) {
+            // ---- a4 while the chunk waves run their local pass and chain
+            // their prefixes: look back for the carry into this tile, which
+            // depends only on earlier tiles, until every chunk wave has
+            // posted (then the aggregate is known).
+            while (!lb.done) {
                 const uint32_t posted = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile uint32_t *>(&s_ready));
-                if ((posted >> wnext) & 1u) {
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-#pragma unroll
-                    for (int k = 0; k < G; ++k) {
-                        const int base = (wnext * G + k) * NP;
-                        const int cpi = act ? s_pi[base + l] : lane;
-                        const cf cd = act ? s_d[base + l] : cf{1.f, 0.f};
-                        const cf ce = act ? s_e[base + l] : cf{0.f, 0.f};
-                        // (op_c o prefix): pi[j] = cpi[ppi[j]], d[j] = cd[ppi[j]] * pd[j],
-                        // e = P_c D_c pe + ce.
-                        const int src = ppi * 4;
-                        const int npi = (int)bperm_a((uint32_t)cpi, src);
-                        cf gd;
-                        gd.r = bperm_a(cd.r, src);
-                        gd.i = CPLX ? bperm_a(cd.i, src) : 0.f;
-                        pe = scatter_add<CPLX>(scr, lane, 0, cpi, cmul(cd, pe), ce);
-                        ppi = npi;
-                        pd = cmul(gd, pd);
-                        if (act) {
-                            s_pi[base + lane] = ppi;
-                            s_d[base + lane] = pd;
-                            s_e[base + lane] = pe;
-                        }
-                    }
-                    ++wnext;
-                    continue;
-                }
-                // Nothing to chain yet: a look-back action that does not wait.
-                if (lb.poll(a, epoch, lane, scr, false))
-                    continue;
-                __builtin_amdgcn_s_sleep(PDSSM_CARRY_NAP);
+                if (posted == (1u << W) - 1u)
+                    break;
+                if (!lb.poll(a, epoch, lane, scr, false))
+                    __builtin_amdgcn_s_sleep(PDSSM_CARRY_NAP);
             }
             const uint32_t nxt = __builtin_amdgcn_readfirstlane(tk);
             if (lane == 0)
@@ -529,12 +542,31 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             if (lane == 0)
                 s_ready = 0;
             const bool more = nxt < total;
-            if (more)
+            // The tile's aggregate: the inclusive prefix of its last chunk;
+            // and the previous tile's outputs, final in s_y since the chunk
+            // waves posted.  Both are read before the table copy starts (the
+            // compiler would make LDS reads wait for it).
+            int ppi = lane;
+            cf pd = {1.f, 0.f}, pe = {0.f, 0.f};
+            if (act) {
+                const int as = wave_at(W - 1) * 64 + (G - 1) * NP + lane;
+                ppi = s_pi[as];
+                pd = s_d[as];
+                pe = s_e[as];
+            }
+            float yv[W];
+#pragma unroll
+            for (int w = 0; w < W; ++w)
+                yv[w] = (lane < G * T) ? s_y[w * G * T + lane] : 0.f;
+            // Every chunk wave is past its local pass, the only reader of the
+            // entry table: stage the next tile's (a workgroup serving one
+            // head keeps its table).
+            if (more && !pinned)
                 stage_table(nxt);
-            // The previous tile's outputs: the chunk waves staged them in s_y
-            // after its (D), before this (B).
             if (have_prev)
-                store_y(prev);
+#pragma unroll
+                for (int w = 0; w < W; ++w)
+                    store_y(w, yv[w]);
             // ---- a4, second part: publish the tile's aggregate if the carry
             // is still unknown (so later tiles need not wait for it), then the
             // state after the tile.
@@ -544,21 +576,25 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                     if (!lb.poll(a, epoch, lane, scr, true) && lb.phase == 0)
                         __builtin_amdgcn_s_sleep(PDSSM_CARRY_NAP);
             }
+            // The next table has landed (it was staged before (B)), then the
+            // state after the tile goes out; its stores need not complete here.
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             publish_incl<NP, CPLX>(a, tile, seq, epoch, lane, ppi, pd, pe, lb.xin, scr);
             s_xin[lane] = lb.xin;
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next table has landed
             __syncthreads();   // (C) carry ready, next table staged
             __syncthreads();   // (D) chunk waves have read the prefixes and the carry
             if (!more)
                 return;
-            prev = cur;
+            pt0 = (int64_t)tile * TILE;
+            py0 = (int64_t)seq * a.L + pt0;
             have_prev = true;
             cur = nxt;
         }
     }
 
     // ================= chunk waves =================
-    // Lane roles: group g of NP lanes runs chunk wave * G + g; lane i of the
+    // Lane roles: group g of NP lanes runs chunk chunk_pos(wave) * G + g of
+    // the tile (its operator slot is wave * 64 + g * NP); lane i of the
     // group holds state i.  Every phase below derives them from its own
     // opaque copy of the lane index, so that per-lane constants are made
     // where they are used instead of being held across the whole loop.
@@ -613,11 +649,11 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
     // first D input steps.
     auto issue_scores = [&](uint32_t u) {
         const Lanes q = lanes();
-        const uint32_t tile = __builtin_amdgcn_readfirstlane(u / S32);
-        const uint32_t seq = u - tile * S32;
+        uint32_t tile, seq;
+        decode(u, tile, seq);
         h = __builtin_amdgcn_readfirstlane(seq % H32);
         row0 = (int64_t)seq * a.L;
-        tw0 = (int)tile * TILE + wave * G * T;
+        tw0 = (int)tile * TILE + chunk_pos(wave) * G * T;
         full = tw0 + G * T <= L;
         // Assigned on every path, so no older value is kept around the loop.
         sc = sel_fast ? select_issue<G * T, NV>(a.sel, opaque_s(a.sel_mode), opaque_s(K), a.L, row0, tw0, q.ln)
@@ -658,6 +694,10 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         lds_order();
     };
 
+    // The zero blocks of this wave's scatter area (never written again).
+#pragma unroll
+    for (int r = kRegions; r < 2 * kRegions; ++r)
+        s_reg[wave][r][lane] = cf{0.f, 0.f};
     __syncthreads();   // (P) first ticket published
     uint32_t cur = __builtin_amdgcn_readfirstlane(s_next);
     if (cur >= total)
@@ -681,6 +721,14 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         const int tc0 = cw0 + q.g * T;      // first step of the chunk
         const int64_t y0 = row0 + cw0;      // y index of the wave's first step
         const int nvalid = max(0, min(T, L - tc0));
+        // The same bound, re-derived where it is tested again, so that the
+        // compiler does not keep one test's outcome alive across blocks.
+        auto nvalid_again = [&]() {
+            if constexpr (G == 1)
+                return opaque_s(__builtin_amdgcn_readfirstlane(nvalid));   // wave-uniform: one chunk per wave
+            else
+                return opaque(nvalid);
+        };
         char *const regp = reinterpret_cast<char *>(&s_reg[wave][0][0]) + q.gbase * (int)sizeof(cf);
         const uint32_t *const tb = s_tab + (a.dict_lds ? q.i : wave * T * 64 + q.ln);
         cf x = {0.f, 0.f};
@@ -704,8 +752,6 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
 #pragma unroll
         for (int tt = 0; tt < T; ++tt) {
             const uint32_t ent = ent_next;
-            if (tt + 1 < T)
-                ent_next = entry(tt + 1);
             const int sl = tt % D;
             cf d;
             if constexpr (CPLX)
@@ -715,60 +761,76 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             const cf b = unpack_raw<CPLX, BCBF>(bv[sl]);
             const Raw craw = cv[sl];
             const cf c = unpack_raw<CPLX, BCBF>(craw);
+            // The gathers at pacc before step t (byte address pa4): c_{t-1}
+            // for the readout weight of step t-1, and pi_t, d_t to extend
+            // the prefix operator.  They do not depend on x, so they are
+            // issued first and their LDS round trip overlaps the scatter's.
+            Raw cgat = zero_raw<CPLX, BCBF>();
+            if (tt > 0)
+                cgat = bperm_raw_a<CPLX, BCBF>(craw_prev, pa4);
+            uint32_t pe;   // set, and used, only on steps inside the sequence
+            cf dd;
+            if (tt < nvalid) {
+                pe = bperm_a(ent, pa4);
+                dd.r = bperm_a(d.r, pa4);
+                dd.i = CPLX ? bperm_a(d.i, pa4) : 0.f;
+            }
+            cf uu[kRegions];
+            if (tt < nvalid_again()) {
+                // x_t = P_t (d_t * x_{t-1}) + b_t.  Source j stores into the
+                // slot its entry names: region rank(j) at row pi(j), so within
+                // a region every row has at most one source and plain stores
+                // suffice.  Sources of rank >= kRegions (rare) go to the spare
+                // block and then add atomically into the last region.  Row i
+                // reads kRegions blocks from the offset its entry names: the
+                // in-degree(i) regions written in this step, then zero blocks.
+                const cf v = cmul(d, x);
+                const uint32_t slot = ent & 0xFFFu;
+                *static_cast<float2 *>(__builtin_assume_aligned(regp + slot, 8)) = make_float2(v.r, v.i);
+                lds_order();
+                if (__any(slot >= kSpareOff)) {
+                    if (slot >= kSpareOff) {
+                        cf *o = reinterpret_cast<cf *>(regp + (slot - kSpareOff));
+                        lds_add(&o->r, v.r);
+                        if constexpr (CPLX)
+                            lds_add(&o->i, v.i);
+                    }
+                    lds_order();
+                }
+                const char *rowp = regp + ((ent >> 12) & 0x7FFu);
+#pragma unroll
+                for (int r = 0; r < kRegions; ++r) {
+                    const float2 u = *static_cast<const float2 *>(__builtin_assume_aligned(rowp + r * kRegionBytes, 8));
+                    uu[r] = {u.x, u.y};
+                }
+                lds_order();
+            }
+            if (tt + 1 < T)
+                ent_next = entry(tt + 1);
             if (tt + D < T)
                 fetch(q, tt + D);
             // Readout weight of step t-1, through the prefix operator before
             // step t:  Re(c_{t-1} . P D X) = Re(sum_j g_{t-1}[j] X[j]) with
             // g_{t-1}[j] = c_{t-1}[pacc_{t-1}[j]] * dacc_{t-1}[j].
             if (tt > 0) {
-                const cf gg = cmul(unpack_raw<CPLX, BCBF>(bperm_raw_a<CPLX, BCBF>(craw_prev, pa4)), dacc);
+                const cf gg = cmul(unpack_raw<CPLX, BCBF>(cgat), dacc);
                 gr[tt - 1] = gg.r;
                 gi[tt - 1] = gg.i;
                 keep_here(gr[tt - 1], gi[tt - 1]);
             }
-            if (tt < nvalid) {
-                // x_t = P_t (d_t * x_{t-1}) + b_t.  Source j stores into the
-                // slot its entry names: region rank(j) at row pi(j), so within
-                // a region every row has at most one source and plain stores
-                // suffice.  Sources of rank >= kRegions (rare) go to a spare
-                // region and then add atomically into the last one.  Row i
-                // reads all regions and keeps those below its in-degree:
-                // exactly the slots written in this step.
-                const cf v = cmul(d, x);
-                const uint32_t slot = ent & 0xFFFu;
-                *static_cast<float2 *>(__builtin_assume_aligned(regp + slot, 8)) = make_float2(v.r, v.i);
-                lds_order();
-                if (__any(slot >= (uint32_t)(kRegions * kRegionBytes))) {
-                    if (slot >= (uint32_t)(kRegions * kRegionBytes)) {
-                        cf *o = reinterpret_cast<cf *>(regp + slot - kRegionBytes);
-                        atomicAdd(&o->r, v.r);
-                        if constexpr (CPLX)
-                            atomicAdd(&o->i, v.i);
-                    }
-                    lds_order();
-                }
-                cf uu[kRegions];
-#pragma unroll
-                for (int r = 0; r < kRegions; ++r)
-                    uu[r] = s_reg[wave][r][q.ln];
-                lds_order();
-                const int deg = (int)((ent >> 12) & 3u);
+            if (tt < nvalid_again()) {
+                // Extend the prefix operator by step t.
+                dacc = cmul(dd, dacc);
+                pa4 = (int)(pe >> 24) + q.gbase * 4;
                 cf sum = b;
 #pragma unroll
                 for (int r = 0; r < kRegions; ++r) {
-                    sum.r += deg > r ? uu[r].r : 0.f;
-                    sum.i += deg > r ? uu[r].i : 0.f;
+                    sum.r += uu[r].r;
+                    sum.i += uu[r].i;
                 }
                 x = sum;
                 const float qv = c.r * x.r - c.i * x.i;
                 qg[tt & 3] = q.row_ok ? qv : 0.f;
-                // Extend the prefix operator by step t.
-                const uint32_t pe = bperm_a(ent, pa4);
-                cf dd;
-                dd.r = bperm_a(d.r, pa4);
-                dd.i = CPLX ? bperm_a(d.i, pa4) : 0.f;
-                dacc = cmul(dd, dacc);
-                pa4 = (int)(pe >> 16) + q.gbase * 4;
             }
             craw_prev = craw;
             if ((tt & 3) == 3)
@@ -791,17 +853,69 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             for (int rr = 0; rr < GB::RF; ++rr)
                 s_q[wave * G * T + q.g * T + GB::step_of(rr, q.i)] = w[rr];
         }
-        int opi = (pa4 >> 2) - q.gbase;
+        // ---- a3: the prefix operators of the tile's chunks, chained in time
+        // order across the chunk waves: this wave waits for the prefix of the
+        // chunks before its own, composes its operator(s) onto it, and posts
+        // the inclusive prefix (slot wave * 64 + g * NP + i) for the next.
+        // Lanes of other groups run along and write nothing.  The chain is
+        // on the tile's critical path, so it runs at raised priority, and
+        // its hand-offs rely on the LDS executing each wave's operations in
+        // order: a prefix is written before its flag, and read after it.
         {
+            const int opi = (pa4 >> 2) - q.gbase;
+            const int pos = chunk_pos(wave);
             const int slot = wave * 64 + q.ln;
-            s_pi[slot] = opi;
-            s_d[slot] = dacc;
-            s_e[slot] = x;
+            cf *scr = &s_reg[wave][0][0];   // scatter scratch: a region the next local pass rewrites
+            __builtin_amdgcn_s_setprio(PDSSM_CARRY_PRIO);
+            int ppi = 0;
+            cf pd = {1.f, 0.f}, pe = {0.f, 0.f};
+            if (pos > 0) {
+                const uint32_t need = 1u << wave_at(pos - 1);
+                const int ps = wave_at(pos - 1) * 64 + (G - 1) * NP + q.i;
+                while (true) {
+                    const uint32_t f = *reinterpret_cast<volatile uint32_t *>(&s_ready);
+                    lds_order();
+                    ppi = s_pi[ps];
+                    pd = s_d[ps];
+                    pe = s_e[ps];
+                    lds_order();
+                    if (__builtin_amdgcn_readfirstlane(f) & need)
+                        break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                int rpi = opi;
+                cf rd = dacc, re = x;
+                if (pos > 0 || g > 0) {
+                    // (op o prefix): pi[j] = opi[ppi[j]], d[j] = dacc[ppi[j]] * pd[j],
+                    // e = P D pe + x.
+                    if (g > 0) {
+                        const int ps = wave * 64 + (g - 1) * NP + q.i;
+                        ppi = s_pi[ps];
+                        pd = s_d[ps];
+                        pe = s_e[ps];
+                    }
+                    const int src = (q.gbase + ppi) * 4;
+                    rpi = (int)bperm_a((uint32_t)opi, src);
+                    cf gd;
+                    gd.r = bperm_a(dacc.r, src);
+                    gd.i = CPLX ? bperm_a(dacc.i, src) : 0.f;
+                    re = scatter_add<CPLX>(scr, q.ln, q.gbase, opi, cmul(dacc, pe), x);
+                    rd = cmul(gd, pd);
+                }
+                if (q.g == g) {
+                    s_pi[slot] = rpi;
+                    s_d[slot] = rd;
+                    s_e[slot] = re;
+                }
+                lds_order();
+            }
+            if (q.ln == 0)
+                __hip_atomic_fetch_or(&s_ready, 1u << wave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            __builtin_amdgcn_s_setprio(0);
         }
-        // Post them: the carry wave chains them while other waves finish.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        if (q.ln == 0)
-            atomicOr(&s_ready, 1u << wave);
         __syncthreads();   // (B) all chunk operators taken, next ticket published
         const uint32_t nxt = __builtin_amdgcn_readfirstlane(s_next);
         const bool more = nxt < total;
@@ -815,7 +929,10 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         //   y_t = sum_j ( Re(c_t[j] x_loc_t[j]) + Re(g_t[j] X_chunk[j]) ).
         {
             const Lanes r = lanes();
-            const int chunk = wave * G + r.g, slot = wave * 64 + r.ln;
+            const int chunk = chunk_pos(wave) * G + r.g, slot = wave * 64 + r.ln;
+            // The slot of the chunk before: this wave's previous group, or
+            // the last group of the wave that runs the chunks before.
+            const int pslot = (r.g > 0) ? slot - NP : wave_at(max(chunk_pos(wave) - 1, 0)) * 64 + (G - 1) * NP + r.i;
             // Scratch for the scatter: the wave's first scatter region, which
             // the local pass rewrites before it reads it.
             cf *scr = &s_reg[wave][0][0];
@@ -823,9 +940,9 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             int ppi = r.i;
             cf pd = {1.f, 0.f}, pe = {0.f, 0.f};
             if (chunk > 0) {
-                ppi = s_pi[slot - NP];
-                pd = s_d[slot - NP];
-                pe = s_e[slot - NP];
+                ppi = s_pi[pslot];
+                pd = s_d[pslot];
+                pe = s_e[pslot];
             }
             // The previous wave's slots are rewritten with its next operator
             // once it has left this barrier.
@@ -878,18 +995,20 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
 // ---------------------------------------------------------------------------
 // Per-call preparation.
 //  * Blocks >= 1, one wave per dictionary entry (h, k): the entry table
-//    tab[h][k][j] = slot(j) | min(deg(j), kRegions) << 12 | (4 * pi(j)) << 16
-//    where slot(j) is the byte offset, inside a wave's scatter regions, of
-//    row pi(j) in region min(rank(j), kRegions), rank(j) counts the sources
-//    j' < j with the same destination and deg(j) the sources whose
-//    destination is j.  Padding sources j >= N map to themselves with rank
-//    0 and in-degree 1.
-//  * Block 0: new epoch and ticket reset; on first use (or after the epoch
+//    tab[h][k][j] = slot(j) | read(j) << 12 | (4 * pi(j)) << 24, byte
+//    offsets inside a chunk wave's scatter area: slot(j) is row pi(j) of
+//    region rank(j) (of the spare block when rank(j) >= kRegions), read(j)
+//    is row j of block kRegions - min(deg(j), kRegions), where rank(j)
+//    counts the sources j' < j with the same destination and deg(j) the
+//    sources whose destination is j.  Padding sources j >= N map to
+//    themselves with rank 0 and in-degree 1.
+//  * Block 0: new epoch and ticket resets; on first use (or after the epoch
 //    wraps) clear every carry record.
 // ---------------------------------------------------------------------------
 constexpr int kPrepThreads = 1024;
 
-__global__ void __launch_bounds__(kPrepThreads) prep_kernel(Header *hdr, uint4 *recs, int64_t n16,
+__global__ void __launch_bounds__(kPrepThreads) prep_kernel(Header *hdr, uint32_t *ctr, int64_t nctr,
+                                                            uint4 *recs, int64_t n16,
                                                             const int32_t *dict, uint32_t *tab,
                                                             int64_t entries, int N, int NP)
 {
@@ -907,8 +1026,10 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(Header *hdr, uint4 *
         }
         if (lane >= N)
             deg = 1;   // padding rows hold their own (zero) state
-        const uint32_t slot = (uint32_t)(min(rank, kRegions) * kRegionBytes + pi * (int)sizeof(cf));
-        tab[e * NP + lane] = slot | ((uint32_t)min(deg, kRegions) << 12) | ((uint32_t)(pi * 4) << 16);
+        const int block = rank < kRegions ? kRegions - 1 - rank : 2 * kRegions;
+        const uint32_t slot = (uint32_t)(block * kRegionBytes + pi * (int)sizeof(cf));
+        const uint32_t rd = (uint32_t)((kRegions - min(deg, kRegions)) * kRegionBytes + lane * (int)sizeof(cf));
+        tab[e * NP + lane] = slot | (rd << 12) | ((uint32_t)(pi * 4) << 24);
         return;
     }
     __shared__ int s_fresh;
@@ -930,6 +1051,8 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(Header *hdr, uint4 *
         }
         hdr->ticket = 0;
     }
+    for (int64_t h = threadIdx.x; h < nctr; h += blockDim.x)
+        ctr[32 * h] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -1108,7 +1231,7 @@ static int check_dims(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K)
 
 struct Layout {
     int NP;
-    int64_t n_tiles, n_ctiles, S, tab_bytes, agg_bytes, incl_bytes, compose_bytes, total;
+    int64_t n_tiles, n_ctiles, S, ctr_bytes, tab_bytes, agg_bytes, incl_bytes, compose_bytes, total;
 };
 
 static Layout layout_of(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K, uint32_t flags)
@@ -1123,8 +1246,9 @@ static Layout layout_of(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K, u
     lo.agg_bytes = recs * lo.NP * (1 + 2 * nc) * 8;
     lo.incl_bytes = recs * lo.NP * nc * 8;
     lo.compose_bytes = lo.n_ctiles * lo.S * lo.NP * (1 + nc) * 4;
+    lo.ctr_bytes = H * 128;   // one ticket counter per head, each on its own 128-byte line
     lo.tab_bytes = (H * (int64_t)K * lo.NP * 4 + 255) / 256 * 256;
-    const int64_t scan = lo.tab_bytes + lo.agg_bytes + lo.incl_bytes;
+    const int64_t scan = lo.ctr_bytes + lo.tab_bytes + lo.agg_bytes + lo.incl_bytes;
     lo.total = (int64_t)sizeof(Header) + ((scan > lo.compose_bytes ? scan : lo.compose_bytes) + 15) / 16 * 16;
     return lo;
 }
@@ -1165,8 +1289,20 @@ static hipError_t launch_scan(const ScanArgs &a, hipStream_t st)
         c_dev = dev;
         c_dyn = dyn;
     }
-    const unsigned grid = (unsigned)((int64_t)a.total < c_wgs ? (int64_t)a.total : c_wgs);
-    hipLaunchKernelGGL((scan_kernel<NP, CPLX, BCBF>), dim3(grid), dim3(block), dyn, st, a);
+    // When the head's table lives in LDS and every head gets at least one
+    // resident workgroup, workgroup w serves head w % H only: its table is
+    // staged once.  Otherwise one ticket stream covers all sequences.
+    ScanArgs b = a;
+    unsigned grid;
+    if (a.dict_lds && a.ctr && (int64_t)c_wgs >= a.H) {
+        const int64_t per_head = ((int64_t)c_wgs / a.H < (int64_t)a.total_head) ? (int64_t)c_wgs / a.H
+                                                                              : (int64_t)a.total_head;
+        grid = (unsigned)(per_head * a.H);
+    } else {
+        b.ctr = nullptr;
+        grid = (unsigned)((int64_t)a.total < c_wgs ? (int64_t)a.total : c_wgs);
+    }
+    hipLaunchKernelGGL((scan_kernel<NP, CPLX, BCBF>), dim3(grid), dim3(block), dyn, st, b);
     return hipSuccess;
 }
 
@@ -1234,8 +1370,11 @@ extern "C" int pdssm_scan_fwd(const void *sel_or_logits, const int32_t *dict_idx
     a.xfinal = static_cast<float *>(x_final);
     a.x0 = static_cast<const float *>(x0);
     a.hdr = static_cast<Header *>(workspace);
-    uint32_t *tab = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + sizeof(Header));
+    uint32_t *ctr = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + sizeof(Header));
+    uint32_t *tab = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(ctr) + lo.ctr_bytes);
     a.tab = tab;
+    a.ctr = ctr;   // launch_scan decides whether the tickets run per head
+    a.total_head = (uint32_t)(lo.n_tiles * B);
     a.agg = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(tab) + lo.tab_bytes);
     a.incl = reinterpret_cast<uint64_t *>(reinterpret_cast<char *>(a.agg) + lo.agg_bytes);
     a.H = H;
@@ -1252,8 +1391,8 @@ extern "C" int pdssm_scan_fwd(const void *sel_or_logits, const int32_t *dict_idx
     const int64_t rec_bytes = lo.agg_bytes + lo.incl_bytes;
     const int64_t entries = H * (int64_t)K;
     const int64_t prep_blocks = 1 + (entries + kPrepThreads / 64 - 1) / (kPrepThreads / 64);
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_blocks), dim3(kPrepThreads), 0, stream, a.hdr,
-                       reinterpret_cast<uint4 *>(a.agg), (int64_t)(rec_bytes / 16), dict_idx, tab,
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)prep_blocks), dim3(kPrepThreads), 0, stream, a.hdr, ctr,
+                       (int64_t)H, reinterpret_cast<uint4 *>(a.agg), (int64_t)(rec_bytes / 16), dict_idx, tab,
                        entries, N, lo.NP);
     rc = hip_status(hipGetLastError());
     if (rc != PDSSM_OK)
