@@ -56,7 +56,7 @@ struct ScanArgs {
     uint32_t sel_mode;
     int y_bf16;
     int dict_lds;   // the head's entry table fits in LDS
-    const uint32_t *tab;   // [H][K][NP]: scatter slot | row read offset << 12 | 4 * pi << 24 (see prep_kernel)
+    const uint16_t *tab;   // [H][K][NP]: pi | scatter block << 6 | row read block << 9 (see prep_kernel)
 };
 
 // Scan tiling: a chunk is kScanT steps of one group of NP lanes; a wave holds
@@ -98,8 +98,7 @@ constexpr int kRegionBytes = 64 * 8;           // one block: 64 complex slots
 // block R-d on: its d regions, then zeros -- no per-region test.
 constexpr int kBlocks = 2 * kRegions + 1;
 constexpr uint32_t kSpareOff = 2 * kRegions * kRegionBytes;
-static_assert(kBlocks * kRegionBytes <= 4096, "scatter slots are 12-bit");
-static_assert(kRegions * kRegionBytes + 63 * 8 < 2048, "row read offsets are 11-bit");
+static_assert(kBlocks <= 8 && kRegions <= 3, "entries hold a 3-bit scatter block and a 2-bit read block");
 
 __host__ __device__ constexpr int scan_tile_steps(int NP) { return kScanW * (64 / NP) * kScanT; }
 
@@ -427,8 +426,8 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
     using Raw = typename RawVec<CPLX, BCBF>::type;
     using DRaw = typename std::conditional<CPLX, float2, float>::type;
     using Stored = typename std::conditional<BCBF, typename std::conditional<CPLX, uint32_t, uint16_t>::type, Raw>::type;
-    // Entry table: the head's [K][NP] (scatter slot | row read offset << 12
-    // | 4 * pi << 24) when it fits, else the tile's entries per (wave, step, lane).
+    // Entry table: the head's [K][NP] 16-bit entries when they fit, else the
+    // tile's entries per (wave, step, lane), one per 32-bit word.
     extern __shared__ __attribute__((aligned(16))) uint32_t s_tab[];
     __shared__ int16_t s_sel[W][G * T];
     __shared__ __attribute__((aligned(16))) cf s_reg[W][kBlocks][64];   // scatter regions, zero blocks, spare
@@ -478,7 +477,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             decode(u, tile, seq);
             const uint32_t h = __builtin_amdgcn_readfirstlane(seq % H32);
             const uint4 *src = reinterpret_cast<const uint4 *>(a.tab + h * (int64_t)K * NP);
-            const int tab_vecs = (K * NP) >> 2;   // 4 entries per 16 bytes
+            const int tab_vecs = (K * NP) >> 3;   // 8 entries per 16 bytes
             for (int w0 = 0; w0 < tab_vecs; w0 += 64) {
                 const int w = min(w0 + lane, tab_vecs - 1);
                 __builtin_amdgcn_global_load_lds(
@@ -684,7 +683,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             wave_select<G * T>(a.sel, mode, Kq, a.L, row0, tw0, s_sel[wave], q.ln);
         if (!a.dict_lds) {
             lds_order();
-            const uint32_t *tab_h = a.tab + h * (int64_t)K * NP;
+            const uint16_t *tab_h = a.tab + h * (int64_t)K * NP;
             uint32_t *tb = s_tab + wave * T * 64 + q.ln;
             for (int tt = 0; tt < T; ++tt) {
                 const int k = s_sel[wave][q.g * T + tt];
@@ -730,7 +729,10 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                 return opaque(nvalid);
         };
         char *const regp = reinterpret_cast<char *>(&s_reg[wave][0][0]) + q.gbase * (int)sizeof(cf);
-        const uint32_t *const tb = s_tab + (a.dict_lds ? q.i : wave * T * 64 + q.ln);
+        // The entries of this lane: column i of the head's table, or its own
+        // word per step of the wave's entries (both as byte addresses).
+        const char *const tbp = reinterpret_cast<const char *>(s_tab) + (a.dict_lds ? q.i * 2 : (wave * T * 64 + q.ln) * 4);
+        const char *const rowbase = regp + q.i * (int)sizeof(cf);   // row i of block 0
         cf x = {0.f, 0.f};
         int pa4 = q.ln * 4;
         cf dacc = {1.f, 0.f};
@@ -744,9 +746,9 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         auto entry = [&](int tt) -> uint32_t {
             if (a.dict_lds) {
                 const int k = (G == 1) ? __builtin_amdgcn_readlane(selv, tt) : (int)s_sel[wave][q.g * T + tt];
-                return tb[k * NP];
+                return *reinterpret_cast<const uint16_t *>(tbp + k * NP * 2);
             }
-            return tb[tt * 64];
+            return *reinterpret_cast<const uint32_t *>(tbp + tt * 256);
         };
         uint32_t ent_next = entry(0);
 #pragma unroll
@@ -785,7 +787,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                 // reads kRegions blocks from the offset its entry names: the
                 // in-degree(i) regions written in this step, then zero blocks.
                 const cf v = cmul(d, x);
-                const uint32_t slot = ent & 0xFFFu;
+                const uint32_t slot = (ent & 0x1FFu) << 3;   // block * 512 + pi * 8
                 *static_cast<float2 *>(__builtin_assume_aligned(regp + slot, 8)) = make_float2(v.r, v.i);
                 lds_order();
                 if (__any(slot >= kSpareOff)) {
@@ -797,7 +799,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                     }
                     lds_order();
                 }
-                const char *rowp = regp + ((ent >> 12) & 0x7FFu);
+                const char *rowp = rowbase + (ent & 0x600u);   // read block * 512
 #pragma unroll
                 for (int r = 0; r < kRegions; ++r) {
                     const float2 u = *static_cast<const float2 *>(__builtin_assume_aligned(rowp + r * kRegionBytes, 8));
@@ -821,7 +823,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             if (tt < nvalid_again()) {
                 // Extend the prefix operator by step t.
                 dacc = cmul(dd, dacc);
-                pa4 = (int)(pe >> 24) + q.gbase * 4;
+                pa4 = (int)((pe & 63u) << 2) + q.gbase * 4;
                 cf sum = b;
 #pragma unroll
                 for (int r = 0; r < kRegions; ++r) {
@@ -995,13 +997,13 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
 // ---------------------------------------------------------------------------
 // Per-call preparation.
 //  * Blocks >= 1, one wave per dictionary entry (h, k): the entry table
-//    tab[h][k][j] = slot(j) | read(j) << 12 | (4 * pi(j)) << 24, byte
-//    offsets inside a chunk wave's scatter area: slot(j) is row pi(j) of
-//    region rank(j) (of the spare block when rank(j) >= kRegions), read(j)
-//    is row j of block kRegions - min(deg(j), kRegions), where rank(j)
-//    counts the sources j' < j with the same destination and deg(j) the
-//    sources whose destination is j.  Padding sources j >= N map to
-//    themselves with rank 0 and in-degree 1.
+//    tab[h][k][j] = pi(j) | block(j) << 6 | (kRegions - min(deg(j), kRegions)) << 9
+//    in 16 bits, blocks of a chunk wave's scatter area: source j stores into
+//    row pi(j) of block(j), the block of region rank(j) (the spare block
+//    when rank(j) >= kRegions); row j reads kRegions blocks from the block
+//    in bits 9-10 on.  rank(j) counts the sources j' < j with the same
+//    destination and deg(j) the sources whose destination is j.  Padding
+//    sources j >= N map to themselves with rank 0 and in-degree 1.
 //  * Block 0: new epoch and ticket resets; on first use (or after the epoch
 //    wraps) clear every carry record.
 // ---------------------------------------------------------------------------
@@ -1009,7 +1011,7 @@ constexpr int kPrepThreads = 1024;
 
 __global__ void __launch_bounds__(kPrepThreads) prep_kernel(Header *hdr, uint32_t *ctr, int64_t nctr,
                                                             uint4 *recs, int64_t n16,
-                                                            const int32_t *dict, uint32_t *tab,
+                                                            const int32_t *dict, uint16_t *tab,
                                                             int64_t entries, int N, int NP)
 {
     if (blockIdx.x > 0) {
@@ -1027,9 +1029,8 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(Header *hdr, uint32_
         if (lane >= N)
             deg = 1;   // padding rows hold their own (zero) state
         const int block = rank < kRegions ? kRegions - 1 - rank : 2 * kRegions;
-        const uint32_t slot = (uint32_t)(block * kRegionBytes + pi * (int)sizeof(cf));
-        const uint32_t rd = (uint32_t)((kRegions - min(deg, kRegions)) * kRegionBytes + lane * (int)sizeof(cf));
-        tab[e * NP + lane] = slot | (rd << 12) | ((uint32_t)(pi * 4) << 24);
+        const int rblock = kRegions - min(deg, kRegions);
+        tab[e * NP + lane] = (uint16_t)(pi | (block << 6) | (rblock << 9));
         return;
     }
     __shared__ int s_fresh;
@@ -1247,7 +1248,7 @@ static Layout layout_of(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K, u
     lo.incl_bytes = recs * lo.NP * nc * 8;
     lo.compose_bytes = lo.n_ctiles * lo.S * lo.NP * (1 + nc) * 4;
     lo.ctr_bytes = H * 128;   // one ticket counter per head, each on its own 128-byte line
-    lo.tab_bytes = (H * (int64_t)K * lo.NP * 4 + 255) / 256 * 256;
+    lo.tab_bytes = (H * (int64_t)K * lo.NP * 2 + 255) / 256 * 256;
     const int64_t scan = lo.ctr_bytes + lo.tab_bytes + lo.agg_bytes + lo.incl_bytes;
     lo.total = (int64_t)sizeof(Header) + ((scan > lo.compose_bytes ? scan : lo.compose_bytes) + 15) / 16 * 16;
     return lo;
@@ -1267,7 +1268,7 @@ template <int NP, bool CPLX, bool BCBF>
 static hipError_t launch_scan(const ScanArgs &a, hipStream_t st)
 {
     // The table is staged in rows of 64 lanes x 16 bytes: whole rows fit.
-    const size_t dyn = a.dict_lds ? (((size_t)a.K * NP * 4 + 1023) & ~(size_t)1023)
+    const size_t dyn = a.dict_lds ? (((size_t)a.K * NP * 2 + 1023) & ~(size_t)1023)
                                   : (size_t)kScanW * kScanT * 64 * 4;
     const int block = (kScanW + 1) * 64;
     // Resident workgroups per device, cached per (device, LDS size).
@@ -1371,7 +1372,7 @@ extern "C" int pdssm_scan_fwd(const void *sel_or_logits, const int32_t *dict_idx
     a.x0 = static_cast<const float *>(x0);
     a.hdr = static_cast<Header *>(workspace);
     uint32_t *ctr = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + sizeof(Header));
-    uint32_t *tab = reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(ctr) + lo.ctr_bytes);
+    uint16_t *tab = reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(ctr) + lo.ctr_bytes);
     a.tab = tab;
     a.ctr = ctr;   // launch_scan decides whether the tickets run per head
     a.total_head = (uint32_t)(lo.n_tiles * B);
@@ -1386,7 +1387,7 @@ extern "C" int pdssm_scan_fwd(const void *sel_or_logits, const int32_t *dict_idx
     a.K = K;
     a.sel_mode = flags & PDSSM_SEL_MASK;
     a.y_bf16 = (flags & PDSSM_Y_BF16) ? 1 : 0;
-    a.dict_lds = ((int64_t)K * lo.NP * 4 <= kDictLdsMax) ? 1 : 0;
+    a.dict_lds = ((int64_t)K * lo.NP * 2 <= kDictLdsMax) ? 1 : 0;
 
     const int64_t rec_bytes = lo.agg_bytes + lo.incl_bytes;
     const int64_t entries = H * (int64_t)K;
