@@ -53,6 +53,9 @@ class Oracle:
         lib.pdssm_oracle_scan.restype = I
         lib.pdssm_oracle_compose.argtypes = [P, I, P, P, I, I64, I64, I64, I32, I32, P, P]
         lib.pdssm_oracle_compose.restype = I
+        lib.pdssm_oracle_scan_bwd.argtypes = [P, I, P, P, P, P, P, P, P, I, I, I64, I64, I64, I32, I32,
+                                              P, P, P, P, I]
+        lib.pdssm_oracle_scan_bwd.restype = I
         self.lib = lib
         self.path = path
 
@@ -112,6 +115,43 @@ class Oracle:
         if complex:
             xf = xf[..., 0] + 1j * xf[..., 1]
         return y, xf
+
+    def scan_bwd(self, sel_or_logits, sel_mode: str, dict_idx, diag, b, c, gy, *, complex: bool,
+                 bc_bf16: bool, x0=None, gxf=None, nthreads: int = 1):
+        """Gradients of sum_t gy_t y_t (+ the x_final term with gradient gxf).
+
+        gy is [B,H,L] (any float dtype, read as float64); gxf is [B,H,N]
+        float64 or complex128, or None.  Returns (gb, gc, gd) [B,H,L,N] and
+        gx0 [B,H,N], float64 or complex128 (grad = dL/dRe + i dL/dIm).
+        """
+        src = self._arr(sel_or_logits)
+        dct = self._arr(dict_idx, np.int32)
+        dg = self._arr(diag, np.float32)
+        bb = self._arr(b)
+        cc = self._arr(c)
+        xx = self._arr(x0, np.float32)
+        g = self._arr(gy).astype(np.float64) if not hasattr(gy, "detach") else \
+            np.ascontiguousarray(gy.detach().cpu().double().numpy())
+        H, K, N = dct.shape
+        B, _, L = dg.shape[:3]
+        gf = None
+        if gxf is not None:
+            gf = np.asarray(gxf)
+            if complex:
+                gf = np.stack([gf.real, gf.imag], axis=-1) if np.iscomplexobj(gf) else gf
+            gf = np.ascontiguousarray(gf, dtype=np.float64)
+        shp = (B, H, L, N, 2) if complex else (B, H, L, N)
+        gb = np.empty(shp, np.float64)
+        gc = np.empty(shp, np.float64)
+        gd = np.empty(shp, np.float64)
+        gx0 = np.empty((B, H, N, 2) if complex else (B, H, N), np.float64)
+        self._check(self.lib.pdssm_oracle_scan_bwd(
+            self._ptr(src), SEL_KIND[sel_mode], self._ptr(dct), self._ptr(dg), self._ptr(bb),
+            self._ptr(cc), self._ptr(xx), self._ptr(g), self._ptr(gf), int(complex), int(bc_bf16),
+            B, H, L, N, K, self._ptr(gb), self._ptr(gc), self._ptr(gd), self._ptr(gx0), int(nthreads)))
+        if complex:
+            gb, gc, gd, gx0 = (a[..., 0] + 1j * a[..., 1] for a in (gb, gc, gd, gx0))
+        return gb, gc, gd, gx0
 
     def compose(self, sel_or_logits, sel_mode: str, dict_idx, diag, *, complex: bool):
         """Total operator A_{L-1}...A_0 per sequence: (pi int32 [B,H,N], d [B,H,N])."""

@@ -262,3 +262,161 @@ int pdssm_oracle_compose(const void *src, int sel_kind, const int32_t *dict_idx,
     }
     return ORC_OK;
 }
+
+/*
+ * Gradients of the forward scan for a real loss whose gradient with respect
+ * to y is gy (and, when given, with respect to x_final is gxf).
+ *
+ * The selection is the hard argmax of the forward pass and receives no
+ * gradient (the pages' straight-through estimator for the scores and the
+ * dictionary is not specified); b, c, the diagonals and x0 do.  A complex
+ * gradient is dL/dRe z + i dL/dIm z.  With the forward states x_t (x_{-1} =
+ * x0) kept for every step, and A_t = P_t D_t, the adjoint runs backwards:
+ *
+ *     lambda_{L-1} = gy_{L-1} conj(c_{L-1}) + gxf
+ *     lambda_t     = gy_t conj(c_t) + A_{t+1}^H lambda_{t+1},
+ *                    (A^H l)[j] = conj(d[j]) l[pi[j]]   (a gather: the
+ *                    transpose of the one-hot column scatter)
+ *     gb_t    = lambda_t
+ *     gc_t    = gy_t conj(x_t)
+ *     gd_t[j] = conj(x_{t-1}[j]) lambda_t[pi_t[j]]
+ *     gx0     = A_0^H lambda_0
+ *
+ * gy is double [B,H,L]; gxf (nullable) double [B,H,N] or [B,H,N,2].  gb, gc,
+ * gd are double [B,H,L,N] or [B,H,L,N,2]; gx0 (nullable) double [B,H,N] or
+ * [B,H,N,2].  Other arguments as in pdssm_oracle_scan.
+ */
+int pdssm_oracle_scan_bwd(const void *src, int sel_kind, const int32_t *dict_idx, const float *diag,
+                          const void *b, const void *c, const float *x0, const double *gy,
+                          const double *gxf, int is_complex, int bc_bf16, int64_t B, int64_t H,
+                          int64_t L, int32_t N, int32_t K, double *gb_out, double *gc_out,
+                          double *gd_out, double *gx0_out, int nthreads)
+{
+    if (!src || !dict_idx || !diag || !b || !c || !gy || !gb_out || !gc_out || !gd_out || B < 0 ||
+        H < 0 || L < 0 || N < 1 || K < 1 || sel_kind < 0 || sel_kind > 3)
+        return ORC_BAD_ARG;
+    const int ncomp = is_complex ? 2 : 1;
+    const int64_t BH = B * H;
+    volatile int err = ORC_OK;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t s = 0; s < BH; ++s) {
+        const int64_t h = s % H;
+        /* xs[t+1] = x_t for t = -1..L-1 (re, im), and the step maps. */
+        double *xs = (double *)calloc((size_t)(L + 1) * N * 2, sizeof(double));
+        int32_t *maps = (int32_t *)malloc((size_t)(L > 0 ? L : 1) * N * sizeof(int32_t));
+        double *lam = (double *)calloc((size_t)N * 2, sizeof(double));
+        double *lnew = (double *)calloc((size_t)N * 2, sizeof(double));
+        if (!xs || !maps || !lam || !lnew) {
+            set_error(&err, ORC_BAD_ARG);
+            free(xs);
+            free(maps);
+            free(lam);
+            free(lnew);
+            continue;
+        }
+        if (x0 != NULL) {
+            for (int32_t i = 0; i < N; ++i) {
+                xs[2 * i] = x0[(s * N + i) * ncomp];
+                xs[2 * i + 1] = is_complex ? x0[(s * N + i) * ncomp + 1] : 0.0;
+            }
+        }
+        /* Forward: the states, exactly as in pdssm_oracle_scan. */
+        for (int64_t t = 0; t < L && err == ORC_OK; ++t) {
+            const int64_t step = s * L + t;
+            const int64_t k = select_step(src, sel_kind, step, K);
+            if (k < 0 || k >= K) {
+                set_error(&err, ORC_BAD_SEL);
+                break;
+            }
+            const int32_t *pi = dict_idx + (h * K + k) * N;
+            const int64_t row = step * N;
+            const double *x = xs + (size_t)t * N * 2;
+            double *xn = xs + (size_t)(t + 1) * N * 2;
+            for (int32_t j = 0; j < N; ++j) {
+                const int32_t i = pi[j];
+                if (i < 0 || i >= N) {
+                    set_error(&err, ORC_BAD_MAP);
+                    break;
+                }
+                maps[t * N + j] = i;
+                const double ar = diag[(row + j) * ncomp];
+                const double ai = is_complex ? diag[(row + j) * ncomp + 1] : 0.0;
+                xn[2 * i] += ar * x[2 * j] - ai * x[2 * j + 1];
+                xn[2 * i + 1] += ar * x[2 * j + 1] + ai * x[2 * j];
+            }
+            for (int32_t i = 0; i < N; ++i) {
+                xn[2 * i] = xn[2 * i] + load_value(b, (row + i) * ncomp, bc_bf16);
+                if (is_complex)
+                    xn[2 * i + 1] = xn[2 * i + 1] + load_value(b, (row + i) * ncomp + 1, bc_bf16);
+            }
+        }
+        if (err != ORC_OK) {
+            free(xs);
+            free(maps);
+            free(lam);
+            free(lnew);
+            continue;
+        }
+        /* Backward. */
+        if (gxf) {
+            for (int32_t i = 0; i < N; ++i) {
+                lam[2 * i] = gxf[(s * N + i) * ncomp];
+                lam[2 * i + 1] = is_complex ? gxf[(s * N + i) * ncomp + 1] : 0.0;
+            }
+        }
+        for (int64_t t = L - 1; t >= 0; --t) {
+            const int64_t step = s * L + t;
+            const int64_t row = step * N;
+            const double g = gy[step];
+            /* lambda_t = (carried part) + gy_t conj(c_t) */
+            for (int32_t i = 0; i < N; ++i) {
+                const double cr = load_value(c, (row + i) * ncomp, bc_bf16);
+                const double ci = is_complex ? load_value(c, (row + i) * ncomp + 1, bc_bf16) : 0.0;
+                lam[2 * i] += g * cr;
+                lam[2 * i + 1] += -g * ci;
+            }
+            const double *xt = xs + (size_t)(t + 1) * N * 2;   /* x_t */
+            const double *xp = xs + (size_t)t * N * 2;         /* x_{t-1} */
+            const int32_t *pi = maps + t * N;
+            for (int32_t i = 0; i < N; ++i) {
+                const int64_t e = (row + i) * ncomp;
+                gb_out[e] = lam[2 * i];
+                gc_out[e] = g * xt[2 * i];
+                if (is_complex) {
+                    gb_out[e + 1] = lam[2 * i + 1];
+                    gc_out[e + 1] = -g * xt[2 * i + 1];
+                }
+            }
+            /* gd_t[j] = conj(x_{t-1}[j]) lambda_t[pi[j]];
+               lambda_{t-1} (before its own readout term) = conj(d_t[j]) lambda_t[pi[j]] */
+            for (int32_t j = 0; j < N; ++j) {
+                const double lr = lam[2 * pi[j]], li = lam[2 * pi[j] + 1];
+                const double xr = xp[2 * j], xi = xp[2 * j + 1];
+                const int64_t e = (row + j) * ncomp;
+                gd_out[e] = xr * lr + xi * li;
+                if (is_complex)
+                    gd_out[e + 1] = xr * li - xi * lr;
+                const double dr = diag[e];
+                const double di = is_complex ? diag[e + 1] : 0.0;
+                lnew[2 * j] = dr * lr + di * li;
+                lnew[2 * j + 1] = dr * li - di * lr;
+            }
+            double *tmp = lam;
+            lam = lnew;
+            lnew = tmp;
+        }
+        if (gx0_out) {
+            for (int32_t i = 0; i < N; ++i) {
+                gx0_out[(s * N + i) * ncomp] = lam[2 * i];
+                if (is_complex)
+                    gx0_out[(s * N + i) * ncomp + 1] = lam[2 * i + 1];
+            }
+        }
+        free(xs);
+        free(maps);
+        free(lam);
+        free(lnew);
+    }
+    return err;
+}

@@ -364,6 +364,105 @@ def pin_segment_chaining(orc):
         assert np.array_equal(xb, xf)
 
 
+# --------------------------------------------------------------------------
+# Gradients (the backward scan).  References: torch autograd through dense
+# N x N step matrices (complex128, CPU), and central finite differences of a
+# numpy dense forward.  Neither uses the oracle's hand-written adjoint.
+# --------------------------------------------------------------------------
+
+def _bwd_case(cplx, seed, bc_bf16=False, sel_mode="sel_i32"):
+    inp = _random_case(5, 11, 3, cplx, bc_bf16, sel_mode, seed=seed, B=1, H=2)
+    g = torch.Generator().manual_seed(seed + 1)
+    gy = torch.randn(inp.B, inp.H, inp.L, generator=g, dtype=torch.float64)
+    gxf = torch.randn(inp.B, inp.H, inp.N, 2 if cplx else 1, generator=g, dtype=torch.float64)
+    gxf = (gxf[..., 0] + 1j * gxf[..., 1]) if cplx else gxf[..., 0]
+    return inp, gy.numpy(), gxf.numpy()
+
+
+def autograd_grads(inp, sel, gy, gxf):
+    """(gb, gc, gd, gx0) of sum_t gy_t y_t + Re(conj(gxf) . x_final) by torch
+    autograd through dense step matrices; complex grads are dL/dRe + i dL/dIm."""
+    cplx = inp.complex
+    def leaf(a):
+        v = _as_complex(_to_f64(a), cplx)
+        return torch.tensor(v, dtype=torch.complex128, requires_grad=True)
+    d, b, c, x0 = leaf(inp.diag), leaf(inp.b), leaf(inp.c), leaf(inp.x0)
+    dct = inp.dict_idx.numpy()
+    N = inp.N
+    loss = torch.zeros((), dtype=torch.float64)
+    for bi in range(inp.B):
+        for hi in range(inp.H):
+            x = x0[bi, hi]
+            for t in range(inp.L):
+                A = torch.zeros((N, N), dtype=torch.complex128)
+                A = A.index_put((torch.as_tensor(dct[hi, sel[bi, hi, t]]), torch.arange(N)), d[bi, hi, t])
+                x = A @ x + b[bi, hi, t]
+                loss = loss + gy[bi, hi, t] * torch.real(torch.sum(c[bi, hi, t] * x))
+            loss = loss + torch.real(torch.sum(torch.conj(torch.as_tensor(gxf[bi, hi])) * x))
+    loss.backward()
+    out = [a.grad.numpy() for a in (b, c, d, x0)]
+    if not cplx:
+        out = [o.real for o in out]
+    return out
+
+
+def pin_bwd_autograd(orc):
+    """The oracle's gradients equal torch autograd through dense matrices."""
+    for cplx in (False, True):
+        for sel_mode, bc in (("sel_i32", False), ("logits_bf16", True)):
+            inp, gy, gxf = _bwd_case(cplx, 910 + 2 * cplx + bc, bc_bf16=bc, sel_mode=sel_mode)
+            sel = _sel_np(inp)
+            ref = autograd_grads(inp, sel, gy, gxf)
+            got = orc.scan_bwd(inp.sel_or_logits, inp.sel_mode, inp.dict_idx, inp.diag, inp.b, inp.c,
+                               gy, complex=cplx, bc_bf16=bc, x0=inp.x0, gxf=gxf)
+            for name, g, r in zip(("gb", "gc", "gd", "gx0"), got, ref):
+                assert _rel(g, r) < 1e-10, (name, cplx, sel_mode, _rel(g, r))
+
+
+def pin_bwd_finite_differences(orc):
+    """Central differences of a numpy dense forward in fp64 match a sample
+    of gradient components (real and imaginary parts separately)."""
+    for cplx in (False, True):
+        inp, gy, gxf = _bwd_case(cplx, 930 + cplx)
+        sel = _sel_np(inp)
+        dct = inp.dict_idx.numpy()
+        base = {k: _as_complex(_to_f64(getattr(inp, k)), cplx) for k in ("diag", "b", "c", "x0")}
+
+        def loss(v):
+            tot = 0.0
+            for bi in range(inp.B):
+                for hi in range(inp.H):
+                    x = v["x0"][bi, hi].copy()
+                    for t in range(inp.L):
+                        xn = np.array(v["b"][bi, hi, t], dtype=np.complex128)
+                        pi = dct[hi, sel[bi, hi, t]]
+                        for j in range(inp.N):
+                            xn[pi[j]] += v["diag"][bi, hi, t, j] * x[j]
+                        x = xn
+                        tot += gy[bi, hi, t] * np.real(np.sum(v["c"][bi, hi, t] * x))
+                    tot += np.real(np.sum(np.conj(gxf[bi, hi]) * x))
+            return tot
+
+        got = dict(zip(("b", "c", "diag", "x0"),
+                       orc.scan_bwd(inp.sel_or_logits, inp.sel_mode, inp.dict_idx, inp.diag, inp.b,
+                                    inp.c, gy, complex=cplx, bc_bf16=False, x0=inp.x0, gxf=gxf)))
+        rng = np.random.default_rng(77 + cplx)
+        eps = 1e-6
+        for key in ("b", "c", "diag", "x0"):
+            arr = base[key]
+            for _ in range(6):
+                idx = tuple(int(rng.integers(0, n)) for n in arr.shape)
+                for part, unit in ((0, 1.0), (1, 1j)) if cplx else ((0, 1.0),):
+                    vp = {k: v.copy() for k, v in base.items()}
+                    vm = {k: v.copy() for k, v in base.items()}
+                    vp[key][idx] += eps * unit
+                    vm[key][idx] -= eps * unit
+                    fd = (loss(vp) - loss(vm)) / (2 * eps)
+                    g = got[key][idx]
+                    an = g.real if part == 0 else g.imag
+                    assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (key, idx, part, fd, an)
+
+
 ALL_PINS = [pin_hand_examples, pin_select_argmax, pin_dense_products, pin_compose_dense, pin_fsa,
             pin_diagonal_closed_form, pin_permutation_invariants, pin_superposition,
-            pin_segment_chaining]
+            pin_segment_chaining, pin_bwd_autograd, pin_bwd_finite_differences]

@@ -45,6 +45,20 @@ MUTANTS = {
     "compose_order": ("                p = dict_idx[(h * K + k) * N + p];\n", ""),
     # bf16 decoded as the low half.
     "bf16_low_half": ("uint32_t w = (uint32_t)bits << 16;", "uint32_t w = (uint32_t)bits << 15;"),
+    # Backward: the readout's adjoint without conjugating c.
+    "bwd_c_not_conjugated": ("lam[2 * i + 1] += -g * ci;", "lam[2 * i + 1] += g * ci;"),
+    # Backward: the adjoint step as a scatter-style index (lambda read at j).
+    "bwd_gather_at_source": ("const double lr = lam[2 * pi[j]], li = lam[2 * pi[j] + 1];",
+                             "const double lr = lam[2 * j], li = lam[2 * j + 1];"),
+    # Backward: d not conjugated in the adjoint step.
+    "bwd_d_not_conjugated": ("lnew[2 * j + 1] = dr * li - di * lr;", "lnew[2 * j + 1] = dr * li + di * lr;"),
+    # Backward: gd from x_t instead of x_{t-1}.
+    "bwd_gd_wrong_state": ("const double *xp = xs + (size_t)t * N * 2;         /* x_{t-1} */",
+                           "const double *xp = xs + (size_t)(t + 1) * N * 2;         /* x_{t-1} */"),
+    # Backward: gc without the conjugate of x.
+    "bwd_gc_sign": ("gc_out[e + 1] = -g * xt[2 * i + 1];", "gc_out[e + 1] = g * xt[2 * i + 1];"),
+    # Backward: the x_final gradient dropped.
+    "bwd_drop_gxf": ("        if (gxf) {\n", "        if (0) {\n"),
 }
 
 
