@@ -112,6 +112,56 @@ size_t pdssm_scan_workspace_bytes(int64_t B, int64_t H, int64_t L, int32_t N, in
                                   uint32_t flags);
 
 /*
+ * pdssm_scan_fwd that also keeps what pdssm_scan_bwd needs: the state just
+ * before every chunk of 16 steps.
+ *   x_chunks  fp32 [B,H,ceil(L/16),N], or [B,H,ceil(L/16),N,2] with
+ *             PDSSM_COMPLEX:  x_chunks[b,h,c] = x_{16c-1}  (x0, or zero, for
+ *             c = 0); caller-owned, 16-byte aligned, not NULL
+ * Every other argument, the workspace size and the errors as pdssm_scan_fwd.
+ */
+int pdssm_scan_fwd_save(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
+                        const void *b, const void *c, void *y, void *x_final, void *x_chunks,
+                        int64_t B, int64_t H, int64_t L, int32_t N, int32_t K, uint32_t flags,
+                        const void *x0, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * Gradients of the forward scan (reverse mode), the pass training needs.
+ * Methodology, "1. Novel Selection Mechanism (Hard Selection)": training
+ * goes through the hard selection; the pages name a straight-through
+ * estimator for the scores but print no formula, so the selection (and the
+ * dictionary) get no gradient here.  For a real loss with dL/dy[b,h,t] = gy
+ * and dL/dx_final = gx_final, complex gradients written dL/dRe + i dL/dIm,
+ * and A_t = P_t D_t as in pdssm_scan_fwd:
+ *     lambda_{L-1} = gy_{L-1} conj(c_{L-1}) + gx_final
+ *     lambda_t     = gy_t conj(c_t) + A_{t+1}^H lambda_{t+1},
+ *                    (A^H l)[j] = conj(d[j]) l[pi[j]]
+ *     gb[t] = lambda_t
+ *     gc[t] = gy_t conj(x_t)
+ *     gd[t][j] = conj(x_{t-1}[j]) lambda_t[pi_t[j]]
+ *     gx0 = A_0^H lambda_0
+ * Inputs: the forward's sel_or_logits, dict_idx, diag, b, c and flags;
+ *   x_chunks from pdssm_scan_fwd_save on the same inputs (and x0);
+ *   gy [B,H,L] in the storage of y (bf16 with PDSSM_Y_BF16, else fp32);
+ *   gx_final fp32 [B,H,N(,2)], or NULL for zero.
+ * Outputs (caller-owned, 16-byte aligned): gb and gc in the storage of b and
+ *   c (bf16, rounded to nearest even, with PDSSM_BC_BF16, else fp32), gd in
+ *   the storage of diag, gx0 fp32 [B,H,N(,2)] or NULL when not wanted.
+ * Arithmetic fp32 (complex fp32), any summation order.  Workspace sized by
+ * pdssm_scan_bwd_workspace_bytes.  Errors as pdssm_scan_fwd.
+ */
+int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
+                   const void *b, const void *c, const void *x_chunks, const void *gy,
+                   const void *gx_final, void *gb, void *gc, void *gd, void *gx0, int64_t B,
+                   int64_t H, int64_t L, int32_t N, int32_t K, uint32_t flags, void *workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes pdssm_scan_bwd needs (O(B*H*L*N/16), never N*N*L); 0 when
+ * the arguments are invalid. */
+size_t pdssm_scan_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K,
+                                      uint32_t flags);
+
+/*
  * The selection step alone: sel_out[b,h,t] = the dictionary entry step t
  * picks (Methodology, "1. Novel Selection Mechanism": argmax of the K
  * scores; index modes copy the index).  flags: selection bits only.

@@ -72,6 +72,14 @@ def library() -> ctypes.CDLL:
         lib.pdssm_select.restype = ctypes.c_int
         lib.pdssm_compose.argtypes = [P, P, P, P, P, I64, I64, I64, I32, I32, U32, P, SZ, P]
         lib.pdssm_compose.restype = ctypes.c_int
+        lib.pdssm_scan_fwd_save.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I32, I32, U32, P, P,
+                                            SZ, P]
+        lib.pdssm_scan_fwd_save.restype = ctypes.c_int
+        lib.pdssm_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I32, I32, U32,
+                                       P, SZ, P]
+        lib.pdssm_scan_bwd.restype = ctypes.c_int
+        lib.pdssm_scan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I32, I32, U32]
+        lib.pdssm_scan_bwd_workspace_bytes.restype = SZ
         lib.pdssm_strerror.argtypes = [ctypes.c_int]
         lib.pdssm_strerror.restype = ctypes.c_char_p
         _LIB = lib
@@ -115,6 +123,26 @@ def pdssm_scan_fwd(sel_or_logits, dict_idx, diag, b, c, y, x_final, B, H, L, N, 
 
 def pdssm_scan_workspace_bytes(B, H, L, N, K, flags) -> int:
     return library().pdssm_scan_workspace_bytes(B, H, L, N, K, flags)
+
+
+def pdssm_scan_fwd_save(sel_or_logits, dict_idx, diag, b, c, y, x_final, x_chunks, B, H, L, N, K,
+                        flags, x0, workspace, workspace_bytes, stream=None) -> int:
+    return library().pdssm_scan_fwd_save(_ptr(sel_or_logits), _ptr(dict_idx), _ptr(diag), _ptr(b),
+                                         _ptr(c), _ptr(y), _ptr(x_final), _ptr(x_chunks), B, H, L, N,
+                                         K, flags, _ptr(x0), _ptr(workspace), workspace_bytes,
+                                         _stream(stream))
+
+
+def pdssm_scan_bwd(sel_or_logits, dict_idx, diag, b, c, x_chunks, gy, gx_final, gb, gc, gd, gx0, B,
+                   H, L, N, K, flags, workspace, workspace_bytes, stream=None) -> int:
+    return library().pdssm_scan_bwd(_ptr(sel_or_logits), _ptr(dict_idx), _ptr(diag), _ptr(b),
+                                    _ptr(c), _ptr(x_chunks), _ptr(gy), _ptr(gx_final), _ptr(gb),
+                                    _ptr(gc), _ptr(gd), _ptr(gx0), B, H, L, N, K, flags,
+                                    _ptr(workspace), workspace_bytes, _stream(stream))
+
+
+def pdssm_scan_bwd_workspace_bytes(B, H, L, N, K, flags) -> int:
+    return library().pdssm_scan_bwd_workspace_bytes(B, H, L, N, K, flags)
 
 
 def pdssm_select(sel_or_logits, sel_out, B, H, L, K, flags, stream=None) -> int:
@@ -180,6 +208,51 @@ def scan(inp, *, workspace: Optional[torch.Tensor] = None, want_x_final: bool = 
                          x_final if want_x_final else None, inp.B, inp.H, inp.L, inp.N, inp.K,
                          flags_of(inp), x0t, workspace, workspace.numel(), stream))
     return y, (x_final if want_x_final else None)
+
+
+CARRY_STRIDE = 16   # steps per saved chunk carry (include/pdssm.h)
+
+
+def scan_save(inp, *, workspace: Optional[torch.Tensor] = None, stream=None):
+    """pdssm_scan_fwd_save on a batch: (y, x_final, x_chunks)."""
+    dev = inp.diag.device
+    y = torch.empty((inp.B, inp.H, inp.L), device=dev,
+                    dtype=torch.bfloat16 if inp.y_bf16 else torch.float32)
+    tail = (inp.N, 2) if inp.complex else (inp.N,)
+    x_final = torch.empty((inp.B, inp.H) + tail, device=dev, dtype=torch.float32)
+    nch = (inp.L + CARRY_STRIDE - 1) // CARRY_STRIDE
+    x_chunks = torch.empty((inp.B, inp.H, nch) + tail, device=dev, dtype=torch.float32)
+    if workspace is None:
+        workspace = workspace_for(inp)
+    check(pdssm_scan_fwd_save(inp.sel_or_logits, inp.dict_idx, inp.diag, inp.b, inp.c, y, x_final,
+                              x_chunks, inp.B, inp.H, inp.L, inp.N, inp.K, flags_of(inp), inp.x0,
+                              workspace, workspace.numel(), stream))
+    return y, x_final, x_chunks
+
+
+def bwd_workspace_for(inp, device=None) -> torch.Tensor:
+    n = pdssm_scan_bwd_workspace_bytes(inp.B, inp.H, inp.L, inp.N, inp.K, flags_of(inp))
+    if n == 0:
+        raise PdssmError(PDSSM_ERR_DIM, "invalid sizes")
+    return torch.empty(n, dtype=torch.uint8, device=device or inp.diag.device)
+
+
+def scan_bwd(inp, x_chunks, gy, gx_final=None, *, want_gx0: bool = True,
+             workspace: Optional[torch.Tensor] = None, stream=None):
+    """pdssm_scan_bwd on a batch: (gb, gc, gd, gx0 or None), in the storage
+    of b, c, diag and x0."""
+    dev = inp.diag.device
+    gb = torch.empty_like(inp.b)
+    gc = torch.empty_like(inp.c)
+    gd = torch.empty_like(inp.diag)
+    tail = (inp.N, 2) if inp.complex else (inp.N,)
+    gx0 = torch.empty((inp.B, inp.H) + tail, device=dev, dtype=torch.float32) if want_gx0 else None
+    if workspace is None:
+        workspace = bwd_workspace_for(inp)
+    check(pdssm_scan_bwd(inp.sel_or_logits, inp.dict_idx, inp.diag, inp.b, inp.c, x_chunks, gy,
+                         gx_final, gb, gc, gd, gx0, inp.B, inp.H, inp.L, inp.N, inp.K, flags_of(inp),
+                         workspace, workspace.numel(), stream))
+    return gb, gc, gd, gx0
 
 
 def select(sel_or_logits, sel_mode: str, K: int, stream=None) -> torch.Tensor:

@@ -627,6 +627,48 @@ __device__ __forceinline__ cf scatter_add(cf *scr, int lane, int base, int pi, c
 }
 
 // ---------------------------------------------------------------------------
+// The collision-free scatter of one step.  A chunk wave's scatter area has
+// 2R + 1 blocks of 64 complex slots: blocks 0 .. R-1 hold regions R-1 .. 0
+// (region r at block R-1-r), R .. 2R-1 stay zero, 2R is the spare for
+// sources of rank >= R.  Source j stores into row pi(j) of the region of
+// its rank (rank = number of sources j' < j with the same destination), so
+// a region never has two sources on one row; row i reads the R blocks from
+// block R - min(deg(i), R) on: its deg(i) regions, then zero blocks.
+// ---------------------------------------------------------------------------
+// The forward scan can keep the state before every chunk of kCarryStride
+// steps; the backward scan works on chunks of the same length.
+constexpr int kCarryStride = 16;
+
+#ifndef PDSSM_SCAN_REGIONS
+#define PDSSM_SCAN_REGIONS 3
+#endif
+constexpr int kRegions = PDSSM_SCAN_REGIONS;   // collision-free regions (ranks 0..kRegions-1)
+constexpr int kRegionBytes = 64 * 8;           // one block: 64 complex slots
+constexpr int kBlocks = 2 * kRegions + 1;
+constexpr uint32_t kSpareOff = 2 * kRegions * kRegionBytes;
+static_assert(kBlocks <= 8 && kRegions <= 3, "entries hold a 3-bit scatter block and a 2-bit read block");
+
+// The 16-bit entry of source `lane` for the index map row[0..N):
+//   pi | scatter block << 6 | read block << 9.
+// Called by a whole wave (lanes >= N are padding sources that map to
+// themselves with rank 0 and in-degree 1); entries outside [0,N) clamp.
+__device__ __forceinline__ uint16_t dict_entry(const int32_t *row, int N, int lane)
+{
+    const int pi = lane < N ? (int)min((unsigned)row[lane], (unsigned)(N - 1)) : lane;
+    int rank = 0, deg = 0;
+    for (int jj = 0; jj < N; ++jj) {
+        const int pj = __builtin_amdgcn_readlane(pi, jj);
+        rank += (jj < lane && pj == pi) ? 1 : 0;
+        deg += (pj == lane) ? 1 : 0;
+    }
+    if (lane >= N)
+        deg = 1;   // padding rows hold their own (zero) state
+    const int block = rank < kRegions ? kRegions - 1 - rank : 2 * kRegions;
+    const int rblock = kRegions - min(deg, kRegions);
+    return (uint16_t)(pi | (block << 6) | (rblock << 9));
+}
+
+// ---------------------------------------------------------------------------
 // Carry records in the workspace.  Each 64-bit word holds a 32-bit payload
 // and, in its upper half, the epoch of the call that wrote it, so a reader
 // knows a word is from this call without any fence between words.

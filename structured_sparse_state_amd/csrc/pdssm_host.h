@@ -1,0 +1,17 @@
+// pdssm_host.h -- host-side checks shared by the library's source files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pdssm {
+
+// True when p is 16-byte aligned.
+__attribute__((visibility("hidden"))) bool aligned16(const void *p);
+// PDSSM_OK, or PDSSM_ERR_DIM when the sizes are out of the supported range.
+__attribute__((visibility("hidden"))) int check_dims(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K);
+// PDSSM_OK for hipSuccess, else PDSSM_ERR_HIP (the HIP text goes to pdssm_strerror).
+__attribute__((visibility("hidden"))) int hip_status(hipError_t e);
+
+}  // namespace pdssm

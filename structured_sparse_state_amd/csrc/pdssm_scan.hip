@@ -31,6 +31,7 @@
 
 #include "pdssm.h"
 #include "pdssm_device.h"
+#include "pdssm_host.h"
 
 namespace pdssm {
 
@@ -52,6 +53,9 @@ struct ScanArgs {
     // w % H and takes its tiles from ctr[32 * h], total_head = n_tiles * B.
     uint32_t *ctr;
     uint32_t total_head;
+    // Optional: the state before each chunk of kScanT steps, [S][nch][N(,2)].
+    float *xsave;
+    int64_t nch;
     int N, K;
     uint32_t sel_mode;
     int y_bf16;
@@ -74,6 +78,7 @@ constexpr int kScanT = PDSSM_SCAN_T;
 constexpr int kScanW = PDSSM_SCAN_W;
 constexpr int kScanD = PDSSM_SCAN_D;   // steps of inputs in flight per lane (register ring)
 static_assert(kScanW >= 1 && kScanW <= 32, "chunk waves post into a 32-bit mask");
+static_assert(kScanT == kCarryStride, "the saved carries are one per chunk of the backward scan");
 constexpr int kDictLdsMax = 32768;   // bytes of the head's entry table kept in LDS
 #ifndef PDSSM_POLL_TICKS
 #define PDSSM_POLL_TICKS 80
@@ -87,18 +92,6 @@ constexpr uint64_t kPollTicks = PDSSM_POLL_TICKS;   // look-back loads are used 
 #ifndef PDSSM_CARRY_PRIO
 #define PDSSM_CARRY_PRIO 2   // s_setprio level of the carry wave (chunk waves stay at 0)
 #endif
-#ifndef PDSSM_SCAN_REGIONS
-#define PDSSM_SCAN_REGIONS 3
-#endif
-constexpr int kRegions = PDSSM_SCAN_REGIONS;   // collision-free scatter regions (ranks 0..kRegions-1)
-constexpr int kRegionBytes = 64 * 8;           // one block: 64 complex slots
-// A chunk wave's scatter area, in blocks:  0 .. R-1 hold regions R-1 .. 0
-// (region r at block R-1-r), R .. 2R-1 are always zero, 2R is the spare
-// for sources of rank >= R.  A row of in-degree d reads the R blocks from
-// block R-d on: its d regions, then zeros -- no per-region test.
-constexpr int kBlocks = 2 * kRegions + 1;
-constexpr uint32_t kSpareOff = 2 * kRegions * kRegionBytes;
-static_assert(kBlocks <= 8 && kRegions <= 3, "entries hold a 3-bit scatter block and a 2-bit read block");
 
 __host__ __device__ constexpr int scan_tile_steps(int NP) { return kScanW * (64 / NP) * kScanT; }
 
@@ -626,6 +619,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
     __amdgpu_buffer_rsrc_t rsd, rsb, rsc;
     const int L = (int)a.L;   // steps fit 31 bits (the host checks)
     int64_t row0 = 0;         // index of the sequence's first step
+    uint32_t cseq = 0;        // the sequence
     int tw0 = 0, wrow = 0;    // the wave's first step; the first buffer row
     bool full = false;        // every chunk of the wave lies inside the sequence
     uint32_t h = 0;
@@ -651,6 +645,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         uint32_t tile, seq;
         decode(u, tile, seq);
         h = __builtin_amdgcn_readfirstlane(seq % H32);
+        cseq = seq;
         row0 = (int64_t)seq * a.L;
         tw0 = (int)tile * TILE + chunk_pos(wave) * G * T;
         full = tw0 + G * T <= L;
@@ -719,6 +714,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         const int cw0 = tw0;                // the wave's first step
         const int tc0 = cw0 + q.g * T;      // first step of the chunk
         const int64_t y0 = row0 + cw0;      // y index of the wave's first step
+        const uint32_t seq0 = cseq;
         const int nvalid = max(0, min(T, L - tc0));
         // The same bound, re-derived where it is tested again, so that the
         // compiler does not keep one test's outcome alive across blocks.
@@ -950,6 +946,17 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             // once it has left this barrier.
             __syncthreads();   // (D) prefixes and carry read
             const cf xc = scatter_add<CPLX>(scr, r.ln, r.gbase, ppi, cmul(pd, xt), pe);
+            // The state before the chunk's first step, kept for the backward scan.
+            if (a.xsave) {
+                const int tcs = cw0 + r.g * T;
+                if (tcs < L && r.row_ok) {
+                    constexpr int NC = CPLX ? 2 : 1;
+                    float *o = a.xsave + (((int64_t)seq0 * a.nch + tcs / T) * N + r.i) * NC;
+                    o[0] = xc.r;
+                    if constexpr (CPLX)
+                        o[1] = xc.i;
+                }
+            }
             float wc[T / 4];
 #pragma unroll
             for (int m = 0; m < T / 4; ++m) {
@@ -997,13 +1004,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
 // ---------------------------------------------------------------------------
 // Per-call preparation.
 //  * Blocks >= 1, one wave per dictionary entry (h, k): the entry table
-//    tab[h][k][j] = pi(j) | block(j) << 6 | (kRegions - min(deg(j), kRegions)) << 9
-//    in 16 bits, blocks of a chunk wave's scatter area: source j stores into
-//    row pi(j) of block(j), the block of region rank(j) (the spare block
-//    when rank(j) >= kRegions); row j reads kRegions blocks from the block
-//    in bits 9-10 on.  rank(j) counts the sources j' < j with the same
-//    destination and deg(j) the sources whose destination is j.  Padding
-//    sources j >= N map to themselves with rank 0 and in-degree 1.
+//    tab[h][k][j] = dict_entry(): the 16-bit scatter entry of source j.
 //  * Block 0: new epoch and ticket resets; on first use (or after the epoch
 //    wraps) clear every carry record.
 // ---------------------------------------------------------------------------
@@ -1019,18 +1020,7 @@ __global__ void __launch_bounds__(kPrepThreads) prep_kernel(Header *hdr, uint32_
         const int64_t e = (int64_t)(blockIdx.x - 1) * (kPrepThreads / 64) + (threadIdx.x >> 6);
         if (e >= entries || lane >= NP)
             return;
-        const int pi = lane < N ? (int)min((unsigned)dict[e * N + lane], (unsigned)(N - 1)) : lane;
-        int rank = 0, deg = 0;
-        for (int jj = 0; jj < N; ++jj) {
-            const int pj = __builtin_amdgcn_readlane(pi, jj);
-            rank += (jj < lane && pj == pi) ? 1 : 0;
-            deg += (pj == lane) ? 1 : 0;
-        }
-        if (lane >= N)
-            deg = 1;   // padding rows hold their own (zero) state
-        const int block = rank < kRegions ? kRegions - 1 - rank : 2 * kRegions;
-        const int rblock = kRegions - min(deg, kRegions);
-        tab[e * NP + lane] = (uint16_t)(pi | (block << 6) | (rblock << 9));
+        tab[e * NP + lane] = dict_entry(dict + e * N, N, lane);
         return;
     }
     __shared__ int s_fresh;
@@ -1212,9 +1202,9 @@ constexpr int64_t kMaxL = (int64_t)1 << 30;
 
 static int pad_states(int N) { return N <= 8 ? 8 : N <= 16 ? 16 : N <= 32 ? 32 : 64; }
 
-static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-static int check_dims(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K)
+int check_dims(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K)
 {
     if (B < 1 || H < 1 || L < 1 || L > kMaxL || N < 1 || N > 64 || K < 1 || K > 32767)
         return PDSSM_ERR_DIM;
@@ -1254,7 +1244,7 @@ static Layout layout_of(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K, u
     return lo;
 }
 
-static int hip_status(hipError_t e)
+int hip_status(hipError_t e)
 {
     if (e == hipSuccess)
         return PDSSM_OK;
@@ -1340,14 +1330,15 @@ extern "C" size_t pdssm_scan_workspace_bytes(int64_t B, int64_t H, int64_t L, in
     return (size_t)layout_of(B, H, L, N, K, flags).total;
 }
 
-extern "C" int pdssm_scan_fwd(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
-                              const void *b, const void *c, void *y, void *x_final, int64_t B,
-                              int64_t H, int64_t L, int32_t N, int32_t K, uint32_t flags,
-                              const void *x0, void *workspace, size_t workspace_bytes,
-                              hipStream_t stream)
+static int scan_fwd(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
+                    const void *b, const void *c, void *y, void *x_final, int64_t B, int64_t H,
+                    int64_t L, int32_t N, int32_t K, uint32_t flags, const void *x0,
+                    void *workspace, size_t workspace_bytes, void *x_chunks, hipStream_t stream)
 {
     if (!sel_or_logits || !dict_idx || !diag || !b || !c || !y || !workspace)
         return PDSSM_ERR_NULL;
+    if (x_chunks && !aligned16(x_chunks))
+        return PDSSM_ERR_ALIGN;
     int rc = check_dims(B, H, L, N, K);
     if (rc != PDSSM_OK)
         return rc;
@@ -1370,6 +1361,8 @@ extern "C" int pdssm_scan_fwd(const void *sel_or_logits, const int32_t *dict_idx
     a.y = y;
     a.xfinal = static_cast<float *>(x_final);
     a.x0 = static_cast<const float *>(x0);
+    a.xsave = static_cast<float *>(x_chunks);
+    a.nch = (L + kScanT - 1) / kScanT;
     a.hdr = static_cast<Header *>(workspace);
     uint32_t *ctr = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + sizeof(Header));
     uint16_t *tab = reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(ctr) + lo.ctr_bytes);
@@ -1409,6 +1402,28 @@ extern "C" int pdssm_scan_fwd(const void *sel_or_logits, const int32_t *dict_idx
     if (e == hipSuccess)
         e = hipGetLastError();
     return hip_status(e);
+}
+
+extern "C" int pdssm_scan_fwd(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
+                              const void *b, const void *c, void *y, void *x_final, int64_t B,
+                              int64_t H, int64_t L, int32_t N, int32_t K, uint32_t flags,
+                              const void *x0, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream)
+{
+    return scan_fwd(sel_or_logits, dict_idx, diag, b, c, y, x_final, B, H, L, N, K, flags, x0,
+                    workspace, workspace_bytes, nullptr, stream);
+}
+
+extern "C" int pdssm_scan_fwd_save(const void *sel_or_logits, const int32_t *dict_idx,
+                                   const void *diag, const void *b, const void *c, void *y,
+                                   void *x_final, void *x_chunks, int64_t B, int64_t H, int64_t L,
+                                   int32_t N, int32_t K, uint32_t flags, const void *x0,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (!x_chunks)
+        return PDSSM_ERR_NULL;
+    return scan_fwd(sel_or_logits, dict_idx, diag, b, c, y, x_final, B, H, L, N, K, flags, x0,
+                    workspace, workspace_bytes, x_chunks, stream);
 }
 
 extern "C" int pdssm_select(const void *sel_or_logits, int32_t *sel_out, int64_t B, int64_t H,

@@ -271,3 +271,19 @@ def make_fsa_inputs(kind: str, *, B: int = 1, H: int = 1, L: int = 256, N: int =
     return ScanInputs(sel_mode=sel_mode, sel_or_logits=sel.contiguous(), dict_idx=dict_idx.contiguous(),
                       diag=diag, b=b, c=c, complex=complex, bc_bf16=False, y_bf16=False, x0=x0,
                       B=B, H=H, L=L, N=N, K=K)
+
+
+def make_grads(inp: ScanInputs, *, seed: int = 0, with_gx_final: bool = True, device=None):
+    """Seeded upstream gradients for the backward scan of ``inp``: gy in the
+    storage of y ([B,H,L], N(0,1), bf16 rounded once when y is bf16) and
+    gx_final fp32 [B,H,N(,2)] N(0,1), or None."""
+    device = device or inp.diag.device
+    g = _gen(device, 7919 + seed)
+    gy = torch.randn((inp.B, inp.H, inp.L), generator=g, device=device, dtype=torch.float32)
+    if inp.y_bf16:
+        gy = gy.to(torch.bfloat16)
+    gxf = None
+    if with_gx_final:
+        tail = (inp.N, 2) if inp.complex else (inp.N,)
+        gxf = torch.randn((inp.B, inp.H) + tail, generator=g, device=device, dtype=torch.float32)
+    return gy, gxf

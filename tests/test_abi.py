@@ -17,7 +17,8 @@ def lib():
 def test_exports_every_declared_function(lib):
     names = pk.header_functions()
     assert set(names) == {"pdssm_scan_fwd", "pdssm_scan_workspace_bytes", "pdssm_select",
-                          "pdssm_compose", "pdssm_strerror"}
+                          "pdssm_compose", "pdssm_strerror", "pdssm_scan_fwd_save",
+                          "pdssm_scan_bwd", "pdssm_scan_bwd_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -91,3 +92,41 @@ def test_workspace_is_linear_in_length_not_quadratic_in_state(lib):
     assert base < 0.03 * inputs
     assert pk.pdssm_scan_workspace_bytes(0, 1, 1, 1, 1, 0) == 0
     assert pk.pdssm_scan_workspace_bytes(1, 1, 1, 1, 1, 0x40) == 0
+
+
+def _bwd(**kw):
+    args = dict(sel=FAKE, dict_idx=FAKE, diag=FAKE, b=FAKE, c=FAKE, xch=FAKE, gy=FAKE, gxf=None,
+                gb=FAKE, gc=FAKE, gd=FAKE, gx0=None, B=2, H=3, L=100, N=16, K=8,
+                flags=pk.PDSSM_LOGITS_BF16, ws=FAKE, ws_bytes=1 << 40)
+    args.update(kw)
+    a = args
+    return pk.pdssm_scan_bwd(a["sel"], a["dict_idx"], a["diag"], a["b"], a["c"], a["xch"], a["gy"],
+                             a["gxf"], a["gb"], a["gc"], a["gd"], a["gx0"], a["B"], a["H"], a["L"],
+                             a["N"], a["K"], a["flags"], a["ws"], a["ws_bytes"], 0)
+
+
+def test_bwd_and_save_argument_errors(lib):
+    for name in ("sel", "dict_idx", "diag", "b", "c", "xch", "gy", "gb", "gc", "gd", "ws"):
+        assert _bwd(**{name: None}) == pk.PDSSM_ERR_NULL, name
+    for bad in (dict(B=0), dict(L=0), dict(N=65), dict(K=0)):
+        assert _bwd(**bad) == pk.PDSSM_ERR_DIM, bad
+    assert _bwd(flags=0x20) == pk.PDSSM_ERR_FLAGS
+    for name in ("sel", "diag", "xch", "gy", "gxf", "gb", "gd", "gx0", "ws"):
+        assert _bwd(**{name: FAKE + 4}) == pk.PDSSM_ERR_ALIGN, name
+    need = pk.pdssm_scan_bwd_workspace_bytes(2, 3, 100, 16, 8, pk.PDSSM_LOGITS_BF16)
+    assert need > 0
+    assert _bwd(ws_bytes=need - 1) == pk.PDSSM_ERR_WORKSPACE
+    assert pk.pdssm_scan_bwd_workspace_bytes(0, 1, 1, 1, 1, 0) == 0
+    s = pk.pdssm_scan_fwd_save
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 2, 3, 100, 16, 8, 0, None, FAKE,
+             1 << 40, 0) == pk.PDSSM_ERR_NULL
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE + 8, 2, 3, 100, 16, 8, 0, None, FAKE,
+             1 << 40, 0) == pk.PDSSM_ERR_ALIGN
+
+
+def test_bwd_workspace_is_linear(lib):
+    f = pk.PDSSM_LOGITS_BF16 | pk.PDSSM_COMPLEX | pk.PDSSM_BC_BF16 | pk.PDSSM_Y_BF16
+    ws = lambda B, H, L: pk.pdssm_scan_bwd_workspace_bytes(B, H, L, 64, 64, f)
+    base = ws(8, 32, 4096)
+    assert ws(8, 32, 8192) <= 2 * base
+    assert ws(16, 32, 4096) <= 2 * base
