@@ -32,6 +32,8 @@
 //              over it from K_c, writing gb, gc and gd.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "pdssm.h"
 #include "pdssm_device.h"
 #include "pdssm_host.h"
@@ -40,7 +42,6 @@ namespace pdssm {
 
 constexpr int kBT = kCarryStride;   // steps per chunk (the forward saves one carry per chunk)
 constexpr int kBW = 4;              // chunk waves per workgroup
-constexpr int kCarryRing = 8;       // chunk records in flight in bwd_carry
 
 struct BwdArgs {
     const void *sel;
@@ -59,6 +60,9 @@ struct BwdArgs {
     int32_t *sig;       // [S*nch][64] composed map of each chunk
     float4 *mv;         // [S*nch][64] (conj dacc, v)
     float2 *kc;         // [S*nch][64] adjoint carried into each chunk's last step
+    int32_t *gsig;      // [S*ng][64] group operators (ng = ceil(nch / kGroup))
+    float4 *gmv;
+    float2 *gk;         // [S*ng][64] adjoint carried into each group's last chunk
     int64_t H, L, S, nch;
     int N, K;
     uint32_t sel_mode;
@@ -72,21 +76,6 @@ __device__ __forceinline__ void store_grad(float *p, int64_t e, cf v)
         reinterpret_cast<float2 *>(p)[e] = make_float2(v.r, v.i);
     else
         p[e] = v.r;
-}
-
-// A gradient in the storage of b or c (bf16, rounded to nearest even, or fp32).
-template <bool CPLX, bool BF16>
-__device__ __forceinline__ void store_vec(void *p, int64_t e, cf v)
-{
-    if constexpr (BF16) {
-        if constexpr (CPLX)
-            reinterpret_cast<uint32_t *>(p)[e] =
-                (uint32_t)f32_to_bf16_rne(v.r) | ((uint32_t)f32_to_bf16_rne(v.i) << 16);
-        else
-            reinterpret_cast<uint16_t *>(p)[e] = f32_to_bf16_rne(v.r);
-    } else {
-        store_grad<CPLX>(reinterpret_cast<float *>(p), e, v);
-    }
 }
 
 __device__ __forceinline__ float load_gy(const BwdArgs &a, int64_t step)
@@ -109,6 +98,138 @@ __global__ void __launch_bounds__(256) bwd_tab_kernel(const int32_t *dict, uint1
 }
 
 // ---------------------------------------------------------------------------
+// Loads and stores of one chunk's rows through buffer resources: the rows of
+// the chunk start at the resource base, the row offset of a step is
+// wave-uniform (scalar), the lane offset is fixed.  Padding lanes (>= N) get
+// an offset past every resource, so their loads read 0 and their stores are
+// dropped by the hardware -- no branches.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kOffLane = 0x80000000u;
+
+// b and c as loaded: bf16 words stay packed (a pair when complex).
+template <bool CPLX, bool BCBF>
+struct RawOf {
+    using type = typename std::conditional<BCBF, uint32_t, typename std::conditional<CPLX, float2, float>::type>::type;
+};
+
+template <bool CPLX, bool BCBF>
+__device__ __forceinline__ cf unpack_c(typename RawOf<CPLX, BCBF>::type v)
+{
+    if constexpr (BCBF)
+        return {bf16_lo(v), CPLX ? bf16_hi(v) : 0.f};
+    else if constexpr (CPLX)
+        return {v.x, v.y};
+    else
+        return {v, 0.f};
+}
+
+// The raw value of the lane at byte address addr (4 * lane).
+template <bool CPLX, bool BCBF>
+__device__ __forceinline__ typename RawOf<CPLX, BCBF>::type bperm_raw(typename RawOf<CPLX, BCBF>::type v, int addr)
+{
+    if constexpr (BCBF)
+        return bperm_a((uint32_t)v, addr);
+    else if constexpr (CPLX)
+        return make_float2(bperm_a(v.x, addr), bperm_a(v.y, addr));
+    else
+        return bperm_a(v, addr);
+}
+
+template <bool CPLX, bool BCBF>
+struct ChunkIO {
+    using DRaw = typename std::conditional<CPLX, float2, float>::type;
+    using Stored = typename std::conditional<BCBF, typename std::conditional<CPLX, uint32_t, uint16_t>::type,
+                                             DRaw>::type;
+    __amdgpu_buffer_rsrc_t rd, rb, rc, rt;
+    uint32_t vd, vs, vt;   // lane offsets (bytes) into diag-like, b/c-like rows and the entry table
+    int N;
+
+    __device__ void init(const BwdArgs &a, int64_t seq, int64_t t0, int nv, int64_t h, int lane)
+    {
+        N = a.N;
+        const int64_t e0 = (seq * a.L + t0) * a.N;   // first element of the chunk
+        const uint64_t rows = (uint64_t)nv * (uint64_t)a.N;
+        rd = make_rsrc(reinterpret_cast<const DRaw *>(a.diag) + e0, rows * sizeof(DRaw));
+        rb = make_rsrc(reinterpret_cast<const Stored *>(a.b) + e0, rows * sizeof(Stored));
+        rc = make_rsrc(reinterpret_cast<const Stored *>(a.c) + e0, rows * sizeof(Stored));
+        rt = make_rsrc(a.tab + h * (int64_t)a.K * 64, (uint64_t)a.K * 64 * 2);
+        const bool act = lane < a.N;
+        vd = act ? (uint32_t)(lane * sizeof(DRaw)) : kOffLane;
+        vs = act ? (uint32_t)(lane * sizeof(Stored)) : kOffLane;
+        vt = (uint32_t)(lane * 2);   // the table has all 64 lanes (padding maps to itself)
+    }
+    __device__ cf d(int tt) const
+    {
+        const DRaw v = bload<DRaw>(rd, vd, (uint32_t)(tt * N * (int)sizeof(DRaw)));
+        if constexpr (CPLX)
+            return {v.x, v.y};
+        else
+            return {v, 0.f};
+    }
+    __device__ typename RawOf<CPLX, BCBF>::type raw_b(int tt) const
+    {
+        return (typename RawOf<CPLX, BCBF>::type)bload<Stored>(rb, vs, (uint32_t)(tt * N * (int)sizeof(Stored)));
+    }
+    __device__ typename RawOf<CPLX, BCBF>::type raw_c(int tt) const
+    {
+        return (typename RawOf<CPLX, BCBF>::type)bload<Stored>(rc, vs, (uint32_t)(tt * N * (int)sizeof(Stored)));
+    }
+    __device__ uint32_t ent(int k) const { return bload<uint16_t>(rt, vt, (uint32_t)(k * 128)); }
+};
+
+// The chunk's 16 upstream gradients gy, one per lane (lanes 0..nv-1).
+__device__ __forceinline__ float chunk_gy(const BwdArgs &a, int64_t step0, int nv, int lane)
+{
+    const int l = min(lane, nv - 1);
+    return load_gy(a, step0 + l);
+}
+
+template <typename V>
+__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, V v, uint32_t voff, uint32_t soff)
+{
+    if constexpr (sizeof(V) == 8) {
+        typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+        u2 w;
+        __builtin_memcpy(&w, &v, 8);
+        __builtin_amdgcn_raw_buffer_store_b64(w, r, voff, soff, 0);
+    } else if constexpr (sizeof(V) == 4) {
+        uint32_t w;
+        __builtin_memcpy(&w, &v, 4);
+        __builtin_amdgcn_raw_buffer_store_b32(w, r, voff, soff, 0);
+    } else {
+        static_assert(sizeof(V) == 2, "2, 4 or 8 bytes");
+        uint16_t w;
+        __builtin_memcpy(&w, &v, 2);
+        __builtin_amdgcn_raw_buffer_store_b16(w, r, voff, soff, 0);
+    }
+}
+
+// A gradient in the raw storage of b or c (bf16 rounded to nearest even, or fp32).
+template <bool CPLX, bool BCBF>
+__device__ __forceinline__ typename ChunkIO<CPLX, BCBF>::Stored pack_vec(cf v)
+{
+    if constexpr (BCBF) {
+        if constexpr (CPLX)
+            return (uint32_t)f32_to_bf16_rne(v.r) | ((uint32_t)f32_to_bf16_rne(v.i) << 16);
+        else
+            return f32_to_bf16_rne(v.r);
+    } else if constexpr (CPLX) {
+        return make_float2(v.r, v.i);
+    } else {
+        return v.r;
+    }
+}
+
+template <bool CPLX>
+__device__ __forceinline__ typename std::conditional<CPLX, float2, float>::type pack_d(cf v)
+{
+    if constexpr (CPLX)
+        return make_float2(v.r, v.i);
+    else
+        return v.r;
+}
+
+// ---------------------------------------------------------------------------
 // bwd_ops: per chunk, lane j follows its forward path (pacc, dacc) through
 // the chunk and sums the adjoint's affine part v[j].
 // ---------------------------------------------------------------------------
@@ -124,89 +245,196 @@ __global__ void __launch_bounds__(kBW * 64) bwd_ops_kernel(BwdArgs a)
     const int64_t t0 = (ch - seq * a.nch) * kBT;
     const int nv = (int)min((int64_t)kBT, a.L - t0);
     const int64_t h = seq % a.H;
-    const int N = a.N, K = a.K;
-    wave_select<kBT>(a.sel, a.sel_mode, K, a.L, seq * a.L, t0, s_sel[wave], lane);
-    const bool act = lane < N;
+    wave_select<kBT>(a.sel, a.sel_mode, a.K, a.L, seq * a.L, t0, s_sel[wave], lane);
+    ChunkIO<CPLX, BCBF> io;
+    io.init(a, seq, t0, nv, h, lane);
+    const float gyv = chunk_gy(a, seq * a.L + t0, nv, lane);
+    using Raw = typename RawOf<CPLX, BCBF>::type;
+    constexpr int D = 4;
+    cf rd[D];
+    Raw rc[D];
+    uint32_t re[D];
+    auto fetch = [&](int tt) {
+        const int ts = min(tt, nv - 1);
+        const int k = __builtin_amdgcn_readfirstlane((int)s_sel[wave][ts]);
+        rd[tt % D] = io.d(ts);
+        rc[tt % D] = io.raw_c(ts);
+        re[tt % D] = io.ent(k);
+    };
+#pragma unroll
+    for (int tt = 0; tt < D; ++tt)
+        fetch(tt);
     int pacc4 = lane * 4;
     cf dacc = {1.f, 0.f}, v = {0.f, 0.f};
-    for (int tt = 0; tt < nv; ++tt) {
-        const int64_t step = seq * a.L + t0 + tt;
-        const int k = s_sel[wave][tt];
-        const int pi = act ? (int)min((unsigned)a.dict[(h * K + k) * N + lane], (unsigned)(N - 1)) : lane;
-        const cf d = act ? load_diag<CPLX>(a.diag, step * N + lane) : cf{1.f, 0.f};
-        const cf cv = act ? load_vec<CPLX, BCBF>(a.c, step * N + lane) : cf{0.f, 0.f};
-        const float g = load_gy(a, step);
-        // pacc_t = pi_t[pacc_{t-1}], dacc_t = d_t[pacc_{t-1}] * dacc_{t-1}
-        const int np = (int)bperm_a((uint32_t)pi, pacc4);
-        cf dd;
-        dd.r = bperm_a(d.r, pacc4);
-        dd.i = CPLX ? bperm_a(d.i, pacc4) : 0.f;
-        dacc = cmul(dd, dacc);
-        pacc4 = np * 4;
-        // readout weight g_t[j] = c_t[pacc_t[j]] dacc_t[j]; v += gy_t conj(g_t)
-        cf cg;
-        cg.r = bperm_a(cv.r, pacc4);
-        cg.i = CPLX ? bperm_a(cv.i, pacc4) : 0.f;
-        const cf w = cmul(cg, dacc);
-        v.r += g * w.r;
-        v.i -= g * w.i;
+#pragma unroll
+    for (int tt = 0; tt < kBT; ++tt) {
+        const cf d = rd[tt % D];
+        const Raw craw = rc[tt % D];
+        const uint32_t ent = re[tt % D];
+        if (tt + D < kBT)
+            fetch(tt + D);
+        if (tt < nv) {
+            const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gyv), tt));
+            // pacc_t = pi_t[pacc_{t-1}], dacc_t = d_t[pacc_{t-1}] * dacc_{t-1}
+            const uint32_t np = bperm_a(ent & 63u, pacc4);
+            cf dd;
+            dd.r = bperm_a(d.r, pacc4);
+            dd.i = CPLX ? bperm_a(d.i, pacc4) : 0.f;
+            dacc = cmul(dd, dacc);
+            pacc4 = (int)(np << 2);
+            // readout weight g_t[j] = c_t[pacc_t[j]] dacc_t[j]; v += gy_t conj(g_t)
+            const cf cg = unpack_c<CPLX, BCBF>(bperm_raw<CPLX, BCBF>(craw, pacc4));
+            const cf w = cmul(cg, dacc);
+            v.r += g * w.r;
+            v.i -= g * w.i;
+        }
     }
     a.sig[ch * 64 + lane] = pacc4 >> 2;
     a.mv[ch * 64 + lane] = make_float4(dacc.r, -dacc.i, v.r, v.i);
 }
 
 // ---------------------------------------------------------------------------
-// bwd_carry: per sequence (one wave, lane = state), right to left over the
-// chunks: record K_c, then K_{c-1} = conj(dacc) K_c[pacc] + v_c.  The chunk
-// records do not depend on K, so a ring of them is in flight ahead.
+// The carries K_c, right to left, in three shallow passes instead of one
+// chain over all chunks: compose each group of kGroup chunk operators (in
+// parallel), chain the group operators per sequence, then expand each group
+// from its carry.  An operator (sig, m, v) maps K to m[j] K[sig[j]] + v[j];
+// applying (sig1, m1, v1) after (sig2, m2, v2) -- the chunk on the left
+// after the one on its right -- gives
+//     sig = sig2[sig1],  m = m1 * m2[sig1],  v = m1 * v2[sig1] + v1.
 // ---------------------------------------------------------------------------
+constexpr int kGroup = 32;   // chunks per group
+
+struct GOp {
+    int sig;
+    cf m, v;
+};
+
 template <bool CPLX>
-__global__ void __launch_bounds__(kBW * 64) bwd_carry_kernel(BwdArgs a)
+__device__ __forceinline__ GOp load_op(const BwdArgs &a, const int32_t *sig, const float4 *mv, int64_t rec, int lane)
+{
+    const float4 q = mv[rec * 64 + lane];
+    return {sig[rec * 64 + lane], {q.x, CPLX ? q.y : 0.f}, {q.z, CPLX ? q.w : 0.f}};
+}
+
+// apply `left` after `right` (right = the operator of the chunks on the right)
+template <bool CPLX>
+__device__ __forceinline__ GOp compose_left(GOp left, GOp right)
+{
+    const int src = left.sig * 4;
+    GOp r;
+    r.sig = (int)bperm_a((uint32_t)right.sig, src);
+    cf m2, v2;
+    m2.r = bperm_a(right.m.r, src);
+    m2.i = CPLX ? bperm_a(right.m.i, src) : 0.f;
+    v2.r = bperm_a(right.v.r, src);
+    v2.i = CPLX ? bperm_a(right.v.i, src) : 0.f;
+    r.m = cmul(left.m, m2);
+    const cf t = cmul(left.m, v2);
+    r.v = {t.r + left.v.r, t.i + left.v.i};
+    return r;
+}
+
+template <bool CPLX>
+__device__ __forceinline__ cf apply_op(GOp op, cf k)
+{
+    cf kg;
+    kg.r = bperm(k.r, op.sig);
+    kg.i = CPLX ? bperm(k.i, op.sig) : 0.f;
+    const cf t = cmul(op.m, kg);
+    return {t.r + op.v.r, t.i + op.v.i};
+}
+
+// One wave per group: the group's operator, its chunks composed right to left.
+template <bool CPLX>
+__global__ void __launch_bounds__(kBW * 64) bwd_group_kernel(BwdArgs a)
+{
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int64_t ng = (a.nch + kGroup - 1) / kGroup;
+    const int64_t gi = (int64_t)blockIdx.x * kBW + wave;
+    if (gi >= a.S * ng)
+        return;
+    const int64_t seq = gi / ng, g = gi - seq * ng;
+    const int64_t c0 = g * kGroup, c1 = min(c0 + kGroup, a.nch) - 1;
+    // ring slot r holds the chunk i = r (mod 4) from the right end of the group
+    GOp ring[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        ring[r] = load_op<CPLX>(a, a.sig, a.mv, seq * a.nch + max(c1 - r, c0), lane);
+    GOp acc = ring[0];
+    for (int64_t i0 = 0; i0 <= c1 - c0; i0 += 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t c = c1 - (i0 + r);
+            if (c >= c0) {
+                const GOp op = ring[r];
+                ring[r] = load_op<CPLX>(a, a.sig, a.mv, seq * a.nch + max(c - 4, c0), lane);
+                acc = (i0 + r == 0) ? op : compose_left<CPLX>(op, acc);
+            }
+        }
+    }
+    a.gsig[gi * 64 + lane] = acc.sig;
+    a.gmv[gi * 64 + lane] = make_float4(acc.m.r, acc.m.i, acc.v.r, acc.v.i);
+}
+
+// One wave per sequence: the carry into each group's last chunk, right to
+// left over the groups; then gx0.
+template <bool CPLX>
+__global__ void __launch_bounds__(kBW * 64) bwd_chain_kernel(BwdArgs a)
 {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int64_t seq = (int64_t)blockIdx.x * kBW + wave;
     if (seq >= a.S)
         return;
+    const int64_t ng = (a.nch + kGroup - 1) / kGroup;
     const bool act = lane < a.N;
     cf kk = {0.f, 0.f};
     if (a.gxf && act)
         kk = load_diag<CPLX>(a.gxf, seq * a.N + lane);
-    const int64_t nch = a.nch, base = seq * nch;
-    int32_t sg[kCarryRing];
-    float4 mv[kCarryRing];
-#pragma unroll
-    for (int r = 0; r < kCarryRing; ++r) {
-        const int64_t c = max(nch - 1 - r, (int64_t)0);
-        sg[r] = a.sig[(base + c) * 64 + lane];
-        mv[r] = a.mv[(base + c) * 64 + lane];
-    }
-    for (int64_t c0 = nch - 1; c0 >= 0; c0 -= kCarryRing) {
-#pragma unroll
-        for (int r = 0; r < kCarryRing; ++r) {
-            const int64_t c = c0 - r;
-            if (c < 0)
-                break;
-            a.kc[(base + c) * 64 + lane] = make_float2(kk.r, kk.i);
-            const int src = sg[r];
-            const float4 m = mv[r];
-            // the record kCarryRing chunks further left, into this slot
-            const int64_t cn = max(c - kCarryRing, (int64_t)0);
-            sg[r] = a.sig[(base + cn) * 64 + lane];
-            mv[r] = a.mv[(base + cn) * 64 + lane];
-            cf kg;
-            kg.r = bperm(kk.r, src);
-            kg.i = CPLX ? bperm(kk.i, src) : 0.f;
-            kk = {m.x * kg.r - m.y * kg.i + m.z, CPLX ? m.x * kg.i + m.y * kg.r + m.w : 0.f};
-        }
+    for (int64_t g = ng - 1; g >= 0; --g) {
+        a.gk[(seq * ng + g) * 64 + lane] = make_float2(kk.r, kk.i);
+        kk = apply_op<CPLX>(load_op<CPLX>(a, a.gsig, a.gmv, seq * ng + g, lane), kk);
     }
     if (a.gx0 && act)
         store_grad<CPLX>(a.gx0, seq * a.N + lane, kk);
 }
 
+// One wave per group: the carry into every chunk of the group.
+template <bool CPLX>
+__global__ void __launch_bounds__(kBW * 64) bwd_expand_kernel(BwdArgs a)
+{
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int64_t ng = (a.nch + kGroup - 1) / kGroup;
+    const int64_t gi = (int64_t)blockIdx.x * kBW + wave;
+    if (gi >= a.S * ng)
+        return;
+    const int64_t seq = gi / ng, g = gi - seq * ng;
+    const int64_t c0 = g * kGroup, c1 = min(c0 + kGroup, a.nch) - 1;
+    const float2 k0 = a.gk[gi * 64 + lane];
+    cf kk = {k0.x, k0.y};
+    GOp ring[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        ring[r] = load_op<CPLX>(a, a.sig, a.mv, seq * a.nch + max(c1 - r, c0), lane);
+    for (int64_t i0 = 0; i0 <= c1 - c0; i0 += 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t c = c1 - (i0 + r);
+            if (c >= c0) {
+                a.kc[(seq * a.nch + c) * 64 + lane] = make_float2(kk.r, kk.i);
+                const GOp op = ring[r];
+                ring[r] = load_op<CPLX>(a, a.sig, a.mv, seq * a.nch + max(c - 4, c0), lane);
+                kk = apply_op<CPLX>(op, kk);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // bwd_grad: per chunk (one wave, lane = state).  The states x_t of the chunk
 // by the forward's collision-free scatter from the saved carry-in (kept in
-// registers), then lambda backwards from K_c by gathers.
+// registers), then lambda backwards from K_c by gathers, writing gb, gc and
+// gd.  Inputs stream through rings of D steps; the loads of both passes are
+// issued before any store of the chunk waits on them.
 // ---------------------------------------------------------------------------
 template <bool CPLX, bool BCBF>
 __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
@@ -221,51 +449,65 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
     const int64_t t0 = (ch - seq * a.nch) * kBT;
     const int nv = (int)min((int64_t)kBT, a.L - t0);
     const int64_t h = seq % a.H;
-    const int N = a.N, K = a.K;
-    const bool act = lane < N;
+    const int N = a.N;
 #pragma unroll
     for (int r = kRegions; r < 2 * kRegions; ++r)
         s_reg[wave][r][lane] = cf{0.f, 0.f};
-    wave_select<kBT>(a.sel, a.sel_mode, K, a.L, seq * a.L, t0, s_sel[wave], lane);
+    wave_select<kBT>(a.sel, a.sel_mode, a.K, a.L, seq * a.L, t0, s_sel[wave], lane);
     char *const regp = reinterpret_cast<char *>(&s_reg[wave][0][0]);
     const char *const rowbase = regp + lane * (int)sizeof(cf);
-    const uint16_t *const tab_h = a.tab + h * (int64_t)K * 64 + lane;
 
-    // The inputs of step tt of the chunk (clamped to its last step, so every
-    // load is in range), two steps ahead of their use.
-    struct In {
-        cf d, bb, cv;
-        float g;
-        uint32_t ent;
-    };
-    auto load_in = [&](int tt, bool with_b) -> In {
-        const int ts = max(0, min(tt, nv - 1));
-        const int64_t step = seq * a.L + t0 + ts;
-        const int64_t e = step * N + (act ? lane : N - 1);
-        In r;
-        r.ent = tab_h[(int)s_sel[wave][ts] * 64];
-        r.d = load_diag<CPLX>(a.diag, e);
-        r.bb = with_b ? load_vec<CPLX, BCBF>(a.b, e) : cf{0.f, 0.f};
-        r.cv = load_vec<CPLX, BCBF>(a.c, e);
-        r.g = load_gy(a, step);
-        return r;
-    };
+    using IO = ChunkIO<CPLX, BCBF>;
+    using Raw = typename RawOf<CPLX, BCBF>::type;
+    using DRaw = typename IO::DRaw;
+    using Stored = typename IO::Stored;
+    IO io;
+    io.init(a, seq, t0, nv, h, lane);
+    const float gyv = chunk_gy(a, seq * a.L + t0, nv, lane);
+    auto gy_at = [&](int tt) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gyv), tt)); };
+    auto sel_at = [&](int ts) { return __builtin_amdgcn_readfirstlane((int)s_sel[wave][ts]); };
+    const int64_t e0 = (seq * a.L + t0) * N;
+    const uint64_t rows = (uint64_t)nv * (uint64_t)N;
+    const __amdgpu_buffer_rsrc_t ogb = make_rsrc(reinterpret_cast<Stored *>(a.gb) + e0, rows * sizeof(Stored));
+    const __amdgpu_buffer_rsrc_t ogc = make_rsrc(reinterpret_cast<Stored *>(a.gc) + e0, rows * sizeof(Stored));
+    const __amdgpu_buffer_rsrc_t ogd = make_rsrc(reinterpret_cast<DRaw *>(a.gd) + e0, rows * sizeof(DRaw));
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(reinterpret_cast<const DRaw *>(a.xch) + ch * N, (uint64_t)N * sizeof(DRaw));
+
+    constexpr int D = 4;
+    cf rd[D];
+    Raw rv[D];   // b in the forward pass, c in the backward pass
+    uint32_t re[D];
 
     // ---- x over the chunk: x_t = P_t (d_t * x_{t-1}) + b_t
-    cf xin = {0.f, 0.f};
-    if (act)
-        xin = load_diag<CPLX>(a.xch, ch * N + lane);
+    auto fetch_f = [&](int tt) {
+        const int ts = min(tt, nv - 1);
+        rd[tt % D] = io.d(ts);
+        rv[tt % D] = io.raw_b(ts);
+        re[tt % D] = io.ent(sel_at(ts));
+    };
+#pragma unroll
+    for (int tt = 0; tt < D; ++tt)
+        fetch_f(tt);
+    cf xin;
+    {
+        const DRaw v = bload<DRaw>(rx, io.vd, 0);
+        if constexpr (CPLX)
+            xin = {v.x, v.y};
+        else
+            xin = {v, 0.f};
+    }
     cf xs[kBT];
     cf x = xin;
-    In ring[2] = {load_in(0, true), load_in(1, true)};
 #pragma unroll
     for (int tt = 0; tt < kBT; ++tt) {
+        const cf d = rd[tt % D];
+        const cf bb = unpack_c<CPLX, BCBF>(rv[tt % D]);
+        const uint32_t ent = re[tt % D];
+        if (tt + D < kBT)
+            fetch_f(tt + D);
         if (tt < nv) {
-            const In in = ring[tt & 1];
-            ring[tt & 1] = load_in(tt + 2, true);
-            const int64_t step = seq * a.L + t0 + tt;
-            const cf v = cmul(in.d, x);
-            const uint32_t slot = (in.ent & 0x1FFu) << 3;
+            const cf v = cmul(d, x);
+            const uint32_t slot = (ent & 0x1FFu) << 3;
             *static_cast<float2 *>(__builtin_assume_aligned(regp + slot, 8)) = make_float2(v.r, v.i);
             lds_order();
             if (__any(slot >= kSpareOff)) {
@@ -277,8 +519,8 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
                 }
                 lds_order();
             }
-            const char *rowp = rowbase + (in.ent & 0x600u);
-            cf sum = in.bb;
+            const char *rowp = rowbase + (ent & 0x600u);
+            cf sum = bb;
 #pragma unroll
             for (int r = 0; r < kRegions; ++r) {
                 const float2 u = *static_cast<const float2 *>(__builtin_assume_aligned(rowp + r * kRegionBytes, 8));
@@ -287,35 +529,45 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
             }
             lds_order();
             x = sum;
-            xs[tt] = x;
-            if (act)
-                store_vec<CPLX, BCBF>(a.gc, step * N + lane, cf{in.g * x.r, -in.g * x.i});
         }
+        xs[tt] = x;
     }
 
-    // ---- lambda back over the chunk
+    // ---- lambda back over the chunk, from the carried part K_c
+    auto fetch_b = [&](int u) {   // u-th step from the end: step 15 - u, clamped into the chunk
+        const int ts = min(kBT - 1 - u, nv - 1);
+        rd[u % D] = io.d(max(ts, 0));
+        rv[u % D] = io.raw_c(max(ts, 0));
+        re[u % D] = io.ent(sel_at(max(ts, 0)));
+    };
+#pragma unroll
+    for (int u = 0; u < D; ++u)
+        fetch_b(u);
     const float2 k0 = a.kc[ch * 64 + lane];
     cf lc = {k0.x, k0.y};   // A_{t+1}^H lambda_{t+1}, the part carried into step t
-    ring[0] = load_in(nv - 1, false);
-    ring[1] = load_in(nv - 2, false);
 #pragma unroll
-    for (int tt = kBT - 1; tt >= 0; --tt) {
+    for (int u = 0; u < kBT; ++u) {
+        const int tt = kBT - 1 - u;
+        const cf d = rd[u % D];
+        const cf cv = unpack_c<CPLX, BCBF>(rv[u % D]);
+        const uint32_t ent = re[u % D];
+        if (u + D < kBT)
+            fetch_b(u + D);
         if (tt < nv) {
-            const int q = (nv - 1 - tt) & 1;   // ring slot of step tt
-            const In in = ring[q];
-            ring[q] = load_in(tt - 2, false);
-            const int64_t step = seq * a.L + t0 + tt;
-            const cf lam = {lc.r + in.g * in.cv.r, lc.i - in.g * in.cv.i};
-            const int pi = (int)(in.ent & 63u);
+            const float g = gy_at(tt);
+            const cf lam = {lc.r + g * cv.r, lc.i - g * cv.i};
+            const int pi4 = (int)((ent & 63u) << 2);
             cf lg;
-            lg.r = bperm(lam.r, pi);
-            lg.i = CPLX ? bperm(lam.i, pi) : 0.f;
+            lg.r = bperm_a(lam.r, pi4);
+            lg.i = CPLX ? bperm_a(lam.i, pi4) : 0.f;
+            const cf xt = xs[tt];
             const cf xp = (tt > 0) ? xs[tt > 0 ? tt - 1 : 0] : xin;
-            if (act) {
-                store_vec<CPLX, BCBF>(a.gb, step * N + lane, lam);
-                store_grad<CPLX>(a.gd, step * N + lane, cf{xp.r * lg.r + xp.i * lg.i, xp.r * lg.i - xp.i * lg.r});
-            }
-            lc = {in.d.r * lg.r + in.d.i * lg.i, in.d.r * lg.i - in.d.i * lg.r};
+            const uint32_t rs = (uint32_t)(tt * N * (int)sizeof(Stored));
+            bstore<Stored>(ogb, pack_vec<CPLX, BCBF>(lam), io.vs, rs);
+            bstore<Stored>(ogc, pack_vec<CPLX, BCBF>(cf{g * xt.r, -g * xt.i}), io.vs, rs);
+            bstore<DRaw>(ogd, pack_d<CPLX>(cf{xp.r * lg.r + xp.i * lg.i, xp.r * lg.i - xp.i * lg.r}), io.vd,
+                         (uint32_t)(tt * N * (int)sizeof(DRaw)));
+            lc = {d.r * lg.r + d.i * lg.i, d.r * lg.i - d.i * lg.r};
         }
     }
 }
@@ -324,7 +576,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
 // Host side.
 // ---------------------------------------------------------------------------
 struct BwdLayout {
-    int64_t nch, S, tab_bytes, sig_bytes, mv_bytes, kc_bytes, total;
+    int64_t nch, S, tab_bytes, sig_bytes, mv_bytes, kc_bytes, grp_bytes, total;
 };
 
 static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t L, int32_t K)
@@ -338,7 +590,9 @@ static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t L, int32_t K)
     lo.sig_bytes = up(chunks * 64 * 4);
     lo.mv_bytes = up(chunks * 64 * 16);
     lo.kc_bytes = up(chunks * 64 * 8);
-    lo.total = lo.tab_bytes + lo.sig_bytes + lo.mv_bytes + lo.kc_bytes;
+    const int64_t groups = lo.S * ((lo.nch + kGroup - 1) / kGroup);
+    lo.grp_bytes = up(groups * 64 * 4) + up(groups * 64 * 16) + up(groups * 64 * 8);
+    lo.total = lo.tab_bytes + lo.sig_bytes + lo.mv_bytes + lo.kc_bytes + lo.grp_bytes;
     return lo;
 }
 
@@ -348,7 +602,10 @@ static void launch_bwd(const BwdArgs &a, hipStream_t st)
     const int64_t chunks = a.S * a.nch;
     const dim3 blk(kBW * 64);
     hipLaunchKernelGGL((bwd_ops_kernel<CPLX, BCBF>), dim3((unsigned)((chunks + kBW - 1) / kBW)), blk, 0, st, a);
-    hipLaunchKernelGGL((bwd_carry_kernel<CPLX>), dim3((unsigned)((a.S + kBW - 1) / kBW)), blk, 0, st, a);
+    const int64_t groups = a.S * ((a.nch + kGroup - 1) / kGroup);
+    hipLaunchKernelGGL((bwd_group_kernel<CPLX>), dim3((unsigned)((groups + kBW - 1) / kBW)), blk, 0, st, a);
+    hipLaunchKernelGGL((bwd_chain_kernel<CPLX>), dim3((unsigned)((a.S + kBW - 1) / kBW)), blk, 0, st, a);
+    hipLaunchKernelGGL((bwd_expand_kernel<CPLX>), dim3((unsigned)((groups + kBW - 1) / kBW)), blk, 0, st, a);
     hipLaunchKernelGGL((bwd_grad_kernel<CPLX, BCBF>), dim3((unsigned)((chunks + kBW - 1) / kBW)), blk, 0, st, a);
 }
 
@@ -405,6 +662,14 @@ extern "C" int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx
     a.sig = reinterpret_cast<int32_t *>(w + lo.tab_bytes);
     a.mv = reinterpret_cast<float4 *>(w + lo.tab_bytes + lo.sig_bytes);
     a.kc = reinterpret_cast<float2 *>(w + lo.tab_bytes + lo.sig_bytes + lo.mv_bytes);
+    {
+        char *gw = w + lo.tab_bytes + lo.sig_bytes + lo.mv_bytes + lo.kc_bytes;
+        const int64_t groups = lo.S * ((lo.nch + kGroup - 1) / kGroup);
+        auto up = [](int64_t n) { return (n + 255) / 256 * 256; };
+        a.gsig = reinterpret_cast<int32_t *>(gw);
+        a.gmv = reinterpret_cast<float4 *>(gw + up(groups * 64 * 4));
+        a.gk = reinterpret_cast<float2 *>(gw + up(groups * 64 * 4) + up(groups * 64 * 16));
+    }
     a.H = H;
     a.L = L;
     a.S = lo.S;
