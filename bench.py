@@ -65,6 +65,47 @@ def counter_traffic(bytes_per_call: int):
         return None
 
 
+def measure_backward(pk, gen, inp, ws, stream, args):
+    """Time pdssm_scan_bwd (and the forward that saves chunk carries) on the
+    same inputs, HIP events on the launch stream; returns the summary object
+    reported beside the forward's."""
+    import torch
+    gy, gxf = gen.make_grads(inp, seed=1)
+    bws = pk.bwd_workspace_for(inp)
+    _, _, xch, sel = pk.scan_save(inp, workspace=ws, stream=stream, want_sel=True)
+    out = pk.scan_bwd(inp, xch, gy, gxf, workspace=bws, stream=stream, sel=sel)
+    steps = max(10, args.steps // 4)
+
+    def timed(fn):
+        for _ in range(max(3, args.warmup // 4)):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e-3
+
+    t_bwd = timed(lambda: pk.scan_bwd(inp, xch, gy, gxf, workspace=bws, stream=stream, out=out,
+                                      sel=sel))
+    t_save = timed(lambda: pk.scan_save(inp, workspace=ws, stream=stream, want_sel=True))
+    ins = (sel, inp.dict_idx, inp.diag, inp.b, inp.c, inp.x0, xch, gy, gxf)
+    alg = sum(t.numel() * t.element_size() for t in ins + tuple(out) if t is not None)
+    tokens = inp.B * inp.H * inp.L
+    print(f"[bench] backward: {t_bwd * 1e6:.1f} us/call, {alg / t_bwd / 1e9:.0f} GB/s algorithmic; "
+          f"forward with saved carries {t_save * 1e6:.1f} us", file=sys.stderr, flush=True)
+    return {"us_per_call": t_bwd * 1e6, "tokens_per_s": tokens / t_bwd,
+            "algorithmic_bytes_per_call": alg, "achieved_GBps": alg / t_bwd / 1e9,
+            "frac": alg / t_bwd / 1e9 / HBM_PEAK_GBS, "steps": steps,
+            "fwd_save_us_per_call": t_save * 1e6,
+            "note": "pdssm_scan_bwd: gradients of b, c, diag, x0 from dy and dx_final, fed "
+                    "with the forward's saved chunk carries and int16 selections; algorithmic "
+                    "bytes = every input read once and every gradient written once"}
+
+
 def cpu_threads() -> int:
     try:
         n = len(os.sched_getaffinity(0))
@@ -83,6 +124,8 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy (known bytes) so that "
                          "rocprofv3 byte counters can be scaled")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the timing of the backward scan (reported beside the forward)")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle over the batch for at least this long")
@@ -146,6 +189,8 @@ def main() -> int:
         print(f"[bench] copy calibration: 3 x {src.numel()} bytes copied", file=sys.stderr, flush=True)
         del src, dst
 
+    bwd = None if args.no_backward else measure_backward(pk, gen, inp, ws, stream, args)
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -196,6 +241,7 @@ def main() -> int:
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_call": alg_bytes},
         "cpu_baseline": cpu,
+        "backward": bwd,
     }
     print(json.dumps(out))
     return 0

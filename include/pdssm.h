@@ -113,16 +113,20 @@ size_t pdssm_scan_workspace_bytes(int64_t B, int64_t H, int64_t L, int32_t N, in
 
 /*
  * pdssm_scan_fwd that also keeps what pdssm_scan_bwd needs: the state just
- * before every chunk of 16 steps.
+ * before every chunk of 16 steps, and optionally every step's selection.
  *   x_chunks  fp32 [B,H,ceil(L/16),N], or [B,H,ceil(L/16),N,2] with
  *             PDSSM_COMPLEX:  x_chunks[b,h,c] = x_{16c-1}  (x0, or zero, for
  *             c = 0); caller-owned, 16-byte aligned, not NULL
+ *   sel_out   int16 [B,H,L]: the dictionary entry each step selected (the
+ *             argmax of its scores in the logits modes), or NULL.  Passed to
+ *             pdssm_scan_bwd with PDSSM_SEL_I16 in place of the scores, it
+ *             spares the backward the K scores per step.
  * Every other argument, the workspace size and the errors as pdssm_scan_fwd.
  */
 int pdssm_scan_fwd_save(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
                         const void *b, const void *c, void *y, void *x_final, void *x_chunks,
-                        int64_t B, int64_t H, int64_t L, int32_t N, int32_t K, uint32_t flags,
-                        const void *x0, void *workspace, size_t workspace_bytes,
+                        int16_t *sel_out, int64_t B, int64_t H, int64_t L, int32_t N, int32_t K,
+                        uint32_t flags, const void *x0, void *workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
 /*
@@ -140,8 +144,10 @@ int pdssm_scan_fwd_save(const void *sel_or_logits, const int32_t *dict_idx, cons
  *     gc[t] = gy_t conj(x_t)
  *     gd[t][j] = conj(x_{t-1}[j]) lambda_t[pi_t[j]]
  *     gx0 = A_0^H lambda_0
- * Inputs: the forward's sel_or_logits, dict_idx, diag, b, c and flags;
- *   x_chunks from pdssm_scan_fwd_save on the same inputs (and x0);
+ * Inputs: the forward's sel_or_logits, dict_idx, diag, b, c and flags (or
+ *   the forward's saved int16 selections with the selection bits of flags
+ *   set to PDSSM_SEL_I16); x_chunks from pdssm_scan_fwd_save on the same
+ *   inputs (and x0);
  *   gy [B,H,L] in the storage of y (bf16 with PDSSM_Y_BF16, else fp32);
  *   gx_final fp32 [B,H,N(,2)], or NULL for zero.
  * Outputs (caller-owned, 16-byte aligned): gb and gc in the storage of b and

@@ -72,8 +72,8 @@ def library() -> ctypes.CDLL:
         lib.pdssm_select.restype = ctypes.c_int
         lib.pdssm_compose.argtypes = [P, P, P, P, P, I64, I64, I64, I32, I32, U32, P, SZ, P]
         lib.pdssm_compose.restype = ctypes.c_int
-        lib.pdssm_scan_fwd_save.argtypes = [P, P, P, P, P, P, P, P, I64, I64, I64, I32, I32, U32, P, P,
-                                            SZ, P]
+        lib.pdssm_scan_fwd_save.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I32, I32, U32, P,
+                                            P, SZ, P]
         lib.pdssm_scan_fwd_save.restype = ctypes.c_int
         lib.pdssm_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I32, I32, U32,
                                        P, SZ, P]
@@ -125,12 +125,12 @@ def pdssm_scan_workspace_bytes(B, H, L, N, K, flags) -> int:
     return library().pdssm_scan_workspace_bytes(B, H, L, N, K, flags)
 
 
-def pdssm_scan_fwd_save(sel_or_logits, dict_idx, diag, b, c, y, x_final, x_chunks, B, H, L, N, K,
-                        flags, x0, workspace, workspace_bytes, stream=None) -> int:
+def pdssm_scan_fwd_save(sel_or_logits, dict_idx, diag, b, c, y, x_final, x_chunks, sel_out, B, H,
+                        L, N, K, flags, x0, workspace, workspace_bytes, stream=None) -> int:
     return library().pdssm_scan_fwd_save(_ptr(sel_or_logits), _ptr(dict_idx), _ptr(diag), _ptr(b),
-                                         _ptr(c), _ptr(y), _ptr(x_final), _ptr(x_chunks), B, H, L, N,
-                                         K, flags, _ptr(x0), _ptr(workspace), workspace_bytes,
-                                         _stream(stream))
+                                         _ptr(c), _ptr(y), _ptr(x_final), _ptr(x_chunks),
+                                         _ptr(sel_out), B, H, L, N, K, flags, _ptr(x0),
+                                         _ptr(workspace), workspace_bytes, _stream(stream))
 
 
 def pdssm_scan_bwd(sel_or_logits, dict_idx, diag, b, c, x_chunks, gy, gx_final, gb, gc, gd, gx0, B,
@@ -213,8 +213,9 @@ def scan(inp, *, workspace: Optional[torch.Tensor] = None, want_x_final: bool = 
 CARRY_STRIDE = 16   # steps per saved chunk carry (include/pdssm.h)
 
 
-def scan_save(inp, *, workspace: Optional[torch.Tensor] = None, stream=None):
-    """pdssm_scan_fwd_save on a batch: (y, x_final, x_chunks)."""
+def scan_save(inp, *, workspace: Optional[torch.Tensor] = None, stream=None, want_sel: bool = False):
+    """pdssm_scan_fwd_save on a batch: (y, x_final, x_chunks), plus the int16
+    selections [B,H,L] when want_sel."""
     dev = inp.diag.device
     y = torch.empty((inp.B, inp.H, inp.L), device=dev,
                     dtype=torch.bfloat16 if inp.y_bf16 else torch.float32)
@@ -224,9 +225,12 @@ def scan_save(inp, *, workspace: Optional[torch.Tensor] = None, stream=None):
     x_chunks = torch.empty((inp.B, inp.H, nch) + tail, device=dev, dtype=torch.float32)
     if workspace is None:
         workspace = workspace_for(inp)
+    sel = torch.empty((inp.B, inp.H, inp.L), device=dev, dtype=torch.int16) if want_sel else None
     check(pdssm_scan_fwd_save(inp.sel_or_logits, inp.dict_idx, inp.diag, inp.b, inp.c, y, x_final,
-                              x_chunks, inp.B, inp.H, inp.L, inp.N, inp.K, flags_of(inp), inp.x0,
+                              x_chunks, sel, inp.B, inp.H, inp.L, inp.N, inp.K, flags_of(inp), inp.x0,
                               workspace, workspace.numel(), stream))
+    if want_sel:
+        return y, x_final, x_chunks, sel
     return y, x_final, x_chunks
 
 
@@ -238,19 +242,29 @@ def bwd_workspace_for(inp, device=None) -> torch.Tensor:
 
 
 def scan_bwd(inp, x_chunks, gy, gx_final=None, *, want_gx0: bool = True,
-             workspace: Optional[torch.Tensor] = None, stream=None):
+             workspace: Optional[torch.Tensor] = None, stream=None, out=None, sel=None):
     """pdssm_scan_bwd on a batch: (gb, gc, gd, gx0 or None), in the storage
-    of b, c, diag and x0."""
+    of b, c, diag and x0.  ``sel``: the forward's saved int16 selections
+    (scan_save(want_sel=True)), used in place of the inputs' scores.  ``out``
+    may hold a previous call's result tuple to write into instead of
+    allocating."""
     dev = inp.diag.device
-    gb = torch.empty_like(inp.b)
-    gc = torch.empty_like(inp.c)
-    gd = torch.empty_like(inp.diag)
-    tail = (inp.N, 2) if inp.complex else (inp.N,)
-    gx0 = torch.empty((inp.B, inp.H) + tail, device=dev, dtype=torch.float32) if want_gx0 else None
+    if out is not None:
+        gb, gc, gd, gx0 = out
+    else:
+        gb = torch.empty_like(inp.b)
+        gc = torch.empty_like(inp.c)
+        gd = torch.empty_like(inp.diag)
+        tail = (inp.N, 2) if inp.complex else (inp.N,)
+        gx0 = torch.empty((inp.B, inp.H) + tail, device=dev, dtype=torch.float32) if want_gx0 else None
     if workspace is None:
         workspace = bwd_workspace_for(inp)
-    check(pdssm_scan_bwd(inp.sel_or_logits, inp.dict_idx, inp.diag, inp.b, inp.c, x_chunks, gy,
-                         gx_final, gb, gc, gd, gx0, inp.B, inp.H, inp.L, inp.N, inp.K, flags_of(inp),
+    flags = flags_of(inp)
+    if sel is not None:
+        flags = (flags & ~PDSSM_SEL_MASK) | PDSSM_SEL_I16
+    check(pdssm_scan_bwd(inp.sel_or_logits if sel is None else sel, inp.dict_idx, inp.diag, inp.b,
+                         inp.c, x_chunks, gy, gx_final, gb, gc, gd, gx0, inp.B, inp.H, inp.L, inp.N,
+                         inp.K, flags,
                          workspace, workspace.numel(), stream))
     return gb, gc, gd, gx0
 

@@ -42,6 +42,9 @@ namespace pdssm {
 
 constexpr int kBT = kCarryStride;   // steps per chunk (the forward saves one carry per chunk)
 constexpr int kBW = 4;              // chunk waves per workgroup
+#ifndef PDSSM_BWD_GRAD_D
+#define PDSSM_BWD_GRAD_D 4   // steps of input in flight per wave (gradient kernel)
+#endif
 
 struct BwdArgs {
     const void *sel;
@@ -63,6 +66,7 @@ struct BwdArgs {
     int32_t *gsig;      // [S*ng][64] group operators (ng = ceil(nch / kGroup))
     float4 *gmv;
     float2 *gk;         // [S*ng][64] adjoint carried into each group's last chunk
+    int16_t *ksel;      // [S*L] selections picked by bwd_ops from logits (logits modes only)
     int64_t H, L, S, nch;
     int N, K;
     uint32_t sel_mode;
@@ -76,13 +80,6 @@ __device__ __forceinline__ void store_grad(float *p, int64_t e, cf v)
         reinterpret_cast<float2 *>(p)[e] = make_float2(v.r, v.i);
     else
         p[e] = v.r;
-}
-
-__device__ __forceinline__ float load_gy(const BwdArgs &a, int64_t step)
-{
-    if (a.y_bf16)
-        return bf16_lo(reinterpret_cast<const uint16_t *>(a.gy)[step]);
-    return reinterpret_cast<const float *>(a.gy)[step];
 }
 
 // ---------------------------------------------------------------------------
@@ -177,11 +174,43 @@ struct ChunkIO {
     __device__ uint32_t ent(int k) const { return bload<uint16_t>(rt, vt, (uint32_t)(k * 128)); }
 };
 
-// The chunk's 16 upstream gradients gy, one per lane (lanes 0..nv-1).
-__device__ __forceinline__ float chunk_gy(const BwdArgs &a, int64_t step0, int nv, int lane)
+// The chunk's 16 upstream gradients gy as stored (fp32 bits, or bf16 bits in
+// the low half), one per lane (lanes 0..nv-1).  They are converted where a
+// step uses them, so that the load stays in flight meanwhile.
+__device__ __forceinline__ uint32_t chunk_gy_raw(const BwdArgs &a, int64_t step0, int nv, int lane)
 {
     const int l = min(lane, nv - 1);
-    return load_gy(a, step0 + l);
+    if (a.y_bf16)
+        return reinterpret_cast<const uint16_t *>(a.gy)[step0 + l];
+    return reinterpret_cast<const uint32_t *>(a.gy)[step0 + l];
+}
+
+__device__ __forceinline__ float gy_step(const BwdArgs &a, uint32_t raw, int tt)
+{
+    const uint32_t r = (uint32_t)__builtin_amdgcn_readlane((int)raw, tt);
+    return __uint_as_float(a.y_bf16 ? r << 16 : r);
+}
+
+// Index-mode selections of a chunk in two halves: sel_raw issues the load
+// (lane l < nv reads step l of the chunk), sel_put stores the clamped index
+// for the step's entry lookups once the chunk's row loads are also in flight.
+__device__ __forceinline__ bool index_mode(uint32_t mode)
+{
+    return mode == PDSSM_SEL_I32 || mode == PDSSM_SEL_I16;
+}
+
+__device__ __forceinline__ int sel_raw(const void *src, uint32_t mode, int64_t row, int nv, int lane)
+{
+    if (lane >= nv)
+        return 0;
+    return mode == PDSSM_SEL_I32 ? reinterpret_cast<const int32_t *>(src)[row + lane]
+                                 : reinterpret_cast<const int16_t *>(src)[row + lane];
+}
+
+__device__ __forceinline__ void sel_put(int k, int K, int nv, int16_t *out, int lane)
+{
+    if (lane < kBT)
+        out[lane] = (int16_t)(lane < nv ? (int)min((unsigned)k, (unsigned)(K - 1)) : 0);
 }
 
 template <typename V>
@@ -245,36 +274,44 @@ __global__ void __launch_bounds__(kBW * 64) bwd_ops_kernel(BwdArgs a)
     const int64_t t0 = (ch - seq * a.nch) * kBT;
     const int nv = (int)min((int64_t)kBT, a.L - t0);
     const int64_t h = seq % a.H;
-    wave_select<kBT>(a.sel, a.sel_mode, a.K, a.L, seq * a.L, t0, s_sel[wave], lane);
+    // The chunk's d and c rows do not depend on the selection: all of them
+    // are in flight before the selections are used.
+    const bool idx = index_mode(a.sel_mode);
+    int kraw = 0;
+    if (idx)
+        kraw = sel_raw(a.sel, a.sel_mode, seq * a.L + t0, nv, lane);
+    const uint32_t gyr = chunk_gy_raw(a, seq * a.L + t0, nv, lane);
     ChunkIO<CPLX, BCBF> io;
     io.init(a, seq, t0, nv, h, lane);
-    const float gyv = chunk_gy(a, seq * a.L + t0, nv, lane);
     using Raw = typename RawOf<CPLX, BCBF>::type;
-    constexpr int D = 4;
-    cf rd[D];
-    Raw rc[D];
-    uint32_t re[D];
-    auto fetch = [&](int tt) {
-        const int ts = min(tt, nv - 1);
-        const int k = __builtin_amdgcn_readfirstlane((int)s_sel[wave][ts]);
-        rd[tt % D] = io.d(ts);
-        rc[tt % D] = io.raw_c(ts);
-        re[tt % D] = io.ent(k);
-    };
+    cf rd[kBT];
+    Raw rc[kBT];
 #pragma unroll
-    for (int tt = 0; tt < D; ++tt)
-        fetch(tt);
+    for (int tt = 0; tt < kBT; ++tt) {
+        const int ts = min(tt, nv - 1);
+        rd[tt] = io.d(ts);
+        rc[tt] = io.raw_c(ts);
+    }
+    if (idx) {
+        sel_put(kraw, a.K, nv, s_sel[wave], lane);
+    } else {
+        wave_select<kBT>(a.sel, a.sel_mode, a.K, a.L, seq * a.L, t0, s_sel[wave], lane);
+        if (a.ksel && lane < nv)   // the gradient pass reads these instead of the K scores
+            a.ksel[seq * a.L + t0 + lane] = s_sel[wave][lane];
+    }
+    uint32_t re[kBT];
+#pragma unroll
+    for (int tt = 0; tt < kBT; ++tt)
+        re[tt] = io.ent(__builtin_amdgcn_readfirstlane((int)s_sel[wave][min(tt, nv - 1)]));
     int pacc4 = lane * 4;
     cf dacc = {1.f, 0.f}, v = {0.f, 0.f};
 #pragma unroll
     for (int tt = 0; tt < kBT; ++tt) {
-        const cf d = rd[tt % D];
-        const Raw craw = rc[tt % D];
-        const uint32_t ent = re[tt % D];
-        if (tt + D < kBT)
-            fetch(tt + D);
+        const cf d = rd[tt];
+        const Raw craw = rc[tt];
+        const uint32_t ent = re[tt];
         if (tt < nv) {
-            const float g = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gyv), tt));
+            const float g = gy_step(a, gyr, tt);
             // pacc_t = pi_t[pacc_{t-1}], dacc_t = d_t[pacc_{t-1}] * dacc_{t-1}
             const uint32_t np = bperm_a(ent & 63u, pacc4);
             cf dd;
@@ -453,7 +490,6 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
 #pragma unroll
     for (int r = kRegions; r < 2 * kRegions; ++r)
         s_reg[wave][r][lane] = cf{0.f, 0.f};
-    wave_select<kBT>(a.sel, a.sel_mode, a.K, a.L, seq * a.L, t0, s_sel[wave], lane);
     char *const regp = reinterpret_cast<char *>(&s_reg[wave][0][0]);
     const char *const rowbase = regp + lane * (int)sizeof(cf);
 
@@ -463,8 +499,13 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
     using Stored = typename IO::Stored;
     IO io;
     io.init(a, seq, t0, nv, h, lane);
-    const float gyv = chunk_gy(a, seq * a.L + t0, nv, lane);
-    auto gy_at = [&](int tt) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gyv), tt)); };
+    // selections: the forward's (index modes) or the ones the operator pass
+    // picked from the scores
+    const void *ssrc = a.ksel ? static_cast<const void *>(a.ksel) : a.sel;
+    const uint32_t smode = a.ksel ? PDSSM_SEL_I16 : a.sel_mode;
+    const int kraw = sel_raw(ssrc, smode, seq * a.L + t0, nv, lane);
+    const uint32_t gyr = chunk_gy_raw(a, seq * a.L + t0, nv, lane);
+    auto gy_at = [&](int tt) { return gy_step(a, gyr, tt); };
     auto sel_at = [&](int ts) { return __builtin_amdgcn_readfirstlane((int)s_sel[wave][ts]); };
     const int64_t e0 = (seq * a.L + t0) * N;
     const uint64_t rows = (uint64_t)nv * (uint64_t)N;
@@ -473,21 +514,29 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
     const __amdgpu_buffer_rsrc_t ogd = make_rsrc(reinterpret_cast<DRaw *>(a.gd) + e0, rows * sizeof(DRaw));
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(reinterpret_cast<const DRaw *>(a.xch) + ch * N, (uint64_t)N * sizeof(DRaw));
 
-    constexpr int D = 4;
+    constexpr int D = PDSSM_BWD_GRAD_D;
     cf rd[D];
     Raw rv[D];   // b in the forward pass, c in the backward pass
     uint32_t re[D];
 
-    // ---- x over the chunk: x_t = P_t (d_t * x_{t-1}) + b_t
-    auto fetch_f = [&](int tt) {
+    // ---- x over the chunk: x_t = P_t (d_t * x_{t-1}) + b_t.  The first
+    // rows of d and b are in flight before the selections are read.
+    auto fetch_db = [&](int tt) {
         const int ts = min(tt, nv - 1);
         rd[tt % D] = io.d(ts);
         rv[tt % D] = io.raw_b(ts);
-        re[tt % D] = io.ent(sel_at(ts));
+    };
+    auto fetch_f = [&](int tt) {
+        fetch_db(tt);
+        re[tt % D] = io.ent(sel_at(min(tt, nv - 1)));
     };
 #pragma unroll
     for (int tt = 0; tt < D; ++tt)
-        fetch_f(tt);
+        fetch_db(tt);
+    sel_put(kraw, a.K, nv, s_sel[wave], lane);
+#pragma unroll
+    for (int tt = 0; tt < D; ++tt)
+        re[tt % D] = io.ent(sel_at(min(tt, nv - 1)));
     cf xin;
     {
         const DRaw v = bload<DRaw>(rx, io.vd, 0);
@@ -496,7 +545,9 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
         else
             xin = {v, 0.f};
     }
-    cf xs[kBT];
+    cf xs[kBT];   // x_t, and d_t and pi_t (four 6-bit maps a word) for the reverse pass
+    cf ds[kBT];
+    uint32_t pis[kBT / 4] = {};
     cf x = xin;
 #pragma unroll
     for (int tt = 0; tt < kBT; ++tt) {
@@ -505,6 +556,8 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
         const uint32_t ent = re[tt % D];
         if (tt + D < kBT)
             fetch_f(tt + D);
+        ds[tt] = d;
+        pis[tt / 4] |= (ent & 63u) << (8 * (tt % 4));
         if (tt < nv) {
             const cf v = cmul(d, x);
             const uint32_t slot = (ent & 0x1FFu) << 3;
@@ -536,9 +589,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
     // ---- lambda back over the chunk, from the carried part K_c
     auto fetch_b = [&](int u) {   // u-th step from the end: step 15 - u, clamped into the chunk
         const int ts = min(kBT - 1 - u, nv - 1);
-        rd[u % D] = io.d(max(ts, 0));
         rv[u % D] = io.raw_c(max(ts, 0));
-        re[u % D] = io.ent(sel_at(max(ts, 0)));
     };
 #pragma unroll
     for (int u = 0; u < D; ++u)
@@ -548,9 +599,9 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
 #pragma unroll
     for (int u = 0; u < kBT; ++u) {
         const int tt = kBT - 1 - u;
-        const cf d = rd[u % D];
+        const cf d = ds[tt];
         const cf cv = unpack_c<CPLX, BCBF>(rv[u % D]);
-        const uint32_t ent = re[u % D];
+        const uint32_t ent = pis[tt / 4] >> (8 * (tt % 4));
         if (u + D < kBT)
             fetch_b(u + D);
         if (tt < nv) {
@@ -576,7 +627,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
 // Host side.
 // ---------------------------------------------------------------------------
 struct BwdLayout {
-    int64_t nch, S, tab_bytes, sig_bytes, mv_bytes, kc_bytes, grp_bytes, total;
+    int64_t nch, S, tab_bytes, sig_bytes, mv_bytes, kc_bytes, grp_bytes, ksel_bytes, total;
 };
 
 static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t L, int32_t K)
@@ -592,7 +643,8 @@ static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t L, int32_t K)
     lo.kc_bytes = up(chunks * 64 * 8);
     const int64_t groups = lo.S * ((lo.nch + kGroup - 1) / kGroup);
     lo.grp_bytes = up(groups * 64 * 4) + up(groups * 64 * 16) + up(groups * 64 * 8);
-    lo.total = lo.tab_bytes + lo.sig_bytes + lo.mv_bytes + lo.kc_bytes + lo.grp_bytes;
+    lo.ksel_bytes = up(lo.S * L * 2);
+    lo.total = lo.tab_bytes + lo.sig_bytes + lo.mv_bytes + lo.kc_bytes + lo.grp_bytes + lo.ksel_bytes;
     return lo;
 }
 
@@ -670,6 +722,8 @@ extern "C" int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx
         a.gmv = reinterpret_cast<float4 *>(gw + up(groups * 64 * 4));
         a.gk = reinterpret_cast<float2 *>(gw + up(groups * 64 * 4) + up(groups * 64 * 16));
     }
+    const bool logits = (flags & PDSSM_SEL_MASK) == PDSSM_LOGITS_F32 || (flags & PDSSM_SEL_MASK) == PDSSM_LOGITS_BF16;
+    a.ksel = logits ? reinterpret_cast<int16_t *>(w + lo.total - lo.ksel_bytes) : nullptr;
     a.H = H;
     a.L = L;
     a.S = lo.S;

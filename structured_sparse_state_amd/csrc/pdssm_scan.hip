@@ -53,8 +53,10 @@ struct ScanArgs {
     // w % H and takes its tiles from ctr[32 * h], total_head = n_tiles * B.
     uint32_t *ctr;
     uint32_t total_head;
-    // Optional: the state before each chunk of kScanT steps, [S][nch][N(,2)].
+    // Optional: the state before each chunk of kScanT steps, [S][nch][N(,2)],
+    // and every step's selected entry, [S][L].
     float *xsave;
+    int16_t *selsave;
     int64_t nch;
     int N, K;
     uint32_t sel_mode;
@@ -686,6 +688,11 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             }
         }
         lds_order();
+        if (a.selsave) {
+            for (int st = q.ln; st < G * T; st += 64)
+                if (tw0 + st < a.L)
+                    a.selsave[row0 + tw0 + st] = s_sel[wave][st];
+        }
     };
 
     // The zero blocks of this wave's scatter area (never written again).
@@ -1333,11 +1340,12 @@ extern "C" size_t pdssm_scan_workspace_bytes(int64_t B, int64_t H, int64_t L, in
 static int scan_fwd(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
                     const void *b, const void *c, void *y, void *x_final, int64_t B, int64_t H,
                     int64_t L, int32_t N, int32_t K, uint32_t flags, const void *x0,
-                    void *workspace, size_t workspace_bytes, void *x_chunks, hipStream_t stream)
+                    void *workspace, size_t workspace_bytes, void *x_chunks, int16_t *sel_save,
+                    hipStream_t stream)
 {
     if (!sel_or_logits || !dict_idx || !diag || !b || !c || !y || !workspace)
         return PDSSM_ERR_NULL;
-    if (x_chunks && !aligned16(x_chunks))
+    if ((x_chunks && !aligned16(x_chunks)) || (sel_save && !aligned16(sel_save)))
         return PDSSM_ERR_ALIGN;
     int rc = check_dims(B, H, L, N, K);
     if (rc != PDSSM_OK)
@@ -1362,6 +1370,7 @@ static int scan_fwd(const void *sel_or_logits, const int32_t *dict_idx, const vo
     a.xfinal = static_cast<float *>(x_final);
     a.x0 = static_cast<const float *>(x0);
     a.xsave = static_cast<float *>(x_chunks);
+    a.selsave = sel_save;
     a.nch = (L + kScanT - 1) / kScanT;
     a.hdr = static_cast<Header *>(workspace);
     uint32_t *ctr = reinterpret_cast<uint32_t *>(static_cast<char *>(workspace) + sizeof(Header));
@@ -1411,19 +1420,20 @@ extern "C" int pdssm_scan_fwd(const void *sel_or_logits, const int32_t *dict_idx
                               hipStream_t stream)
 {
     return scan_fwd(sel_or_logits, dict_idx, diag, b, c, y, x_final, B, H, L, N, K, flags, x0,
-                    workspace, workspace_bytes, nullptr, stream);
+                    workspace, workspace_bytes, nullptr, nullptr, stream);
 }
 
 extern "C" int pdssm_scan_fwd_save(const void *sel_or_logits, const int32_t *dict_idx,
                                    const void *diag, const void *b, const void *c, void *y,
-                                   void *x_final, void *x_chunks, int64_t B, int64_t H, int64_t L,
-                                   int32_t N, int32_t K, uint32_t flags, const void *x0,
-                                   void *workspace, size_t workspace_bytes, hipStream_t stream)
+                                   void *x_final, void *x_chunks, int16_t *sel_out, int64_t B,
+                                   int64_t H, int64_t L, int32_t N, int32_t K, uint32_t flags,
+                                   const void *x0, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream)
 {
     if (!x_chunks)
         return PDSSM_ERR_NULL;
     return scan_fwd(sel_or_logits, dict_idx, diag, b, c, y, x_final, B, H, L, N, K, flags, x0,
-                    workspace, workspace_bytes, x_chunks, stream);
+                    workspace, workspace_bytes, x_chunks, sel_out, stream);
 }
 
 extern "C" int pdssm_select(const void *sel_or_logits, int32_t *sel_out, int64_t B, int64_t H,

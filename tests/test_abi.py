@@ -118,10 +118,12 @@ def test_bwd_and_save_argument_errors(lib):
     assert _bwd(ws_bytes=need - 1) == pk.PDSSM_ERR_WORKSPACE
     assert pk.pdssm_scan_bwd_workspace_bytes(0, 1, 1, 1, 1, 0) == 0
     s = pk.pdssm_scan_fwd_save
-    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 2, 3, 100, 16, 8, 0, None, FAKE,
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 2, 3, 100, 16, 8, 0, None, FAKE,
              1 << 40, 0) == pk.PDSSM_ERR_NULL
-    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE + 8, 2, 3, 100, 16, 8, 0, None, FAKE,
-             1 << 40, 0) == pk.PDSSM_ERR_ALIGN
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE + 8, None, 2, 3, 100, 16, 8, 0, None,
+             FAKE, 1 << 40, 0) == pk.PDSSM_ERR_ALIGN
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE + 2, 2, 3, 100, 16, 8, 0, None,
+             FAKE, 1 << 40, 0) == pk.PDSSM_ERR_ALIGN
 
 
 def test_bwd_workspace_is_linear(lib):

@@ -1,7 +1,9 @@
 """GPU parity of the backward scan and of the forward's saved chunk carries.
 
-pdssm_scan_fwd_save must give the same y as pdssm_scan_fwd and the states
-x_{16c-1} of the fp64 oracle; pdssm_scan_bwd must give the oracle's gradients
+pdssm_scan_fwd_save must give the same y as pdssm_scan_fwd, the states
+x_{16c-1} of the fp64 oracle and (bit-exact) the oracle's selections;
+pdssm_scan_bwd must give the oracle's gradients, fed with either the scores or
+the saved selections,
 (gb, gc, gd, gx0) within the per-sequence relative tolerance (1e-4 with fp32
 I/O, 2e-2 with bf16 b/c/y).  The oracle's gradients are themselves pinned to
 torch autograd and finite differences (tests/oracle_pins.py).
@@ -50,9 +52,12 @@ def check_save(orc, inp, label):
     say(f"[case] save {label}: B={inp.B} H={inp.H} L={inp.L} N={inp.N} cplx={inp.complex}")
     g = inp.to(DEV)
     y1, _ = pk.scan(g)
-    y2, xf2, xch = pk.scan_save(g)
+    y2, xf2, xch, sel = pk.scan_save(g, want_sel=True)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2), f"{label}: y differs with the carries kept"
+    ref_sel = orc.select(inp.sel_or_logits, inp.sel_mode, inp.K)
+    assert np.array_equal(sel.cpu().numpy().astype(np.int64), ref_sel.astype(np.int64)), \
+        f"{label}: saved selections differ from the oracle's"
     nch = xch.shape[2]
     tol = tol_of(inp)
     for c in range(nch):
@@ -75,13 +80,14 @@ def check_save(orc, inp, label):
         assert e <= tol, f"{label}: chunk {c} carry error {e:.3e}"
 
 
-def check_bwd(orc, inp, label, with_gxf=True, seed=0):
+def check_bwd(orc, inp, label, with_gxf=True, seed=0, saved_sel=False):
     say(f"[case] bwd {label}: B={inp.B} H={inp.H} L={inp.L} N={inp.N} K={inp.K} mode={inp.sel_mode} "
-        f"cplx={inp.complex} bf16={inp.bc_bf16}/{inp.y_bf16} x0={inp.x0 is not None} gxf={with_gxf}")
+        f"cplx={inp.complex} bf16={inp.bc_bf16}/{inp.y_bf16} x0={inp.x0 is not None} gxf={with_gxf} "
+        f"saved_sel={saved_sel}")
     g = inp.to(DEV)
     gy, gxf = gen.make_grads(g, seed=seed, with_gx_final=with_gxf)
-    _, _, xch = pk.scan_save(g)
-    gb, gc, gd, gx0 = pk.scan_bwd(g, xch, gy, gxf)
+    _, _, xch, sel = pk.scan_save(g, want_sel=True)
+    gb, gc, gd, gx0 = pk.scan_bwd(g, xch, gy, gxf, sel=sel if saved_sel else None)
     torch.cuda.synchronize()
     gxf_ref = None if gxf is None else x_to_np(gxf, inp.complex)
     ref = orc.scan_bwd(inp.sel_or_logits, inp.sel_mode, inp.dict_idx, inp.diag, inp.b, inp.c,
@@ -124,16 +130,18 @@ BWD_SHAPES = [
 
 @pytest.mark.parametrize("N,L,K,mode,cplx,bcbf,ybf", BWD_SHAPES)
 def test_bwd_shapes(orc, N, L, K, mode, cplx, bcbf, ybf):
-    for with_x0, with_gxf in ((False, False), (True, True)):
+    for with_x0, with_gxf, saved in ((False, False, False), (True, True, False), (True, False, True)):
         inp = gen.make_inputs("tiny", B=2, H=2, L=L, N=N, K=K, sel_mode=mode, complex=cplx,
                               bc_bf16=bcbf, y_bf16=ybf, dmin=0.8, dmax=1.0, with_x0=with_x0,
                               seed=3000 + N * 7 + L)
-        check_bwd(orc, inp, f"shape N={N} L={L} K={K}", with_gxf=with_gxf, seed=N + L)
+        check_bwd(orc, inp, f"shape N={N} L={L} K={K}", with_gxf=with_gxf, seed=N + L,
+                  saved_sel=saved)
 
 
 @pytest.mark.parametrize("name,B,H,L", [("lm", 1, 3, 4096), ("long", 1, 2, 4000), ("small", 2, 2, 2048)])
 def test_bwd_workloads_scaled(orc, name, B, H, L):
-    check_bwd(orc, gen.make_inputs(name, B=B, H=H, L=L, with_x0=True), f"{name} scaled")
+    check_bwd(orc, gen.make_inputs(name, B=B, H=H, L=L, with_x0=True), f"{name} scaled",
+              saved_sel=(name == "lm"))
 
 
 def test_bwd_lm_full_size_sampled(orc):
@@ -141,9 +149,12 @@ def test_bwd_lm_full_size_sampled(orc):
     say("[case] bwd lm full size")
     g = gen.make_inputs("lm", device=DEV)
     gy, gxf = gen.make_grads(g, seed=5)
-    _, _, xch = pk.scan_save(g)
-    gb, gc, gd, gx0 = pk.scan_bwd(g, xch, gy, gxf)
+    _, _, xch, sel = pk.scan_save(g, want_sel=True)
+    gb, gc, gd, gx0 = pk.scan_bwd(g, xch, gy, gxf, sel=sel)
     torch.cuda.synchronize()
+    # the same call fed with the scores gives the same bits
+    for a, b in zip((gb, gc, gd, gx0), pk.scan_bwd(g, xch, gy, gxf)):
+        assert torch.equal(a, b)
     tol = tol_of(g)
     for (bi, hi) in ((0, 0), (3, 17), (g.B - 1, g.H - 1)):
         one = g.sequence(bi, hi).to("cpu")
