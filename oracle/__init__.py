@@ -56,6 +56,8 @@ class Oracle:
         lib.pdssm_oracle_scan_bwd.argtypes = [P, I, P, P, P, P, P, P, P, I, I, I64, I64, I64, I32, I32,
                                               P, P, P, P, I]
         lib.pdssm_oracle_scan_bwd.restype = I
+        lib.pdssm_oracle_dict_hardmax.argtypes = [P, I, I64, I32, I32, P]
+        lib.pdssm_oracle_dict_hardmax.restype = I
         self.lib = lib
         self.path = path
 
@@ -92,6 +94,20 @@ class Oracle:
         out = np.empty((B, H, L), dtype=np.int32)
         self._check(self.lib.pdssm_oracle_select(self._ptr(src), SEL_KIND[sel_mode], B, H, L, K,
                                                  self._ptr(out)))
+        return out
+
+    def dict_hardmax(self, m) -> np.ndarray:
+        """dict_idx int32 [H,K,N] from dense matrices m [H,K,N,N] (fp32, or a
+        bf16 torch tensor): the column-wise hardmax of every matrix."""
+        src = self._arr(m)
+        H, K, N, N2 = src.shape
+        assert N == N2
+        is_bf16 = src.dtype == np.uint16
+        if not is_bf16 and src.dtype != np.float32:
+            raise TypeError(f"expected fp32 or bf16, got {src.dtype}")
+        out = np.empty((H, K, N), dtype=np.int32)
+        self._check(self.lib.pdssm_oracle_dict_hardmax(self._ptr(src), int(is_bf16), H, K, N,
+                                                        self._ptr(out)))
         return out
 
     def scan(self, sel_or_logits, sel_mode: str, dict_idx, diag, b, c, *, complex: bool,

@@ -61,10 +61,24 @@ static double load_value(const void *base, int64_t i, int is_bf16)
 }
 
 /*
+ * The argmax rule of every hard selection: scanning candidates in order, a
+ * later value v replaces the best so far when it is strictly larger, so ties
+ * go to the lowest index (the first maximum) and -0 equals +0 under ordinary
+ * comparison; a NaN counts as larger than every number, and the first NaN
+ * wins.
+ */
+static int beats(double v, double best_v)
+{
+    if (isnan(best_v))
+        return 0;
+    if (isnan(v))
+        return 1;
+    return v > best_v;
+}
+
+/*
  * Hard selection for one step: index mode reads the stored index; logits
- * mode takes the argmax over the K scores.  Ties go to the lowest index
- * (the first maximum), -0 equals +0 under ordinary comparison, and a NaN
- * score counts as larger than every number (the first NaN wins).
+ * mode takes the argmax over the K scores.
  */
 static int64_t select_step(const void *src, int sel_kind, int64_t step, int32_t K)
 {
@@ -78,14 +92,7 @@ static int64_t select_step(const void *src, int sel_kind, int64_t step, int32_t 
     double best_v = load_value(src, row, is_bf16);
     for (int32_t k = 1; k < K; ++k) {
         double v = load_value(src, row + k, is_bf16);
-        int take;
-        if (isnan(best_v))
-            take = 0;
-        else if (isnan(v))
-            take = 1;
-        else
-            take = v > best_v;
-        if (take) {
+        if (beats(v, best_v)) {
             best = k;
             best_v = v;
         }
@@ -111,6 +118,39 @@ int pdssm_oracle_select(const void *src, int sel_kind, int64_t B, int64_t H, int
         if (k < 0 || k >= K)
             return ORC_BAD_SEL;
         sel_out[s] = (int32_t)k;
+    }
+    return ORC_OK;
+}
+
+/*
+ * Dictionary pre-compute.  Methodology, "1. Novel Selection Mechanism (Hard
+ * Selection)": the K structured matrices come from K dense N x N matrices by
+ * a column-wise hardmax, which leaves one non-zero per column, i.e. a one-hot
+ * column selector.  For every entry (h,k) and column j:
+ *     dict_out[h,k,j] = the row i with the largest m[h,k,i,j]
+ * under the same argmax rule as the selection (first maximum, NaN above all).
+ * m is [H,K,N,N] row-major (row i, column j), fp32 or bf16 (is_bf16);
+ * dict_out is int32 [H,K,N].
+ */
+int pdssm_oracle_dict_hardmax(const void *m, int is_bf16, int64_t H, int32_t K, int32_t N,
+                              int32_t *dict_out)
+{
+    if (!m || !dict_out || H < 1 || K < 1 || N < 1)
+        return ORC_BAD_ARG;
+    for (int64_t e = 0; e < H * K; ++e) {
+        const int64_t base = e * N * N;   /* matrix (h,k) */
+        for (int32_t col = 0; col < N; ++col) {
+            int32_t best = 0;
+            double best_v = load_value(m, base + col, is_bf16);
+            for (int32_t r = 1; r < N; ++r) {
+                double v = load_value(m, base + (int64_t)r * N + col, is_bf16);
+                if (beats(v, best_v)) {
+                    best = r;
+                    best_v = v;
+                }
+            }
+            dict_out[e * N + col] = best;
+        }
     }
     return ORC_OK;
 }

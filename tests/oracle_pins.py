@@ -11,8 +11,9 @@ if the oracle disagrees with an independent source of truth:
 * invariants (norm preservation under unit-modulus permutations,
   superposition in (b, x0), segment chaining);
 * hand-worked examples in ``tests/golden/hand_examples.json``;
-* ``numpy.argmax`` for the hard selection (Methodology, "1. Novel Selection
-  Mechanism (Hard Selection)").
+* ``numpy.argmax`` for the hard selection and for the column-wise hardmax
+  that turns dense matrices into the dictionary (Methodology, "1. Novel
+  Selection Mechanism (Hard Selection)").
 
 They are plain functions so ``test_oracle_mutants.py`` can run the same pins
 against builds of the oracle with planted mistakes and show each one fails.
@@ -463,6 +464,53 @@ def pin_bwd_finite_differences(orc):
                     assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (key, idx, part, fd, an)
 
 
+def hardmax_matrices(H, K, N, *, bf16: bool, seed: int, ties: bool = True, specials: bool = True):
+    """Dense [H,K,N,N] test matrices: few distinct values when ``ties`` (so
+    equal maxima in one column are common), plus -0/+0 and NaN entries when
+    ``specials``."""
+    g = torch.Generator().manual_seed(seed)
+    if ties:
+        m = torch.randint(-3, 4, (H, K, N, N), generator=g).to(torch.float32) * 0.5
+    else:
+        m = torch.randn((H, K, N, N), generator=g)
+    if specials:
+        flat = m.view(-1)
+        n = flat.numel()
+        idx = torch.randperm(n, generator=g)
+        flat[idx[: max(1, n // 50)]] = -0.0
+        flat[idx[max(1, n // 50): max(2, n // 50 + n // 200)]] = float("nan")
+    return m.to(torch.bfloat16) if bf16 else m
+
+
+def pin_dict_hardmax(orc):
+    """Column-wise hardmax: numpy.argmax down each column (first occurrence;
+    numpy also ranks NaN first-occurring above numbers and -0 equal to +0),
+    a round trip from dense P D matrices with positive d, and invariance under
+    adding a constant to each column."""
+    for (H, K, N, bf16, ties, specials) in ((2, 3, 8, False, True, True), (1, 5, 16, True, True, True),
+                                           (2, 2, 64, False, False, False), (1, 4, 33, True, True, False),
+                                           (1, 1, 1, False, True, True)):
+        m = hardmax_matrices(H, K, N, bf16=bf16, seed=900 + N, ties=ties, specials=specials)
+        got = orc.dict_hardmax(m)
+        ref = np.argmax(_to_f64(m), axis=-2)
+        assert np.array_equal(got, ref), (H, K, N, bf16)
+    # Round trip: the hardmax of P D (positive d, zeros elsewhere) is pi.
+    g = torch.Generator().manual_seed(901)
+    H, K, N = 2, 4, 12
+    pi = torch.randint(0, N, (H, K, N), generator=g)
+    dense = torch.zeros((H, K, N, N))
+    d = torch.rand((H, K, N), generator=g) + 0.25
+    for h in range(H):
+        for k in range(K):
+            for j in range(N):
+                dense[h, k, pi[h, k, j], j] = d[h, k, j]
+    assert np.array_equal(orc.dict_hardmax(dense), pi.numpy())
+    # A constant added to a column leaves its argmax; integers keep it exact.
+    m = torch.randint(-50, 50, (1, 3, 10, 10), generator=g).to(torch.float32)
+    shift = torch.randint(-20, 20, (1, 3, 1, 10), generator=g).to(torch.float32)
+    assert np.array_equal(orc.dict_hardmax(m), orc.dict_hardmax(m + shift))
+
+
 ALL_PINS = [pin_hand_examples, pin_select_argmax, pin_dense_products, pin_compose_dense, pin_fsa,
             pin_diagonal_closed_form, pin_permutation_invariants, pin_superposition,
-            pin_segment_chaining, pin_bwd_autograd, pin_bwd_finite_differences]
+            pin_segment_chaining, pin_bwd_autograd, pin_bwd_finite_differences, pin_dict_hardmax]

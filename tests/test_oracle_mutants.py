@@ -29,9 +29,15 @@ MUTANTS = {
     "drop_b": ("xn[2 * i] += load_value(b, (row + i) * ncomp, bc_bf16);",
                "xn[2 * i] += 0.0 * load_value(b, (row + i) * ncomp, bc_bf16);"),
     # Last maximum wins instead of the first.
-    "last_max_wins": ("take = v > best_v;", "take = v >= best_v;"),
+    "last_max_wins": ("return v > best_v;", "return v >= best_v;"),
     # NaN not treated as the maximum.
-    "nan_not_max": ("else if (isnan(v))\n            take = 1;", "else if (isnan(v))\n            take = 0;"),
+    "nan_not_max": ("if (isnan(v))\n        return 1;", "if (isnan(v))\n        return 0;"),
+    # Dictionary hardmax taken along rows instead of down each column.
+    "hardmax_row_wise": ("double v = load_value(m, base + (int64_t)r * N + col, is_bf16);",
+                         "double v = load_value(m, base + (int64_t)col * N + r, is_bf16);"),
+    # Dictionary hardmax whose first candidate is taken from the wrong row.
+    "hardmax_first_row": ("double best_v = load_value(m, base + col, is_bf16);",
+                          "double best_v = load_value(m, base + (int64_t)col * N, is_bf16);"),
     # Initial state ignored.
     "ignore_x0": ("if (x0) {\n            for", "if (0) {\n            for"),
     # Readout of the state before the update (y_t from x_{t-1}).
