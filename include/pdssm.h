@@ -168,6 +168,47 @@ size_t pdssm_scan_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int32_t N
                                       uint32_t flags);
 
 /*
+ * Dictionary pre-compute: the index maps from dense matrices.  Flash PD-SSM
+ * summary, Methodology, "1. Novel Selection Mechanism (Hard Selection)": a
+ * column-wise hardmax of each dense N x N dictionary matrix leaves a single
+ * non-zero per column, a one-hot column selector.  For every entry (h,k) and
+ * column j:
+ *     dict_idx[h,k,j] = argmax_i m[h,k,i,j]
+ * with the selection's rule (the first maximum wins, -0 equals +0, a NaN
+ * counts above every number and the first NaN wins).
+ *   m         dense matrices [H,K,N,N], row-major (row i, column j); fp32 with
+ *             flags = PDSSM_LOGITS_F32, bf16 with PDSSM_LOGITS_BF16 (no other
+ *             bits); device pointer, 16-byte aligned
+ *   dict_idx  int32 [H,K,N] output, device pointer, 16-byte aligned
+ * Errors: PDSSM_ERR_NULL, PDSSM_ERR_DIM (H < 1, N not in [1,64], K not in
+ * [1,32767]), PDSSM_ERR_FLAGS, PDSSM_ERR_ALIGN, PDSSM_ERR_HIP.  Asynchronous
+ * on stream; allocates nothing.
+ */
+int pdssm_dict_hardmax(const void *m, int32_t *dict_idx, int64_t H, int32_t K, int32_t N,
+                       uint32_t flags, hipStream_t stream);
+
+/*
+ * One recurrent decode step for every sequence (b,h): the scan with L = 1,
+ * the state carried by the caller between calls (the recurrent inference
+ * mode the Flash PD-SSM summary names for state-space models, Problem
+ * Statement).  With k the step's selection and pi = dict_idx[h,k,:]:
+ *     x[b,h] <- P (d * x[b,h]) + b,   y[b,h] = Re(sum_i c[i] x[b,h,i])
+ * (x on the right is the state before the call).
+ *   sel_or_logits  sel int32/int16 [B,H] or logits fp32/bf16 [B,H,K]
+ *   diag, b, c     [B,H,N] or [B,H,N,2] (complex), storages as in
+ *                  pdssm_scan_fwd
+ *   y              [B,H] output (bf16 with PDSSM_Y_BF16, else fp32)
+ *   x              fp32 [B,H,N(,2)] state, read and overwritten in place
+ *   flags          as pdssm_scan_fwd
+ * Arithmetic fp32; collisions of pi sum in any order.  All pointers are
+ * device pointers, 16-byte aligned, not NULL.  Errors as pdssm_scan_fwd
+ * (no workspace).  Asynchronous on stream; allocates nothing.
+ */
+int pdssm_decode_step(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
+                      const void *b, const void *c, void *y, void *x, int64_t B, int64_t H,
+                      int32_t N, int32_t K, uint32_t flags, hipStream_t stream);
+
+/*
  * The selection step alone: sel_out[b,h,t] = the dictionary entry step t
  * picks (Methodology, "1. Novel Selection Mechanism": argmax of the K
  * scores; index modes copy the index).  flags: selection bits only.

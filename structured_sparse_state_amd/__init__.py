@@ -82,6 +82,10 @@ def library() -> ctypes.CDLL:
         lib.pdssm_scan_bwd_workspace_bytes.restype = SZ
         lib.pdssm_strerror.argtypes = [ctypes.c_int]
         lib.pdssm_strerror.restype = ctypes.c_char_p
+        lib.pdssm_dict_hardmax.argtypes = [P, P, I64, I32, I32, U32, P]
+        lib.pdssm_dict_hardmax.restype = ctypes.c_int
+        lib.pdssm_decode_step.argtypes = [P, P, P, P, P, P, P, I64, I64, I32, I32, U32, P]
+        lib.pdssm_decode_step.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -155,6 +159,17 @@ def pdssm_compose(sel_or_logits, dict_idx, diag, pi_out, d_out, B, H, L, N, K, f
     return library().pdssm_compose(_ptr(sel_or_logits), _ptr(dict_idx), _ptr(diag), _ptr(pi_out),
                                    _ptr(d_out), B, H, L, N, K, flags, _ptr(workspace),
                                    workspace_bytes, _stream(stream))
+
+
+def pdssm_dict_hardmax(m, dict_idx, H, K, N, flags, stream=None) -> int:
+    return library().pdssm_dict_hardmax(_ptr(m), _ptr(dict_idx), H, K, N, flags, _stream(stream))
+
+
+def pdssm_decode_step(sel_or_logits, dict_idx, diag, b, c, y, x, B, H, N, K, flags,
+                      stream=None) -> int:
+    return library().pdssm_decode_step(_ptr(sel_or_logits), _ptr(dict_idx), _ptr(diag), _ptr(b),
+                                       _ptr(c), _ptr(y), _ptr(x), B, H, N, K, flags,
+                                       _stream(stream))
 
 
 def pdssm_strerror(status: int) -> str:
@@ -289,3 +304,31 @@ def compose(inp, workspace: Optional[torch.Tensor] = None, stream=None):
     check(pdssm_compose(inp.sel_or_logits, inp.dict_idx, inp.diag, pi, d, inp.B, inp.H, inp.L,
                         inp.N, inp.K, flags, workspace, workspace.numel(), stream))
     return pi, d
+
+
+def dict_hardmax(m: torch.Tensor, stream=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dict_idx int32 [H,K,N] from dense matrices m [H,K,N,N] (fp32 or bf16):
+    the column-wise hardmax of every matrix."""
+    H, K, N, N2 = m.shape
+    if N != N2:
+        raise ValueError("m must be [H,K,N,N]")
+    flags = PDSSM_LOGITS_BF16 if m.dtype == torch.bfloat16 else PDSSM_LOGITS_F32
+    if out is None:
+        out = torch.empty((H, K, N), dtype=torch.int32, device=m.device)
+    check(pdssm_dict_hardmax(m, out, H, K, N, flags, stream))
+    return out
+
+
+def decode_step(sel_or_logits, dict_idx, diag, b, c, x, *, sel_mode: str, complex: bool,
+                bc_bf16: bool, y_bf16: bool, y: Optional[torch.Tensor] = None, stream=None):
+    """One recurrent step for every (b, h): updates the state x [B,H,N(,2)]
+    in place and returns y [B,H]."""
+    B, H = diag.shape[:2]
+    K, N = dict_idx.shape[1], dict_idx.shape[2]
+    flags = SEL_FLAG[sel_mode] | (PDSSM_COMPLEX if complex else 0) | \
+        (PDSSM_BC_BF16 if bc_bf16 else 0) | (PDSSM_Y_BF16 if y_bf16 else 0)
+    if y is None:
+        y = torch.empty((B, H), device=diag.device,
+                        dtype=torch.bfloat16 if y_bf16 else torch.float32)
+    check(pdssm_decode_step(sel_or_logits, dict_idx, diag, b, c, y, x, B, H, N, K, flags, stream))
+    return y

@@ -273,6 +273,20 @@ def make_fsa_inputs(kind: str, *, B: int = 1, H: int = 1, L: int = 256, N: int =
                       B=B, H=H, L=L, N=N, K=K)
 
 
+def make_dense_dict(H: int, K: int, N: int, *, bf16: bool = False, seed: int = 21, device="cpu",
+                    ties: bool = False) -> torch.Tensor:
+    """Dense dictionary matrices [H,K,N,N] (row i, column j) whose column-wise
+    hardmax gives the index maps: N(0,1) draws, or, with ``ties``, a few
+    distinct values so that equal maxima in a column are common.  bf16 from
+    one RNE rounding of the fp32 draws."""
+    g = _gen(device, seed)
+    if ties:
+        m = torch.randint(-3, 4, (H, K, N, N), generator=g, device=device).to(torch.float32) * 0.5
+    else:
+        m = torch.randn((H, K, N, N), generator=g, device=device, dtype=torch.float32)
+    return m.to(torch.bfloat16) if bf16 else m
+
+
 def make_grads(inp: ScanInputs, *, seed: int = 0, with_gx_final: bool = True, device=None):
     """Seeded upstream gradients for the backward scan of ``inp``: gy in the
     storage of y ([B,H,L], N(0,1), bf16 rounded once when y is bf16) and

@@ -18,7 +18,8 @@ def test_exports_every_declared_function(lib):
     names = pk.header_functions()
     assert set(names) == {"pdssm_scan_fwd", "pdssm_scan_workspace_bytes", "pdssm_select",
                           "pdssm_compose", "pdssm_strerror", "pdssm_scan_fwd_save",
-                          "pdssm_scan_bwd", "pdssm_scan_bwd_workspace_bytes"}
+                          "pdssm_scan_bwd", "pdssm_scan_bwd_workspace_bytes", "pdssm_dict_hardmax",
+                          "pdssm_decode_step"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -132,3 +133,35 @@ def test_bwd_workspace_is_linear(lib):
     base = ws(8, 32, 4096)
     assert ws(8, 32, 8192) <= 2 * base
     assert ws(16, 32, 4096) <= 2 * base
+
+
+def test_dict_hardmax_argument_errors(lib):
+    h = pk.pdssm_dict_hardmax
+    f = pk.PDSSM_LOGITS_F32
+    assert h(None, FAKE, 2, 4, 8, f, 0) == pk.PDSSM_ERR_NULL
+    assert h(FAKE, None, 2, 4, 8, f, 0) == pk.PDSSM_ERR_NULL
+    for H, K, N in ((0, 4, 8), (2, 0, 8), (2, 4, 0), (2, 4, 65), (2, 32768, 8)):
+        assert h(FAKE, FAKE, H, K, N, f, 0) == pk.PDSSM_ERR_DIM, (H, K, N)
+    for bad in (pk.PDSSM_SEL_I32, pk.PDSSM_SEL_I16, f | pk.PDSSM_COMPLEX):
+        assert h(FAKE, FAKE, 2, 4, 8, bad, 0) == pk.PDSSM_ERR_FLAGS, bad
+    assert h(FAKE + 4, FAKE, 2, 4, 8, f, 0) == pk.PDSSM_ERR_ALIGN
+    assert h(FAKE, FAKE + 4, 2, 4, 8, pk.PDSSM_LOGITS_BF16, 0) == pk.PDSSM_ERR_ALIGN
+
+
+def _dec(**kw):
+    args = dict(sel=FAKE, dict_idx=FAKE, diag=FAKE, b=FAKE, c=FAKE, y=FAKE, x=FAKE, B=2, H=3, N=16,
+                K=8, flags=pk.PDSSM_LOGITS_BF16)
+    args.update(kw)
+    return pk.pdssm_decode_step(args["sel"], args["dict_idx"], args["diag"], args["b"], args["c"],
+                                args["y"], args["x"], args["B"], args["H"], args["N"], args["K"],
+                                args["flags"], 0)
+
+
+def test_decode_argument_errors(lib):
+    for name in ("sel", "dict_idx", "diag", "b", "c", "y", "x"):
+        assert _dec(**{name: None}) == pk.PDSSM_ERR_NULL, name
+    for bad in (dict(B=0), dict(H=0), dict(N=0), dict(N=65), dict(K=0), dict(K=40000)):
+        assert _dec(**bad) == pk.PDSSM_ERR_DIM, bad
+    assert _dec(flags=0x20) == pk.PDSSM_ERR_FLAGS
+    for name in ("sel", "dict_idx", "diag", "b", "c", "y", "x"):
+        assert _dec(**{name: FAKE + 4}) == pk.PDSSM_ERR_ALIGN, name
