@@ -106,6 +106,61 @@ def measure_backward(pk, gen, inp, ws, stream, args):
                     "bytes = every input read once and every gradient written once"}
 
 
+def _event_time(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps * 1e-3
+
+
+def measure_aux(pk, gen, inp, stream):
+    """The dictionary pre-compute and one decode step at the workload's
+    shape, HIP events on the launch stream."""
+    import torch
+    B, H, N, K = inp.B, inp.H, inp.N, inp.K
+    dev = inp.diag.device
+    m = gen.make_dense_dict(H, K, N, device=dev)
+    dct = pk.dict_hardmax(m, stream=stream)
+    t_hm = _event_time(lambda: pk.dict_hardmax(m, stream=stream, out=dct), 50, 5, stream)
+    hm_bytes = m.numel() * m.element_size() + dct.numel() * dct.element_size()
+
+    if inp.sel_mode.startswith("sel"):
+        sel = inp.sel_or_logits[:, :, 0].contiguous()
+    else:
+        sel = inp.sel_or_logits[:, :, 0, :].contiguous()
+    d, b, c = (t[:, :, 0].contiguous() for t in (inp.diag, inp.b, inp.c))
+    x = torch.zeros((B, H, N, 2) if inp.complex else (B, H, N), device=dev, dtype=torch.float32)
+    y = torch.empty((B, H), device=dev, dtype=torch.bfloat16 if inp.y_bf16 else torch.float32)
+
+    def dec():
+        pk.decode_step(sel, inp.dict_idx, d, b, c, x, sel_mode=inp.sel_mode, complex=inp.complex,
+                       bc_bf16=inp.bc_bf16, y_bf16=inp.y_bf16, y=y, stream=stream)
+
+    t_dec = _event_time(dec, 200, 20, stream)
+    dec_bytes = sum(t.numel() * t.element_size() for t in (sel, d, b, c, y)) + 2 * x.numel() * 4
+    print(f"[bench] dict hardmax {t_hm * 1e6:.1f} us ({hm_bytes / t_hm / 1e9:.0f} GB/s); decode step "
+          f"{t_dec * 1e6:.2f} us ({B * H / t_dec:.3g} tokens/s)", file=sys.stderr, flush=True)
+    return {
+        "dict_hardmax": {"us_per_call": t_hm * 1e6, "shape": f"H={H} K={K} N={N} fp32",
+                         "algorithmic_bytes_per_call": hm_bytes,
+                         "achieved_GBps": hm_bytes / t_hm / 1e9,
+                         "frac": hm_bytes / t_hm / 1e9 / HBM_PEAK_GBS},
+        "decode_step": {"us_per_call": t_dec * 1e6, "tokens_per_s": B * H / t_dec,
+                        "shape": f"B={B} H={H} N={N} K={K}, one step per sequence",
+                        "algorithmic_bytes_per_call": dec_bytes,
+                        "note": "launch- and latency-bound: one step reads and writes "
+                                f"{dec_bytes} bytes"},
+    }
+
+
 def cpu_threads() -> int:
     try:
         n = len(os.sched_getaffinity(0))
@@ -125,7 +180,8 @@ def main() -> int:
                     help="also run a plain 1 GiB device-to-device copy (known bytes) so that "
                          "rocprofv3 byte counters can be scaled")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip the timing of the backward scan (reported beside the forward)")
+                    help="skip the timings reported beside the forward (backward scan, dictionary "
+                         "pre-compute, decode step)")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle over the batch for at least this long")
@@ -190,6 +246,7 @@ def main() -> int:
         del src, dst
 
     bwd = None if args.no_backward else measure_backward(pk, gen, inp, ws, stream, args)
+    aux = None if args.no_backward else measure_aux(pk, gen, inp, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -242,6 +299,7 @@ def main() -> int:
                      "algorithmic_bytes_per_call": alg_bytes},
         "cpu_baseline": cpu,
         "backward": bwd,
+        "next_rows": aux,
     }
     print(json.dumps(out))
     return 0
