@@ -58,6 +58,8 @@ class Oracle:
         lib.pdssm_oracle_scan_bwd.restype = I
         lib.pdssm_oracle_dict_hardmax.argtypes = [P, I, I64, I32, I32, P]
         lib.pdssm_oracle_dict_hardmax.restype = I
+        lib.pdssm_oracle_router_select.argtypes = [P, P, I64, I64, I64, I32, I32, P, P, I]
+        lib.pdssm_oracle_router_select.restype = I
         self.lib = lib
         self.path = path
 
@@ -109,6 +111,22 @@ class Oracle:
         self._check(self.lib.pdssm_oracle_dict_hardmax(self._ptr(src), int(is_bf16), H, K, N,
                                                         self._ptr(out)))
         return out
+
+    def router_select(self, u, w, *, want_logits: bool = False, nthreads: int = 1):
+        """sel int32 [B,H,L] (and the float64 scores [B,H,L,K] when asked)
+        from bf16 inputs u [B,L,D] and router weights w [H,K,D]."""
+        uu = self._arr(u)
+        ww = self._arr(w)
+        if uu.dtype != np.uint16 or ww.dtype != np.uint16:
+            raise TypeError("u and w must be bf16")
+        B, L, D = uu.shape
+        H, K, D2 = ww.shape
+        assert D == D2
+        sel = np.empty((B, H, L), dtype=np.int32)
+        lg = np.empty((B, H, L, K), dtype=np.float64) if want_logits else None
+        self._check(self.lib.pdssm_oracle_router_select(self._ptr(uu), self._ptr(ww), B, L, H, K, D,
+                                                         self._ptr(sel), self._ptr(lg), int(nthreads)))
+        return (sel, lg) if want_logits else sel
 
     def scan(self, sel_or_logits, sel_mode: str, dict_idx, diag, b, c, *, complex: bool,
              bc_bf16: bool, x0=None, nthreads: int = 1):

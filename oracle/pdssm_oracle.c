@@ -156,6 +156,53 @@ int pdssm_oracle_dict_hardmax(const void *m, int is_bf16, int64_t H, int32_t K, 
 }
 
 /*
+ * Router selection.  Methodology, "1. Novel Selection Mechanism (Hard
+ * Selection)": at every step the input u_t produces the K scores by a linear
+ * transformation, and the largest score picks the dictionary entry.  With one
+ * K-wide block of weights per head (no bias):
+ *     logits[b,h,t,k] = sum_{d = 0..D-1 ascending} u[b,t,d] * w[h,k,d]
+ *     sel[b,h,t]      = argmax_k logits[b,h,t,k]   (the selection's rule)
+ * u is bf16 [B,L,D], w is bf16 [H,K,D]; products of bf16 values are exact in
+ * double and the sums are double.  sel_out is int32 [B,H,L]; logits_out, when
+ * not NULL, receives the double scores [B,H,L,K].  Rows (b,t) are
+ * independent; nthreads > 0 runs that many at once.
+ */
+int pdssm_oracle_router_select(const uint16_t *u, const uint16_t *w, int64_t B, int64_t L, int64_t H,
+                               int32_t K, int32_t D, int32_t *sel_out, double *logits_out,
+                               int nthreads)
+{
+    if (!u || !w || !sel_out || B < 1 || L < 1 || H < 1 || K < 1 || D < 1)
+        return ORC_BAD_ARG;
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 16) if (nthreads > 1)
+#endif
+    for (int64_t row = 0; row < B * L; ++row) {
+        const int64_t bi = row / L, t = row % L;
+        const uint16_t *ur = u + row * D;
+        for (int64_t h = 0; h < H; ++h) {
+            int32_t best = 0;
+            double best_v = 0.0;
+            for (int32_t k = 0; k < K; ++k) {
+                const uint16_t *wr = w + (h * K + k) * (int64_t)D;
+                double acc = 0.0;
+                for (int32_t d = 0; d < D; ++d)
+                    acc += bf16_value(ur[d]) * bf16_value(wr[d]);
+                if (logits_out)
+                    logits_out[((bi * H + h) * L + t) * K + k] = acc;
+                if (k == 0 || beats(acc, best_v)) {
+                    best = k;
+                    best_v = acc;
+                }
+            }
+            sel_out[(bi * H + h) * L + t] = best;
+        }
+    }
+    return ORC_OK;
+}
+
+/*
  * The forward scan.  For every sequence (b,h), starting from x0[b,h] (zero
  * when x0 is NULL), for t = 0..L-1:
  *     k   = selected entry of step t

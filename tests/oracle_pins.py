@@ -511,6 +511,28 @@ def pin_dict_hardmax(orc):
     assert np.array_equal(orc.dict_hardmax(m), orc.dict_hardmax(m + shift))
 
 
+def pin_router_select(orc):
+    """Router scores and their argmax: numpy fp64 matmul + numpy.argmax.
+    Small-integer inputs make every score an exact integer, so ties are
+    common and the first-maximum rule is checked too; the scores themselves
+    must match exactly.  Shapes keep K != D so that a transposed weight
+    index reads other weights."""
+    g = torch.Generator().manual_seed(950)
+    for (B, L, H, K, D) in ((1, 7, 1, 4, 12), (2, 33, 3, 16, 40), (1, 50, 2, 64, 96), (1, 5, 1, 1, 8)):
+        u = torch.randint(-3, 4, (B, L, D), generator=g).to(torch.bfloat16)
+        w = torch.randint(-2, 3, (H, K, D), generator=g).to(torch.bfloat16)
+        sel, lg = orc.router_select(u, w, want_logits=True)
+        ref = np.einsum("bld,hkd->bhlk", _to_f64(u), _to_f64(w))
+        assert np.array_equal(lg, ref), (B, L, H, K, D)
+        assert np.array_equal(sel, np.argmax(ref, axis=-1)), (B, L, H, K, D)
+    # Gaussian inputs: the same argmax as numpy's fp64 product.
+    u = torch.randn((2, 40, 64), generator=g).to(torch.bfloat16)
+    w = (torch.randn((4, 16, 64), generator=g) / 8).to(torch.bfloat16)
+    ref = np.argmax(np.einsum("bld,hkd->bhlk", _to_f64(u), _to_f64(w)), axis=-1)
+    assert np.array_equal(orc.router_select(u, w), ref)
+
+
 ALL_PINS = [pin_hand_examples, pin_select_argmax, pin_dense_products, pin_compose_dense, pin_fsa,
             pin_diagonal_closed_form, pin_permutation_invariants, pin_superposition,
-            pin_segment_chaining, pin_bwd_autograd, pin_bwd_finite_differences, pin_dict_hardmax]
+            pin_segment_chaining, pin_bwd_autograd, pin_bwd_finite_differences, pin_dict_hardmax,
+            pin_router_select]

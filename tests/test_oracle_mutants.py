@@ -32,6 +32,12 @@ MUTANTS = {
     "last_max_wins": ("return v > best_v;", "return v >= best_v;"),
     # NaN not treated as the maximum.
     "nan_not_max": ("if (isnan(v))\n        return 1;", "if (isnan(v))\n        return 0;"),
+    # Router weights read transposed ([H,D,K] instead of [H,K,D]).
+    "router_w_transposed": ("const uint16_t *wr = w + (h * K + k) * (int64_t)D;",
+                            "const uint16_t *wr = w + h * K * (int64_t)D + k;"),
+    # Router scores missing the last input feature.
+    "router_drop_last": ("for (int32_t d = 0; d < D; ++d)\n                    acc +=",
+                         "for (int32_t d = 0; d < D - 1; ++d)\n                    acc +="),
     # Dictionary hardmax taken along rows instead of down each column.
     "hardmax_row_wise": ("double v = load_value(m, base + (int64_t)r * N + col, is_bf16);",
                          "double v = load_value(m, base + (int64_t)col * N + r, is_bf16);"),
