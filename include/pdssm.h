@@ -209,6 +209,29 @@ int pdssm_decode_step(const void *sel_or_logits, const int32_t *dict_idx, const 
                       int32_t N, int32_t K, uint32_t flags, hipStream_t stream);
 
 /*
+ * Router selection fused with its matrix product: the scores never reach
+ * memory, only the selected entries do.  Flash PD-SSM summary, Methodology,
+ * "1. Novel Selection Mechanism (Hard Selection)": at every step the input
+ * u_t produces the K scores by a linear transformation and the largest picks
+ * the dictionary entry.  With one K-wide block of weights per head and no
+ * bias:
+ *     scores[b,h,t,k] = sum_d u[b,t,d] * w[h,k,d]      (fp32 accumulation)
+ *     sel_out[b,h,t]  = argmax_k scores[b,h,t,k]       (first maximum wins)
+ * The result feeds pdssm_scan_fwd with PDSSM_SEL_I16.
+ *   u        bf16 [B,L,D] step inputs
+ *   w        bf16 [H,K,D] router weights
+ *   sel_out  int16 [B,H,L] output
+ *   K in [1,64]; D a positive multiple of 32; flags must be 0.
+ * The scores are fp32 sums in an unspecified order: where two scores are
+ * within their rounding error of each other, either index may be returned.
+ * All pointers are device pointers, 16-byte aligned.  Errors:
+ * PDSSM_ERR_NULL, PDSSM_ERR_DIM, PDSSM_ERR_FLAGS, PDSSM_ERR_ALIGN,
+ * PDSSM_ERR_HIP.  Asynchronous on stream; allocates nothing.
+ */
+int pdssm_router_select(const void *u, const void *w, int16_t *sel_out, int64_t B, int64_t L,
+                        int64_t H, int32_t K, int32_t D, uint32_t flags, hipStream_t stream);
+
+/*
  * The selection step alone: sel_out[b,h,t] = the dictionary entry step t
  * picks (Methodology, "1. Novel Selection Mechanism": argmax of the K
  * scores; index modes copy the index).  flags: selection bits only.

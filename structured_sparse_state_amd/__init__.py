@@ -86,6 +86,8 @@ def library() -> ctypes.CDLL:
         lib.pdssm_dict_hardmax.restype = ctypes.c_int
         lib.pdssm_decode_step.argtypes = [P, P, P, P, P, P, P, I64, I64, I32, I32, U32, P]
         lib.pdssm_decode_step.restype = ctypes.c_int
+        lib.pdssm_router_select.argtypes = [P, P, P, I64, I64, I64, I32, I32, U32, P]
+        lib.pdssm_router_select.restype = ctypes.c_int
         _LIB = lib
     return _LIB
 
@@ -170,6 +172,11 @@ def pdssm_decode_step(sel_or_logits, dict_idx, diag, b, c, y, x, B, H, N, K, fla
     return library().pdssm_decode_step(_ptr(sel_or_logits), _ptr(dict_idx), _ptr(diag), _ptr(b),
                                        _ptr(c), _ptr(y), _ptr(x), B, H, N, K, flags,
                                        _stream(stream))
+
+
+def pdssm_router_select(u, w, sel_out, B, L, H, K, D, flags, stream=None) -> int:
+    return library().pdssm_router_select(_ptr(u), _ptr(w), _ptr(sel_out), B, L, H, K, D, flags,
+                                         _stream(stream))
 
 
 def pdssm_strerror(status: int) -> str:
@@ -332,3 +339,18 @@ def decode_step(sel_or_logits, dict_idx, diag, b, c, x, *, sel_mode: str, comple
                         dtype=torch.bfloat16 if y_bf16 else torch.float32)
     check(pdssm_decode_step(sel_or_logits, dict_idx, diag, b, c, y, x, B, H, N, K, flags, stream))
     return y
+
+
+def router_select(u: torch.Tensor, w: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """sel int16 [B,H,L] from bf16 step inputs u [B,L,D] and router weights
+    w [H,K,D]: the argmax of each head's K scores, computed on the matrix
+    cores without writing the scores."""
+    B, L, D = u.shape
+    H, K, D2 = w.shape
+    if D != D2 or u.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise ValueError("u [B,L,D] and w [H,K,D] must be bf16 with the same D")
+    if out is None:
+        out = torch.empty((B, H, L), dtype=torch.int16, device=u.device)
+    check(pdssm_router_select(u, w, out, B, L, H, K, D, 0, stream))
+    return out

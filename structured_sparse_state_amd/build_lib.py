@@ -10,7 +10,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libpdssm.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("pdssm_scan.hip", "pdssm_bwd.hip", "pdssm_aux.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("pdssm_scan.hip", "pdssm_bwd.hip", "pdssm_aux.hip",
+                                            "pdssm_router.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -287,6 +287,23 @@ def make_dense_dict(H: int, K: int, N: int, *, bf16: bool = False, seed: int = 2
     return m.to(torch.bfloat16) if bf16 else m
 
 
+def make_router_inputs(B: int, L: int, H: int, K: int, D: int, *, seed: int = 31, device="cpu",
+                       integers: bool = False):
+    """Step inputs u bf16 [B,L,D] ~ N(0,1) and router weights w bf16 [H,K,D]
+    ~ N(0, 1/D) (so every score is of order one), each from one RNE
+    rounding of fp32 draws; with ``integers``, small integers instead, so
+    that every fp32 sum of products is exact and equal scores are common."""
+    g = _gen(device, seed)
+    if integers:
+        u = torch.randint(-3, 4, (B, L, D), generator=g, device=device).to(torch.bfloat16)
+        w = torch.randint(-2, 3, (H, K, D), generator=g, device=device).to(torch.bfloat16)
+        return u, w
+    u = torch.randn((B, L, D), generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+    w = (torch.randn((H, K, D), generator=g, device=device, dtype=torch.float32) / math.sqrt(D)).to(
+        torch.bfloat16)
+    return u, w
+
+
 def make_grads(inp: ScanInputs, *, seed: int = 0, with_gx_final: bool = True, device=None):
     """Seeded upstream gradients for the backward scan of ``inp``: gy in the
     storage of y ([B,H,L], N(0,1), bf16 rounded once when y is bf16) and

@@ -19,7 +19,7 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"pdssm_scan_fwd", "pdssm_scan_workspace_bytes", "pdssm_select",
                           "pdssm_compose", "pdssm_strerror", "pdssm_scan_fwd_save",
                           "pdssm_scan_bwd", "pdssm_scan_bwd_workspace_bytes", "pdssm_dict_hardmax",
-                          "pdssm_decode_step"}
+                          "pdssm_decode_step", "pdssm_router_select"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -165,3 +165,16 @@ def test_decode_argument_errors(lib):
     assert _dec(flags=0x20) == pk.PDSSM_ERR_FLAGS
     for name in ("sel", "dict_idx", "diag", "b", "c", "y", "x"):
         assert _dec(**{name: FAKE + 4}) == pk.PDSSM_ERR_ALIGN, name
+
+
+def test_router_argument_errors(lib):
+    r = pk.pdssm_router_select
+    assert r(None, FAKE, FAKE, 2, 100, 3, 64, 256, 0, 0) == pk.PDSSM_ERR_NULL
+    assert r(FAKE, FAKE, None, 2, 100, 3, 64, 256, 0, 0) == pk.PDSSM_ERR_NULL
+    for B, L, H, K, D in ((0, 100, 3, 64, 256), (2, 0, 3, 64, 256), (2, 100, 0, 64, 256),
+                          (2, 100, 3, 0, 256), (2, 100, 3, 65, 256), (2, 100, 3, 64, 0),
+                          (2, 100, 3, 64, 48), (2, 100, 3, 64, 16)):
+        assert r(FAKE, FAKE, FAKE, B, L, H, K, D, 0, 0) == pk.PDSSM_ERR_DIM, (B, L, H, K, D)
+    assert r(FAKE, FAKE, FAKE, 2, 100, 3, 64, 256, 1, 0) == pk.PDSSM_ERR_FLAGS
+    assert r(FAKE + 2, FAKE, FAKE, 2, 100, 3, 64, 256, 0, 0) == pk.PDSSM_ERR_ALIGN
+    assert r(FAKE, FAKE, FAKE + 2, 2, 100, 3, 64, 256, 0, 0) == pk.PDSSM_ERR_ALIGN

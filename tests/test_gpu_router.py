@@ -1,0 +1,119 @@
+"""GPU parity of the fused router product + argmax (pdssm_router_select).
+
+The oracle computes every score in fp64 (exact products of the bf16 inputs)
+and takes the first maximum.  The kernel sums in fp32, so where two scores
+lie within their rounding error of each other either index is correct: the
+test demands, for every (b,h,t), that the kernel's choice k satisfies
+    s_max - s_k <= E_k + E_kmax,   E_j = D * 2^-24 * sum_d |u_d w_jd|
+(the first-order bound on an fp32 sum of D exact products), and that it
+equals the oracle's index whenever the two are not that close.  With
+small-integer inputs every fp32 sum is exact, and the kernel must return the
+oracle's index everywhere, ties included.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import structured_sparse_state_amd as pk
+from structured_sparse_state_amd import inputs as gen
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.get()
+
+
+def check_choice(u, w, got, ref, lg):
+    """got/ref int [B,H,L], lg fp64 scores [B,H,L,K] for the same tokens."""
+    uf = u.double().abs().numpy()
+    wf = w.double().abs().numpy()
+    D = uf.shape[-1]
+    bound = np.einsum("bld,hkd->bhlk", uf, wf) * D * 2.0 ** -24 * 1.001
+    smax = lg.max(axis=-1)
+    take = np.take_along_axis
+    s_got = take(lg, got[..., None].astype(np.int64), -1)[..., 0]
+    e_got = take(bound, got[..., None].astype(np.int64), -1)[..., 0]
+    e_ref = take(bound, ref[..., None].astype(np.int64), -1)[..., 0]
+    assert np.all((got >= 0) & (got < lg.shape[-1]))
+    ok = (got == ref) | (smax - s_got <= e_got + e_ref)
+    assert ok.all(), f"{(~ok).sum()} choices outside the rounding bound"
+    return int((got != ref).sum())
+
+
+ROUTER_SHAPES = [
+    # B, L, H, K, D
+    (1, 1, 1, 1, 32),
+    (2, 100, 3, 5, 64),
+    (1, 300, 2, 64, 256),
+    (2, 257, 5, 33, 96),
+    (1, 511, 4, 64, 2048),
+    (3, 90, 1, 17, 160),
+]
+
+
+@pytest.mark.parametrize("B,L,H,K,D", ROUTER_SHAPES)
+def test_router_matches_oracle(orc, B, L, H, K, D):
+    say(f"[case] router B={B} L={L} H={H} K={K} D={D}")
+    u, w = gen.make_router_inputs(B, L, H, K, D, seed=B * 1000 + L + K)
+    ref, lg = orc.router_select(u, w, want_logits=True, nthreads=8)
+    got = pk.router_select(u.to(DEV), w.to(DEV))
+    torch.cuda.synchronize()
+    n = check_choice(u, w, got.cpu().numpy(), ref, lg)
+    say(f"  {n} near-tie choices differ from the oracle's of {ref.size}")
+
+
+@pytest.mark.parametrize("B,L,H,K,D", [(1, 300, 3, 64, 64), (2, 129, 2, 7, 512), (1, 256, 2, 64, 2048)])
+def test_router_exact_integers(orc, B, L, H, K, D):
+    """Exact sums: the kernel's index equals the oracle's everywhere (the
+    first maximum on ties)."""
+    say(f"[case] router exact B={B} L={L} H={H} K={K} D={D}")
+    u, w = gen.make_router_inputs(B, L, H, K, D, seed=7 + D, integers=True)
+    ref = orc.router_select(u, w, nthreads=8)
+    got = pk.router_select(u.to(DEV), w.to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+def test_router_lm_full_size_sampled(orc):
+    """The LM-layer router at full size (B=8 L=4096 H=32 K=64, D=2048): sampled
+    tokens against the oracle, including the first and last of several
+    256-token tiles."""
+    B, L, H, K, D = 8, 4096, 32, 64, 2048
+    say(f"[case] router lm full size B={B} L={L} H={H} K={K} D={D}")
+    u, w = gen.make_router_inputs(B, L, H, K, D, seed=4, device=DEV)
+    got = pk.router_select(u, w)
+    torch.cuda.synchronize()
+    ts = sorted({0, 1, 255, 256, 257, 511, 1000, 2047, 2048, 3071, 4094, 4095})
+    for bi in (0, 5, B - 1):
+        us = u[bi:bi + 1, ts].cpu().contiguous()
+        ref, lg = orc.router_select(us, w.cpu(), want_logits=True, nthreads=8)
+        check_choice(us, w.cpu(), got[bi:bi + 1][:, :, ts].cpu().numpy(), ref, lg)
+
+
+def test_router_feeds_scan(orc):
+    """Router selections drive the scan exactly like the oracle's."""
+    inp = gen.make_inputs("lm", B=1, H=4, L=300, seed=91)
+    u, w = gen.make_router_inputs(1, 300, 4, 64, 128, seed=92, integers=True)
+    inp.sel_or_logits = torch.from_numpy(orc.router_select(u, w)).to(torch.int16)
+    inp.sel_mode = gen.SEL_I16
+    g = inp.to(DEV)
+    g.sel_or_logits = pk.router_select(u.to(DEV), w.to(DEV))
+    assert torch.equal(g.sel_or_logits.cpu(), inp.sel_or_logits)
+    y, _ = pk.scan(g)
+    y_ref, _ = pk.scan(inp.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
