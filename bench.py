@@ -25,6 +25,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "scanned tokens/sec (B·H·L) and achieved HBM GB/s vs peak, N=64 L=4096"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
+ROUTER_D = 2048                  # router input features per token
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "scan_kernel_lm_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "structured_sparse_state_amd", "csrc", f)
                   for f in ("pdssm_scan.hip", "pdssm_device.h")]
@@ -145,9 +147,20 @@ def measure_aux(pk, gen, inp, stream):
                        bc_bf16=inp.bc_bf16, y_bf16=inp.y_bf16, y=y, stream=stream)
 
     t_dec = _event_time(dec, 200, 20, stream)
+
+    # Router scores + argmax from the step inputs (D = 2048 features per
+    # token), only the int16 selections written.
+    D = ROUTER_D
+    ru, rw = gen.make_router_inputs(B, inp.L, H, K, D, seed=4, device=dev)
+    rsel = pk.router_select(ru, rw, stream=stream)
+    t_rt = _event_time(lambda: pk.router_select(ru, rw, out=rsel, stream=stream), 20, 3, stream)
+    rt_flops = 2.0 * B * inp.L * H * K * D
+    rt_pad_flops = 2.0 * B * inp.L * H * 64 * D
+    del ru, rw, rsel
     dec_bytes = sum(t.numel() * t.element_size() for t in (sel, d, b, c, y)) + 2 * x.numel() * 4
     print(f"[bench] dict hardmax {t_hm * 1e6:.1f} us ({hm_bytes / t_hm / 1e9:.0f} GB/s); decode step "
-          f"{t_dec * 1e6:.2f} us ({B * H / t_dec:.3g} tokens/s)", file=sys.stderr, flush=True)
+          f"{t_dec * 1e6:.2f} us ({B * H / t_dec:.3g} tokens/s); router D={D} {t_rt * 1e6:.1f} us "
+          f"({rt_flops / t_rt / 1e12:.0f} TFLOP/s)", file=sys.stderr, flush=True)
     return {
         "dict_hardmax": {"us_per_call": t_hm * 1e6, "shape": f"H={H} K={K} N={N} fp32",
                          "algorithmic_bytes_per_call": hm_bytes,
@@ -158,6 +171,13 @@ def measure_aux(pk, gen, inp, stream):
                         "algorithmic_bytes_per_call": dec_bytes,
                         "note": "launch- and latency-bound: one step reads and writes "
                                 f"{dec_bytes} bytes"},
+        "router_select": {"us_per_call": t_rt * 1e6, "tokens_per_s": B * inp.L * H / t_rt,
+                          "shape": f"B={B} L={inp.L} H={H} K={K} D={D}, bf16 inputs, fp32 sums",
+                          "roofline": {"bound": "mfma", "achieved": rt_flops / t_rt / 1e12,
+                                       "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": rt_flops / t_rt / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                                       "flops_per_call": rt_flops,
+                                       "issued_flops_per_call": rt_pad_flops}},
     }
 
 

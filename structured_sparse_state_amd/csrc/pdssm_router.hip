@@ -32,14 +32,27 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kRM = 256;                  // tokens per workgroup tile
 constexpr int kRH = 2;                    // heads per workgroup tile
 constexpr int kRN = kRH * 64;             // padded score columns per tile
-constexpr int kRK = 32;                   // features per LDS stage
-constexpr int kRowBytes = kRK * 2;        // 64: four 16-byte chunks per row
-constexpr int kABytes = kRM * kRowBytes;  // 16 KB of token rows per stage
-constexpr int kBBytes = kRN * kRowBytes;  // 8 KB of weight rows per stage
+#ifndef PDSSM_ROUTER_BK
+#define PDSSM_ROUTER_BK 32
+#endif
+#ifndef PDSSM_ROUTER_STAGES
+#define PDSSM_ROUTER_STAGES 2
+#endif
+constexpr int kRK = PDSSM_ROUTER_BK;      // features per LDS stage (32 or 64)
+constexpr int kRStages = PDSSM_ROUTER_STAGES;
+constexpr int kRowBytes = kRK * 2;        // bytes of one row of a stage
+constexpr int kChunks = kRK / 8;          // 16-byte chunks per row
+constexpr int kRowsPerLoad = 64 / kChunks;   // rows one 64-lane 16-byte load fills
+constexpr int kABytes = kRM * kRowBytes;  // token rows per stage
+constexpr int kBBytes = kRN * kRowBytes;  // weight rows per stage
+constexpr int kStageBytes = kABytes + kBBytes;
 constexpr int kRThreads = 256;
-constexpr int kALoads = kRM / 16 / 4;     // direct-to-LDS loads per wave per stage (16 rows each)
-constexpr int kBLoads = kRN / 16 / 4;
+constexpr int kALoads = kRM / kRowsPerLoad / 4;   // direct-to-LDS loads per wave per stage
+constexpr int kBLoads = kRN / kRowsPerLoad / 4;
 constexpr int kLoadsPerStage = kALoads + kBLoads;
+constexpr int kRWavesPerEU = kRStages * kStageBytes <= 80 * 1024 ? 2 : 1;
+static_assert(kRK == 32 || kRK == 64, "stage depth");
+static_assert(kRStages >= 2 && kRStages * kStageBytes <= 160 * 1024, "stages fit in LDS");
 
 struct RouterArgs {
     const uint16_t *u;   // [M][D] bf16
@@ -50,10 +63,16 @@ struct RouterArgs {
     uint32_t m_tiles, h_tiles;
 };
 
-// Position of 16-byte chunk c of row r inside the row: the chunks of rows two
-// apart are rotated, so the fragment reads of eight consecutive rows (one
-// LDS cycle of ds_read_b128) land on eight different 16-byte bank groups.
-__device__ __forceinline__ int chunk_pos(int r, int c) { return c ^ ((r >> 1) & 3); }
+// Position of 16-byte chunk c of row r inside the row.  A fragment read
+// (ds_read_b128) has lane l read row l % 32 of a 32-row block; the chunks are
+// rotated from row to row so that both the 8 lanes of every 128-byte group
+// and the 16 lanes of every 256-byte group of the read land on distinct
+// 16-byte bank groups.  The rotation depends on r % 32 only: fragments
+// start at multiples of 32 rows.
+__device__ __forceinline__ int chunk_pos(int r, int c)
+{
+    return kChunks == 4 ? (c ^ (((r >> 1) ^ (r >> 3)) & 3)) : (c ^ ((r ^ ((r >> 3) & 3)) & 7));
+}
 
 // s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
 template <int N>
@@ -63,25 +82,9 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Three LDS stages, each its own variable so that the compiler can tell which
-// stage a fragment read touches and waits only for that stage's loads.
-__shared__ __attribute__((aligned(1024))) char s_stage0[kABytes + kBBytes];
-__shared__ __attribute__((aligned(1024))) char s_stage1[kABytes + kBBytes];
-__shared__ __attribute__((aligned(1024))) char s_stage2[kABytes + kBBytes];
-
-template <int S>
-__device__ __forceinline__ char *stage_buf()
+__global__ void __launch_bounds__(kRThreads, kRWavesPerEU) router_kernel(RouterArgs a)
 {
-    if constexpr (S == 0)
-        return s_stage0;
-    else if constexpr (S == 1)
-        return s_stage1;
-    else
-        return s_stage2;
-}
-
-__global__ void __launch_bounds__(kRThreads, 2) router_kernel(RouterArgs a)
-{
+    __shared__ __attribute__((aligned(1024))) char smem[kRStages * kStageBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
@@ -96,36 +99,45 @@ __global__ void __launch_bounds__(kRThreads, 2) router_kernel(RouterArgs a)
     const int64_t h0 = (int64_t)ht * kRH;
     const int D = a.D, K = a.K;
 
-    // Direct-to-LDS loads: load j of this wave fills rows 16 g .. 16 g + 15 of
-    // the stage (g = wave * loads + j), lane i writing the 16-byte slot i,
-    // i.e. row 16 g + i / 4 at position i % 4, which holds the chunk
-    // chunk_pos(row, i % 4) (the swizzle is its own inverse).  Rows past the
-    // token count or padding score columns read row 0 instead: their results
-    // are never used.
+    // Direct-to-LDS loads: load j of this wave fills the kRowsPerLoad rows
+    // from R g on (g = wave * loads + j, R = kRowsPerLoad), lane i writing
+    // the 16-byte slot i, i.e. row R g + i / kChunks at position
+    // i % kChunks, which holds the chunk chunk_pos(row, i % kChunks) (the
+    // swizzle is its own inverse).  Rows past the token count or padding
+    // score columns read row 0 instead: their results are never used.
     const uint16_t *asrc[kALoads];
 #pragma unroll
     for (int j = 0; j < kALoads; ++j) {
-        const int r = 16 * (wave * kALoads + j) + (lane >> 2);
+        const int r = kRowsPerLoad * (wave * kALoads + j) + lane / kChunks;
         const int64_t m = m0 + r;
-        asrc[j] = a.u + (m < a.M ? m : 0) * (int64_t)D + chunk_pos(r, lane & 3) * 8;
+        asrc[j] = a.u + (m < a.M ? m : 0) * (int64_t)D + chunk_pos(r, lane % kChunks) * 8;
     }
     const uint16_t *bsrc[kBLoads];
 #pragma unroll
     for (int j = 0; j < kBLoads; ++j) {
-        const int col = 16 * (wave * kBLoads + j) + (lane >> 2);
+        const int col = kRowsPerLoad * (wave * kBLoads + j) + lane / kChunks;
         const int64_t h = h0 + col / 64;
         const int k = col % 64;
-        bsrc[j] = a.w + ((h < a.H && k < K) ? (h * K + k) : 0) * (int64_t)D + chunk_pos(col, lane & 3) * 8;
+        bsrc[j] = a.w + ((h < a.H && k < K) ? (h * K + k) : 0) * (int64_t)D + chunk_pos(col, lane % kChunks) * 8;
     }
+    // The loads are written in asm so that the compiler does not see them
+    // as stores to LDS: it would otherwise make every fragment read wait
+    // for all of them (it cannot tell the stages apart).  They write no
+    // registers; the stage waits below are explicit.
+    auto dma = [](const uint16_t *src, uint32_t lds) {
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(src), "s"(lds)
+                     : "memory", "m0");
+    };
     auto issue = [&](char *buf, int k0) {
-        typedef __attribute__((address_space(3))) void lds_void;
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(buf));
 #pragma unroll
         for (int j = 0; j < kALoads; ++j)
-            __builtin_amdgcn_global_load_lds(asrc[j] + k0, (lds_void *)(buf + (wave * kALoads + j) * 1024), 16, 0, 0);
+            dma(asrc[j] + k0, base + (uint32_t)((wave * kALoads + j) * 1024));
 #pragma unroll
         for (int j = 0; j < kBLoads; ++j)
-            __builtin_amdgcn_global_load_lds(bsrc[j] + k0, (lds_void *)(buf + kABytes + (wave * kBLoads + j) * 1024),
-                                             16, 0, 0);
+            dma(bsrc[j] + k0, base + (uint32_t)(kABytes + (wave * kBLoads + j) * 1024));
     };
 
     // This wave: tokens wm*128 .. +128 of the tile, head wn of the tile.
@@ -146,35 +158,18 @@ __global__ void __launch_bounds__(kRThreads, 2) router_kernel(RouterArgs a)
 #pragma unroll
     for (int ks = 0; ks < kRK / 16; ++ks)
         lane_off[ks] = (uint32_t)((lane & 31) * kRowBytes + chunk_pos(lane & 31, ks * 2 + (lane >> 5)) * 16);
-    // The six fragment reads of a k-step are one asm block that waits for
-    // them: written as C++, the compiler would make every LDS read wait for
-    // all global-to-LDS loads in flight (it cannot tell the stages apart),
-    // which would serialise the ring.
     auto compute = [&](const char *base) {
-        const uint32_t ab = lds_addr(base) + (uint32_t)(wm * 128 * kRowBytes);
-        const uint32_t bb = lds_addr(base) + (uint32_t)(kABytes + wn * 64 * kRowBytes);
+        const char *ab = base + wm * 128 * kRowBytes;
+        const char *bb = base + kABytes + wn * 64 * kRowBytes;
 #pragma unroll
         for (int ks = 0; ks < kRK / 16; ++ks) {
-            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-            u32x4 f0, f1, f2, f3, g0, g1;
-            asm volatile(
-                "ds_read_b128 %0, %6\n\t"
-                "ds_read_b128 %1, %6 offset:2048\n\t"
-                "ds_read_b128 %2, %6 offset:4096\n\t"
-                "ds_read_b128 %3, %6 offset:6144\n\t"
-                "ds_read_b128 %4, %7\n\t"
-                "ds_read_b128 %5, %7 offset:2048\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=v"(f0), "=v"(f1), "=v"(f2), "=v"(f3), "=v"(g0), "=v"(g1)
-                : "v"(ab + lane_off[ks]), "v"(bb + lane_off[ks])
-                : "memory");
             bf16x8 af[4], bf[2];
-            __builtin_memcpy(&af[0], &f0, 16);
-            __builtin_memcpy(&af[1], &f1, 16);
-            __builtin_memcpy(&af[2], &f2, 16);
-            __builtin_memcpy(&af[3], &f3, 16);
-            __builtin_memcpy(&bf[0], &g0, 16);
-            __builtin_memcpy(&bf[1], &g1, 16);
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+                af[mi] = *reinterpret_cast<const bf16x8 *>(ab + mi * 32 * kRowBytes + lane_off[ks]);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                bf[ni] = *reinterpret_cast<const bf16x8 *>(bb + ni * 32 * kRowBytes + lane_off[ks]);
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -183,33 +178,29 @@ __global__ void __launch_bounds__(kRThreads, 2) router_kernel(RouterArgs a)
         }
     };
 
-    // Three-stage ring: stage s is consumed while s + 1 and s + 2 load.
-    // Before consuming s each wave waits for its own loads of s (the loads of
-    // the two younger stages may stay in flight), then the barrier makes
-    // every wave's rows of s visible and frees the buffer of s - 1, which
-    // the loads of s + 2 then refill.
+    // Ring of kRStages stages: stage s is consumed while the next
+    // kRStages - 1 load.  Before consuming s each wave waits for its own
+    // loads of s (those of the younger stages may stay in flight), then the
+    // barrier makes every wave's rows of s visible and frees the buffer of
+    // s - 1, which the loads of s + kRStages - 1 then refill.
     const int stages = D / kRK;
-    issue(stage_buf<0>(), 0);
-    if (stages > 1)
-        issue(stage_buf<1>(), kRK);
-    auto step = [&](auto S, int s) {
-        constexpr int cur = decltype(S)::value;
-        constexpr int nxt = (cur + 2) % 3;
-        if (s + 1 < stages)
+#pragma unroll
+    for (int p = 0; p < kRStages - 1; ++p)
+        if (p < stages)
+            issue(smem + p * kStageBytes, p * kRK);
+    for (int s = 0; s < stages; ++s) {
+        const int ahead = min(stages - 1 - s, kRStages - 2);   // younger stages already issued
+        if (ahead >= kRStages - 2)
+            wait_vm<kLoadsPerStage * (kRStages - 2)>();
+        else if (kRStages > 3 && ahead == 1)
             wait_vm<kLoadsPerStage>();
         else
             wait_vm<0>();
         __builtin_amdgcn_s_barrier();
-        if (s + 2 < stages)
-            issue(stage_buf<nxt>(), (s + 2) * kRK);
-        compute(stage_buf<cur>());
-    };
-    for (int s = 0; s < stages; s += 3) {
-        step(std::integral_constant<int, 0>(), s);
-        if (s + 1 < stages)
-            step(std::integral_constant<int, 1>(), s + 1);
-        if (s + 2 < stages)
-            step(std::integral_constant<int, 2>(), s + 2);
+        lds_order();   // no LDS access moves across the barrier
+        if (s + kRStages - 1 < stages)
+            issue(smem + ((s + kRStages - 1) % kRStages) * kStageBytes, (s + kRStages - 1) * kRK);
+        compute(smem + (s % kRStages) * kStageBytes);
     }
 
     // Argmax per token over the head's K scores.  acc[mi][ni][e] is the
