@@ -50,7 +50,8 @@ constexpr int kRThreads = 256;
 constexpr int kALoads = kRM / kRowsPerLoad / 4;   // direct-to-LDS loads per wave per stage
 constexpr int kBLoads = kRN / kRowsPerLoad / 4;
 constexpr int kLoadsPerStage = kALoads + kBLoads;
-constexpr int kRWavesPerEU = kRStages * kStageBytes <= 80 * 1024 ? 2 : 1;
+// Workgroups per CU that the LDS allows (one wave of each per SIMD).
+constexpr int kRWavesPerEU = (160 * 1024) / (kRStages * kStageBytes) < 4 ? (160 * 1024) / (kRStages * kStageBytes) : 4;
 static_assert(kRK == 32 || kRK == 64, "stage depth");
 static_assert(kRStages >= 2 && kRStages * kStageBytes <= 160 * 1024, "stages fit in LDS");
 
@@ -205,47 +206,65 @@ __global__ void __launch_bounds__(kRThreads, kRWavesPerEU) router_kernel(RouterA
 
     // Argmax per token over the head's K scores.  acc[mi][ni][e] is the
     // score of token wm*128 + mi*32 + 8*(e/4) + 4*(lane/32) + e%4 and entry
-    // k = ni*32 + lane%32: compare the lane's two entries, then reduce over
-    // the 32 lanes of each half-wave (ties to the lower index).
+    // k = ni*32 + lane%32.  Each lane first keeps the better of its two
+    // entries for each of its 64 tokens (c = mi*16 + e); then the 32 lanes
+    // of each half-wave reduce by recursive halving: at the exchange with the
+    // lane 2^s apart, a lane keeps half of its tokens and hands the other
+    // half to its partner, so after five exchanges lane l holds the result of
+    // tokens c = 2 (l % 32) and 2 (l % 32) + 1 (62 values sent per lane
+    // instead of 5 per token).  better() orders by score, then by lower
+    // index, so the merge order does not matter.
     const int64_t h = h0 + wn;
-    int keep[2] = {0, 0};
+    float bv[64];
+    int bk[64];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
+            const int c = mi * 16 + e;
             const int k0 = lane & 31, k1 = 32 + (lane & 31);
-            float bv = __uint_as_float(0xFF800000u);   // -inf, beaten by any score
-            int bk = 64;
+            bv[c] = __uint_as_float(0xFF800000u);   // -inf, beaten by any score
+            bk[c] = 64;
             if (k0 < K) {
-                bv = acc[mi][0][e];
-                bk = k0;
+                bv[c] = acc[mi][0][e];
+                bk[c] = k0;
             }
-            if (k1 < K && better(acc[mi][1][e], k1, bv, bk)) {
-                bv = acc[mi][1][e];
-                bk = k1;
+            if (k1 < K && better(acc[mi][1][e], k1, bv[c], bk[c])) {
+                bv[c] = acc[mi][1][e];
+                bk[c] = k1;
             }
+        }
+    }
 #pragma unroll
-            for (int x = 1; x < 32; x <<= 1) {
-                const float ov = __shfl_xor(bv, x, 64);
-                const int ok = __shfl_xor(bk, x, 64);
-                if (better(ov, ok, bv, bk)) {
-                    bv = ov;
-                    bk = ok;
-                }
+    for (int st = 0; st < 5; ++st) {
+        const int m = 16 >> st;          // partner distance
+        const int n = 32 >> st;          // tokens kept after this exchange
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int i = 0; i < n; ++i) {
+            // keep i (lower lane) or n + i (upper lane); send the other
+            const float sv = upper ? bv[i] : bv[n + i];
+            const int sk = upper ? bk[i] : bk[n + i];
+            float kv = upper ? bv[n + i] : bv[i];
+            int kk = upper ? bk[n + i] : bk[i];
+            const float ov = __shfl_xor(sv, m, 64);
+            const int ok = __shfl_xor(sk, m, 64);
+            if (better(ov, ok, kv, kk)) {
+                kv = ov;
+                kk = ok;
             }
-            const int c = mi * 16 + e;   // lane c % 32 of each half keeps combination c
-            if ((lane & 31) == (c & 31))
-                keep[c >> 5] = bk;
+            bv[i] = kv;
+            bk[i] = kk;
         }
     }
     if (h < a.H) {
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-            const int c = r * 32 + (lane & 31), mi = c >> 4, e = c & 15;
+            const int c = 2 * (lane & 31) + r, mi = c >> 4, e = c & 15;
             const int64_t m = m0 + wm * 128 + mi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
             if (m < a.M) {
                 const int64_t b = m / a.L, t = m - b * a.L;
-                a.sel[(b * a.H + h) * a.L + t] = (int16_t)keep[r];
+                a.sel[(b * a.H + h) * a.L + t] = (int16_t)bk[r];
             }
         }
     }
