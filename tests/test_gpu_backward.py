@@ -125,6 +125,7 @@ BWD_SHAPES = [
     (47, 2000, 33, gen.SEL_I32, True, False, False),
     (64, 17, 64, gen.LOGITS_BF16, True, True, True),
     (64, 1000, 128, gen.LOGITS_BF16, True, True, True),
+    (64, 300, 3000, gen.SEL_I32, True, False, False),
 ]
 
 

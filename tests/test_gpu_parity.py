@@ -114,6 +114,12 @@ SHAPES = [
     (64, 1, 64, gen.LOGITS_BF16, True, True, True),
     (64, 127, 2, gen.SEL_I32, False, False, False),
     (64, 5000, 128, gen.LOGITS_BF16, True, True, True),
+    # Entry tables too large for LDS (K * 64 * 2 bytes > 32 KB): the tile's
+    # entries are staged per step instead, and one ticket stream serves all
+    # sequences.  K = 32767 is the largest the int16 selections allow.
+    (64, 700, 300, gen.LOGITS_BF16, True, True, True),
+    (16, 500, 3000, gen.SEL_I32, False, False, False),
+    (64, 300, 32767, gen.SEL_I16, True, True, True),
 ]
 
 
@@ -124,6 +130,13 @@ def test_shapes(orc, N, L, K, mode, cplx, bcbf, ybf):
                               bc_bf16=bcbf, y_bf16=ybf, dmin=0.8, dmax=1.0, with_x0=with_x0,
                               seed=1000 + N * 7 + L)
         run_and_compare(orc, inp, f"shape N={N} L={L} K={K} x0={with_x0}")
+
+
+def test_more_heads_than_workgroups(orc):
+    """More heads than resident workgroups: one ticket stream for all
+    sequences even though each head's table fits in LDS."""
+    inp = gen.make_inputs("tiny", B=1, H=3000, L=40, N=8, K=4, seed=4242, with_x0=True)
+    run_and_compare(orc, inp, "H=3000 L=40 N=8")
 
 
 # ---------------------------------------------------------------------------
