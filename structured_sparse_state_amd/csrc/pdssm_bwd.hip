@@ -560,7 +560,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
         pis[tt / 4] |= (ent & 63u) << (8 * (tt % 4));
         if (tt < nv) {
             const cf v = cmul(d, x);
-            const uint32_t slot = (ent & 0x1FFu) << 3;
+            const uint32_t slot = entry_slot(ent);
             *static_cast<float2 *>(__builtin_assume_aligned(regp + slot, 8)) = make_float2(v.r, v.i);
             lds_order();
             if (__any(slot >= kSpareOff)) {
@@ -572,7 +572,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
                 }
                 lds_order();
             }
-            const char *rowp = rowbase + (ent & 0x600u);
+            const char *rowp = rowbase + entry_row(ent);
             cf sum = bb;
 #pragma unroll
             for (int r = 0; r < kRegions; ++r) {

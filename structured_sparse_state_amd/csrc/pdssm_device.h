@@ -646,10 +646,19 @@ constexpr int kRegions = PDSSM_SCAN_REGIONS;   // collision-free regions (ranks 
 constexpr int kRegionBytes = 64 * 8;           // one block: 64 complex slots
 constexpr int kBlocks = 2 * kRegions + 1;
 constexpr uint32_t kSpareOff = 2 * kRegions * kRegionBytes;
-static_assert(kBlocks <= 8 && kRegions <= 3, "entries hold a 3-bit scatter block and a 2-bit read block");
+constexpr int kBlockBits = kBlocks <= 8 ? 3 : 4;   // bits of the scatter block field
+static_assert(kRegions >= 1 && kRegions <= 4, "the entry's read-block field holds 0..kRegions in 3 bits");
+
+// Byte offset of a source's scatter slot (block * 512 + pi * 8) and of the
+// first block its row reads, from its entry.
+__device__ __forceinline__ uint32_t entry_slot(uint32_t ent) { return (ent & ((1u << (6 + kBlockBits)) - 1u)) << 3; }
+__device__ __forceinline__ uint32_t entry_row(uint32_t ent)
+{
+    return ((ent >> (6 + kBlockBits)) & 7u) * (uint32_t)kRegionBytes;
+}
 
 // The 16-bit entry of source `lane` for the index map row[0..N):
-//   pi | scatter block << 6 | read block << 9.
+//   pi | scatter block << 6 | read block << (6 + kBlockBits).
 // Called by a whole wave (lanes >= N are padding sources that map to
 // themselves with rank 0 and in-degree 1); entries outside [0,N) clamp.
 __device__ __forceinline__ uint16_t dict_entry(const int32_t *row, int N, int lane)
@@ -665,7 +674,7 @@ __device__ __forceinline__ uint16_t dict_entry(const int32_t *row, int N, int la
         deg = 1;   // padding rows hold their own (zero) state
     const int block = rank < kRegions ? kRegions - 1 - rank : 2 * kRegions;
     const int rblock = kRegions - min(deg, kRegions);
-    return (uint16_t)(pi | (block << 6) | (rblock << 9));
+    return (uint16_t)(pi | (block << 6) | (rblock << (6 + kBlockBits)));
 }
 
 // ---------------------------------------------------------------------------

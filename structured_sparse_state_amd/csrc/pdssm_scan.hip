@@ -62,7 +62,7 @@ struct ScanArgs {
     uint32_t sel_mode;
     int y_bf16;
     int dict_lds;   // the head's entry table fits in LDS
-    const uint16_t *tab;   // [H][K][NP]: pi | scatter block << 6 | row read block << 9 (see prep_kernel)
+    const uint16_t *tab;   // [H][K][NP]: dict_entry() of every source (see prep_kernel)
 };
 
 // Scan tiling: a chunk is kScanT steps of one group of NP lanes; a wave holds
@@ -790,7 +790,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                 // reads kRegions blocks from the offset its entry names: the
                 // in-degree(i) regions written in this step, then zero blocks.
                 const cf v = cmul(d, x);
-                const uint32_t slot = (ent & 0x1FFu) << 3;   // block * 512 + pi * 8
+                const uint32_t slot = entry_slot(ent);   // block * 512 + pi * 8
                 *static_cast<float2 *>(__builtin_assume_aligned(regp + slot, 8)) = make_float2(v.r, v.i);
                 lds_order();
                 if (__any(slot >= kSpareOff)) {
@@ -802,7 +802,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                     }
                     lds_order();
                 }
-                const char *rowp = rowbase + (ent & 0x600u);   // read block * 512
+                const char *rowp = rowbase + entry_row(ent);   // read block * 512
 #pragma unroll
                 for (int r = 0; r < kRegions; ++r) {
                     const float2 u = *static_cast<const float2 *>(__builtin_assume_aligned(rowp + r * kRegionBytes, 8));
