@@ -50,9 +50,10 @@ constexpr int kRThreads = 256;
 constexpr int kALoads = kRM / kRowsPerLoad / 4;   // direct-to-LDS loads per wave per stage
 constexpr int kBLoads = kRN / kRowsPerLoad / 4;
 constexpr int kLoadsPerStage = kALoads + kBLoads;
-// Workgroups per CU that the LDS allows (one wave of each per SIMD).
-constexpr int kRWavesPerEU = (160 * 1024) / (kRStages * kStageBytes) < 4 ? (160 * 1024) / (kRStages * kStageBytes) : 4;
-static_assert(kRK == 32 || kRK == 64, "stage depth");
+// Workgroups per CU that the LDS allows (one wave of each per SIMD), at most
+// three: a wave needs about 168 VGPRs (128 of them accumulators).
+constexpr int kRWavesPerEU = (160 * 1024) / (kRStages * kStageBytes) < 3 ? (160 * 1024) / (kRStages * kStageBytes) : 3;
+static_assert(kRK == 16 || kRK == 32 || kRK == 64, "stage depth");
 static_assert(kRStages >= 2 && kRStages * kStageBytes <= 160 * 1024, "stages fit in LDS");
 
 struct RouterArgs {
@@ -72,7 +73,12 @@ struct RouterArgs {
 // start at multiples of 32 rows.
 __device__ __forceinline__ int chunk_pos(int r, int c)
 {
-    return kChunks == 4 ? (c ^ (((r >> 1) ^ (r >> 3)) & 3)) : (c ^ ((r ^ ((r >> 3) & 3)) & 7));
+    if constexpr (kChunks == 2)
+        return c ^ (((r >> 2) ^ (r >> 3)) & 1);
+    else if constexpr (kChunks == 4)
+        return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+    else
+        return c ^ ((r ^ ((r >> 3) & 3)) & 7);
 }
 
 // s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
