@@ -422,7 +422,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
     using DRaw = typename std::conditional<CPLX, float2, float>::type;
     using Stored = typename std::conditional<BCBF, typename std::conditional<CPLX, uint32_t, uint16_t>::type, Raw>::type;
     // Entry table: the head's [K][NP] 16-bit entries when they fit, else the
-    // tile's entries per (wave, step, lane), one per 32-bit word.
+    // tile's entries, one row of NP 16-bit entries per (wave, step).
     extern __shared__ __attribute__((aligned(16))) uint32_t s_tab[];
     __shared__ int16_t s_sel[W][G * T];
     __shared__ __attribute__((aligned(16))) cf s_reg[W][kBlocks][64];   // scatter regions, zero blocks, spare
@@ -679,12 +679,13 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         else
             wave_select<G * T>(a.sel, mode, Kq, a.L, row0, tw0, s_sel[wave], q.ln);
         if (!a.dict_lds) {
+            // The entries of the wave's steps, one NP-wide row per step.
             lds_order();
             const uint16_t *tab_h = a.tab + h * (int64_t)K * NP;
-            uint32_t *tb = s_tab + wave * T * 64 + q.ln;
+            uint16_t *tb = reinterpret_cast<uint16_t *>(s_tab) + (wave * G * T + q.g * T) * NP + q.i;
             for (int tt = 0; tt < T; ++tt) {
                 const int k = s_sel[wave][q.g * T + tt];
-                tb[tt * 64] = tab_h[k * NP + q.i];
+                tb[tt * NP] = tab_h[k * NP + q.i];
             }
         }
         lds_order();
@@ -734,7 +735,10 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         char *const regp = reinterpret_cast<char *>(&s_reg[wave][0][0]) + q.gbase * (int)sizeof(cf);
         // The entries of this lane: column i of the head's table, or its own
         // word per step of the wave's entries (both as byte addresses).
-        const char *const tbp = reinterpret_cast<const char *>(s_tab) + (a.dict_lds ? q.i * 2 : (wave * T * 64 + q.ln) * 4);
+        // Both are rows of NP 16-bit entries: the head's table, row = the
+        // step's selection, or the wave's staged entries, row = the step.
+        const char *const tbp = reinterpret_cast<const char *>(s_tab) +
+                                (a.dict_lds ? q.i * 2 : ((wave * G * T + q.g * T) * NP + q.i) * 2);
         const char *const rowbase = regp + q.i * (int)sizeof(cf);   // row i of block 0
         cf x = {0.f, 0.f};
         int pa4 = q.ln * 4;
@@ -745,13 +749,13 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         // the chunk's selections in one register and broadcast them per step.
         int selv = 0;
         if constexpr (G == 1)
-            selv = s_sel[wave][q.ln % T];
+            selv = a.dict_lds ? (int)s_sel[wave][q.ln % T] : q.ln % T;
         auto entry = [&](int tt) -> uint32_t {
-            if (a.dict_lds) {
-                const int k = (G == 1) ? __builtin_amdgcn_readlane(selv, tt) : (int)s_sel[wave][q.g * T + tt];
-                return *reinterpret_cast<const uint16_t *>(tbp + k * NP * 2);
-            }
-            return *reinterpret_cast<const uint32_t *>(tbp + tt * 256);
+            if constexpr (G == 1)
+                return *reinterpret_cast<const uint16_t *>(tbp + __builtin_amdgcn_readlane(selv, tt) * NP * 2);
+            if (a.dict_lds)
+                return *reinterpret_cast<const uint16_t *>(tbp + (int)s_sel[wave][q.g * T + tt] * NP * 2);
+            return *reinterpret_cast<const uint16_t *>(tbp + tt * NP * 2);
         };
         uint32_t ent_next = entry(0);
 #pragma unroll
@@ -1266,7 +1270,7 @@ static hipError_t launch_scan(const ScanArgs &a, hipStream_t st)
 {
     // The table is staged in rows of 64 lanes x 16 bytes: whole rows fit.
     const size_t dyn = a.dict_lds ? (((size_t)a.K * NP * 2 + 1023) & ~(size_t)1023)
-                                  : (size_t)kScanW * kScanT * 64 * 4;
+                                  : (size_t)kScanW * kScanT * 64 * 2;
     const int block = (kScanW + 1) * 64;
     // Resident workgroups per device, cached per (device, LDS size).
     static thread_local int c_dev = -1, c_wgs = 0;
