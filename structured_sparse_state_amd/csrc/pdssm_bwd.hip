@@ -71,7 +71,31 @@ struct BwdArgs {
     int N, K;
     uint32_t sel_mode;
     int y_bf16;
+    int idx32;          // chunk and sequence counts fit 31 bits: 32-bit index arithmetic
 };
+
+// Sequence and first step of chunk ch, and the sequence's head.  The
+// divisions are 32-bit when the counts allow (a 64-bit one costs a few
+// hundred instructions before the chunk's first load can go out).
+struct ChunkPos {
+    int64_t seq, t0, h;
+};
+__device__ __forceinline__ ChunkPos chunk_of(const BwdArgs &a, int64_t ch)
+{
+    ChunkPos p;
+    if (a.idx32) {
+        const uint32_t c = (uint32_t)ch, n = (uint32_t)a.nch;
+        const uint32_t sq = c / n;
+        p.seq = sq;
+        p.t0 = (int64_t)(c - sq * n) * kBT;
+        p.h = sq % (uint32_t)a.H;
+    } else {
+        p.seq = ch / a.nch;
+        p.t0 = (ch - p.seq * a.nch) * kBT;
+        p.h = p.seq % a.H;
+    }
+    return p;
+}
 
 template <bool CPLX>
 __device__ __forceinline__ void store_grad(float *p, int64_t e, cf v)
@@ -270,10 +294,9 @@ __global__ void __launch_bounds__(kBW * 64) bwd_ops_kernel(BwdArgs a)
     const int64_t ch = (int64_t)blockIdx.x * kBW + wave;
     if (ch >= a.S * a.nch)
         return;
-    const int64_t seq = ch / a.nch;
-    const int64_t t0 = (ch - seq * a.nch) * kBT;
+    const ChunkPos cp = chunk_of(a, ch);
+    const int64_t seq = cp.seq, t0 = cp.t0, h = cp.h;
     const int nv = (int)min((int64_t)kBT, a.L - t0);
-    const int64_t h = seq % a.H;
     // The chunk's d and c rows do not depend on the selection: all of them
     // are in flight before the selections are used.
     const bool idx = index_mode(a.sel_mode);
@@ -482,10 +505,9 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
     const int64_t ch = (int64_t)blockIdx.x * kBW + wave;
     if (ch >= a.S * a.nch)
         return;
-    const int64_t seq = ch / a.nch;
-    const int64_t t0 = (ch - seq * a.nch) * kBT;
+    const ChunkPos cp = chunk_of(a, ch);
+    const int64_t seq = cp.seq, t0 = cp.t0, h = cp.h;
     const int nv = (int)min((int64_t)kBT, a.L - t0);
-    const int64_t h = seq % a.H;
     const int N = a.N;
 #pragma unroll
     for (int r = kRegions; r < 2 * kRegions; ++r)
@@ -732,6 +754,7 @@ extern "C" int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx
     a.K = K;
     a.sel_mode = flags & PDSSM_SEL_MASK;
     a.y_bf16 = (flags & PDSSM_Y_BF16) ? 1 : 0;
+    a.idx32 = (lo.S * lo.nch < ((int64_t)1 << 31) && H < ((int64_t)1 << 31)) ? 1 : 0;
 
     const int64_t entries = H * (int64_t)K;
     hipLaunchKernelGGL(bwd_tab_kernel, dim3((unsigned)((entries + 3) / 4)), dim3(256), 0, stream, dict_idx,
