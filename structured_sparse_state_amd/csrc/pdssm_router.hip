@@ -81,6 +81,16 @@ __device__ __forceinline__ int chunk_pos(int r, int c)
         return c ^ ((r ^ ((r >> 3) & 3)) & 7);
 }
 
+// better() of the selection (the score, then the lower index; a NaN above
+// every number, the first NaN winning) as one boolean expression, so that the
+// compiler selects instead of branching per comparison.
+__device__ __forceinline__ bool beats(float v2, int k2, float v1, int k1)
+{
+    const bool n1 = v1 != v1, n2 = v2 != v2;
+    const bool klt = k2 < k1;
+    return (n2 & (!n1 | klt)) | (!n2 & !n1 & ((v2 > v1) | ((v2 == v1) & klt)));
+}
+
 // s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vm()
@@ -229,16 +239,11 @@ __global__ void __launch_bounds__(kRThreads, kRWavesPerEU) router_kernel(RouterA
         for (int e = 0; e < 16; ++e) {
             const int c = mi * 16 + e;
             const int k0 = lane & 31, k1 = 32 + (lane & 31);
-            bv[c] = __uint_as_float(0xFF800000u);   // -inf, beaten by any score
-            bk[c] = 64;
-            if (k0 < K) {
-                bv[c] = acc[mi][0][e];
-                bk[c] = k0;
-            }
-            if (k1 < K && better(acc[mi][1][e], k1, bv[c], bk[c])) {
-                bv[c] = acc[mi][1][e];
-                bk[c] = k1;
-            }
+            bv[c] = (k0 < K) ? acc[mi][0][e] : __uint_as_float(0xFF800000u);   // -inf: beaten by any score
+            bk[c] = (k0 < K) ? k0 : 64;
+            const bool take = (k1 < K) & beats(acc[mi][1][e], k1, bv[c], bk[c]);
+            bv[c] = take ? acc[mi][1][e] : bv[c];
+            bk[c] = take ? k1 : bk[c];
         }
     }
 #pragma unroll
@@ -255,12 +260,9 @@ __global__ void __launch_bounds__(kRThreads, kRWavesPerEU) router_kernel(RouterA
             int kk = upper ? bk[n + i] : bk[i];
             const float ov = __shfl_xor(sv, m, 64);
             const int ok = __shfl_xor(sk, m, 64);
-            if (better(ov, ok, kv, kk)) {
-                kv = ov;
-                kk = ok;
-            }
-            bv[i] = kv;
-            bk[i] = kk;
+            const bool take = beats(ov, ok, kv, kk);
+            bv[i] = take ? ov : kv;
+            bk[i] = take ? ok : kk;
         }
     }
     if (h < a.H) {
