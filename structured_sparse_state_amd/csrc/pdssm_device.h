@@ -365,12 +365,22 @@ __device__ __forceinline__ V bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint
 // the K scores (coalesced, 16-byte loads when aligned), then the slices
 // combine across lanes.  Writes k to out[q] for q < SPW (0 past the end).
 // ---------------------------------------------------------------------------
+// (v2, k2) beats (v1, k1): the higher score, then the lower index; a NaN is
+// above every number and the first NaN wins.  One boolean expression, so
+// that callers select instead of branching per comparison.
 __device__ __forceinline__ bool better(float v2, int k2, float v1, int k1)
 {
     const bool n1 = v1 != v1, n2 = v2 != v2;
-    if (n2)
-        return !n1 || k2 < k1;
-    return !n1 && (v2 > v1 || (v2 == v1 && k2 < k1));
+    const bool klt = k2 < k1;
+    return (n2 & (!n1 | klt)) | (!n2 & !n1 & ((v2 > v1) | ((v2 == v1) & klt)));
+}
+
+// Keep the better of (bv, bk) and (v, k); `ok` false leaves them as they are.
+__device__ __forceinline__ void take_better(float v, int k, bool ok, float &bv, int &bk)
+{
+    const bool t = ok & better(v, k, bv, bk);
+    bv = t ? v : bv;
+    bk = t ? k : bk;
 }
 
 __device__ __forceinline__ void slice_argmax(const void *__restrict__ src, uint32_t mode,
@@ -381,15 +391,15 @@ __device__ __forceinline__ void slice_argmax(const void *__restrict__ src, uint3
         if (((K | k0 | k1) & 3) == 0) {
             for (int q = k0; q < k1; q += 4) {
                 const float4 v = *reinterpret_cast<const float4 *>(row + q);
-                if (better(v.x, q, bv, bk)) { bv = v.x; bk = q; }
-                if (better(v.y, q + 1, bv, bk)) { bv = v.y; bk = q + 1; }
-                if (better(v.z, q + 2, bv, bk)) { bv = v.z; bk = q + 2; }
-                if (better(v.w, q + 3, bv, bk)) { bv = v.w; bk = q + 3; }
+                take_better(v.x, q, true, bv, bk);
+                take_better(v.y, q + 1, true, bv, bk);
+                take_better(v.z, q + 2, true, bv, bk);
+                take_better(v.w, q + 3, true, bv, bk);
             }
         } else {
             for (int q = k0; q < k1; ++q) {
                 const float v = row[q];
-                if (better(v, q, bv, bk)) { bv = v; bk = q; }
+                take_better(v, q, true, bv, bk);
             }
         }
     } else {
@@ -401,14 +411,14 @@ __device__ __forceinline__ void slice_argmax(const void *__restrict__ src, uint3
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const float lo = bf16_lo(ws[m]), hi = bf16_hi(ws[m]);
-                    if (better(lo, q + 2 * m, bv, bk)) { bv = lo; bk = q + 2 * m; }
-                    if (better(hi, q + 2 * m + 1, bv, bk)) { bv = hi; bk = q + 2 * m + 1; }
+                    take_better(lo, q + 2 * m, true, bv, bk);
+                    take_better(hi, q + 2 * m + 1, true, bv, bk);
                 }
             }
         } else {
             for (int q = k0; q < k1; ++q) {
                 const float v = bf16_lo(row[q]);
-                if (better(v, q, bv, bk)) { bv = v; bk = q; }
+                take_better(v, q, true, bv, bk);
             }
         }
     }
@@ -449,7 +459,7 @@ __device__ __forceinline__ void wave_select(const void *__restrict__ src, uint32
                 const int from = (lane ^ m) << 2;
                 const float ov = bperm_a(bv, from);
                 const int ok = (int)bperm_a((uint32_t)bk, from);
-                if (better(ov, ok, bv, bk)) { bv = ov; bk = ok; }
+                take_better(ov, ok, true, bv, bk);
             }
             k = bk;
         }
@@ -551,10 +561,7 @@ __device__ __forceinline__ void select_finish(const ScoreSlice<NV> &s, uint32_t 
                     continue;
                 const float val = bf ? ((m & 1) ? bf16_hi(w[m >> 1]) : bf16_lo(w[m >> 1]))
                                      : __uint_as_float(w[m]);
-                if (kk < k1 && better(val, kk, bv, bk)) {
-                    bv = val;
-                    bk = kk;
-                }
+                take_better(val, kk, kk < k1, bv, bk);
             }
         }
 #pragma unroll
@@ -572,10 +579,7 @@ __device__ __forceinline__ void select_finish(const ScoreSlice<NV> &s, uint32_t 
                 ov = bperm_a(bv, src);
                 ok = (int)bperm_a((uint32_t)bk, src);
             }
-            if (better(ov, ok, bv, bk)) {
-                bv = ov;
-                bk = ok;
-            }
+            take_better(ov, ok, true, bv, bk);
         }
         k = bk;
     }
