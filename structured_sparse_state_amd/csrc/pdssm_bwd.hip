@@ -263,7 +263,7 @@ __device__ __forceinline__ typename ChunkIO<CPLX, BCBF>::Stored pack_vec(cf v)
 {
     if constexpr (BCBF) {
         if constexpr (CPLX)
-            return (uint32_t)f32_to_bf16_rne(v.r) | ((uint32_t)f32_to_bf16_rne(v.i) << 16);
+            return f32x2_to_bf16x2_rne(v.r, v.i);
         else
             return f32_to_bf16_rne(v.r);
     } else if constexpr (CPLX) {

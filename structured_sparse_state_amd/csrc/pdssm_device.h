@@ -60,13 +60,25 @@ __device__ __forceinline__ uint32_t opaque_s(uint32_t v)
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// fp32 -> bf16, rounded to nearest even: one v_cvt_pk_bf16_f32 (a NaN
+// stays a quiet NaN).  The pair form converts (lo, hi) into one word.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u)   // NaN: keep it a (quiet) NaN
-        return (uint16_t)((u >> 16) | 0x40u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const __bf16 h = (__bf16)f;
+    uint16_t u;
+    __builtin_memcpy(&u, &h, 2);
+    return u;
+}
+
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float lo, float hi)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    const bf16x2_t h = __builtin_convertvector(v, bf16x2_t);
+    uint32_t u;
+    __builtin_memcpy(&u, &h, 4);
+    return u;
 }
 
 // ---------------------------------------------------------------------------
