@@ -55,3 +55,28 @@ def test_fsa_dictionaries():
     inp = gen.make_fsa_inputs("parity", L=10)
     assert float(inp.c[0, 0, 0, 1]) == 2.0 and float(inp.c[0, 0, 0, 0]) == 1.0
     assert math.isclose(float(inp.diag.sum()), 10 * 8)
+
+
+def test_router_and_dictionary_generators():
+    u1, w1 = gen.make_router_inputs(2, 5, 3, 4, 32, seed=9)
+    u2, w2 = gen.make_router_inputs(2, 5, 3, 4, 32, seed=9)
+    assert torch.equal(u1, u2) and torch.equal(w1, w2)
+    assert u1.shape == (2, 5, 32) and w1.shape == (3, 4, 32)
+    assert u1.dtype == torch.bfloat16 and w1.dtype == torch.bfloat16
+    ui, wi = gen.make_router_inputs(1, 7, 2, 3, 16, integers=True)
+    assert torch.equal(ui.float(), ui.float().round()) and float(ui.float().abs().max()) <= 3
+    assert torch.equal(wi.float(), wi.float().round()) and float(wi.float().abs().max()) <= 2
+    m = gen.make_dense_dict(2, 3, 8, seed=5)
+    assert m.shape == (2, 3, 8, 8) and m.dtype == torch.float32
+    assert torch.equal(m, gen.make_dense_dict(2, 3, 8, seed=5))
+    assert gen.make_dense_dict(1, 2, 4, bf16=True).dtype == torch.bfloat16
+
+
+def test_upstream_gradients():
+    inp = gen.make_inputs("lm", B=1, H=2, L=20)
+    gy, gxf = gen.make_grads(inp, seed=2)
+    assert gy.shape == (1, 2, 20) and gy.dtype == torch.bfloat16
+    assert gxf.shape == (1, 2, 64, 2) and gxf.dtype == torch.float32
+    gy2, _ = gen.make_grads(inp, seed=2)
+    assert torch.equal(gy, gy2)
+    assert gen.make_grads(inp, seed=2, with_gx_final=False)[1] is None
