@@ -29,8 +29,13 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+#ifndef PDSSM_ROUTER_HEADS
+#define PDSSM_ROUTER_HEADS 2
+#endif
 constexpr int kRM = 256;                  // tokens per workgroup tile
-constexpr int kRH = 2;                    // heads per workgroup tile
+constexpr int kRH = PDSSM_ROUTER_HEADS;   // heads per workgroup tile (2 or 4)
+constexpr int kWH = kRH / 2;              // heads per wave (waves are 2 x 2)
+constexpr int kNT = 2 * kWH;              // 32-column MFMA tiles per wave
 constexpr int kRN = kRH * 64;             // padded score columns per tile
 #ifndef PDSSM_ROUTER_BK
 #define PDSSM_ROUTER_BK 32
@@ -51,8 +56,12 @@ constexpr int kALoads = kRM / kRowsPerLoad / 4;   // direct-to-LDS loads per wav
 constexpr int kBLoads = kRN / kRowsPerLoad / 4;
 constexpr int kLoadsPerStage = kALoads + kBLoads;
 // Workgroups per CU that the LDS allows (one wave of each per SIMD), at most
-// three: a wave needs about 168 VGPRs (128 of them accumulators).
-constexpr int kRWavesPerEU = (160 * 1024) / (kRStages * kStageBytes) < 3 ? (160 * 1024) / (kRStages * kStageBytes) : 3;
+// three with one head per wave (about 168 VGPRs, 128 of them accumulators)
+// and one with two (256 accumulators).
+constexpr int kRWaveCap = kWH == 1 ? 3 : 1;
+constexpr int kRWavesPerEU = (160 * 1024) / (kRStages * kStageBytes) < kRWaveCap
+                                 ? (160 * 1024) / (kRStages * kStageBytes) : kRWaveCap;
+static_assert(kRH == 2 || kRH == 4, "heads per tile");
 static_assert(kRK == 16 || kRK == 32 || kRK == 64, "stage depth");
 static_assert(kRStages >= 2 && kRStages * kStageBytes <= 160 * 1024, "stages fit in LDS");
 
@@ -157,13 +166,13 @@ __global__ void __launch_bounds__(kRThreads, kRWavesPerEU) router_kernel(RouterA
             dma(bsrc[j] + k0, base + (uint32_t)(kABytes + (wave * kBLoads + j) * 1024));
     };
 
-    // This wave: tokens wm*128 .. +128 of the tile, head wn of the tile.
+    // This wave: tokens wm*128 .. +128 of the tile, heads wn*kWH .. +kWH.
     const int wm = wave >> 1, wn = wave & 1;
-    f32x16 acc[4][2];
+    f32x16 acc[4][kNT];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int ni = 0; ni < kNT; ++ni)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 acc[mi][ni][e] = 0.f;
@@ -177,20 +186,20 @@ __global__ void __launch_bounds__(kRThreads, kRWavesPerEU) router_kernel(RouterA
         lane_off[ks] = (uint32_t)((lane & 31) * kRowBytes + chunk_pos(lane & 31, ks * 2 + (lane >> 5)) * 16);
     auto compute = [&](const char *base) {
         const char *ab = base + wm * 128 * kRowBytes;
-        const char *bb = base + kABytes + wn * 64 * kRowBytes;
+        const char *bb = base + kABytes + wn * kWH * 64 * kRowBytes;
 #pragma unroll
         for (int ks = 0; ks < kRK / 16; ++ks) {
-            bf16x8 af[4], bf[2];
+            bf16x8 af[4], bf[kNT];
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
                 af[mi] = *reinterpret_cast<const bf16x8 *>(ab + mi * 32 * kRowBytes + lane_off[ks]);
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
+            for (int ni = 0; ni < kNT; ++ni)
                 bf[ni] = *reinterpret_cast<const bf16x8 *>(bb + ni * 32 * kRowBytes + lane_off[ks]);
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
+                for (int ni = 0; ni < kNT; ++ni)
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
         }
     };
@@ -230,49 +239,52 @@ __global__ void __launch_bounds__(kRThreads, kRWavesPerEU) router_kernel(RouterA
     // tokens c = 2 (l % 32) and 2 (l % 32) + 1 (62 values sent per lane
     // instead of 5 per token).  better() orders by score, then by lower
     // index, so the merge order does not matter.
-    const int64_t h = h0 + wn;
-    float bv[64];
-    int bk[64];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+    for (int hn = 0; hn < kWH; ++hn) {
+        const int64_t h = h0 + wn * kWH + hn;
+        float bv[64];
+        int bk[64];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int c = mi * 16 + e;
-            const int k0 = lane & 31, k1 = 32 + (lane & 31);
-            bv[c] = (k0 < K) ? acc[mi][0][e] : __uint_as_float(0xFF800000u);   // -inf: beaten by any score
-            bk[c] = (k0 < K) ? k0 : 64;
-            const bool take = (k1 < K) & beats(acc[mi][1][e], k1, bv[c], bk[c]);
-            bv[c] = take ? acc[mi][1][e] : bv[c];
-            bk[c] = take ? k1 : bk[c];
+        for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int c = mi * 16 + e;
+                const int k0 = lane & 31, k1 = 32 + (lane & 31);
+                bv[c] = (k0 < K) ? acc[mi][2 * hn][e] : __uint_as_float(0xFF800000u);   // -inf: beaten by any score
+                bk[c] = (k0 < K) ? k0 : 64;
+                const bool take = (k1 < K) & beats(acc[mi][2 * hn + 1][e], k1, bv[c], bk[c]);
+                bv[c] = take ? acc[mi][2 * hn + 1][e] : bv[c];
+                bk[c] = take ? k1 : bk[c];
+            }
         }
-    }
 #pragma unroll
-    for (int st = 0; st < 5; ++st) {
-        const int m = 16 >> st;          // partner distance
-        const int n = 32 >> st;          // tokens kept after this exchange
-        const bool upper = (lane & m) != 0;
+        for (int st = 0; st < 5; ++st) {
+            const int m = 16 >> st;          // partner distance
+            const int n = 32 >> st;          // tokens kept after this exchange
+            const bool upper = (lane & m) != 0;
 #pragma unroll
-        for (int i = 0; i < n; ++i) {
-            // keep i (lower lane) or n + i (upper lane); send the other
-            const float sv = upper ? bv[i] : bv[n + i];
-            const int sk = upper ? bk[i] : bk[n + i];
-            float kv = upper ? bv[n + i] : bv[i];
-            int kk = upper ? bk[n + i] : bk[i];
-            const float ov = __shfl_xor(sv, m, 64);
-            const int ok = __shfl_xor(sk, m, 64);
-            const bool take = beats(ov, ok, kv, kk);
-            bv[i] = take ? ov : kv;
-            bk[i] = take ? ok : kk;
+            for (int i = 0; i < n; ++i) {
+                // keep i (lower lane) or n + i (upper lane); send the other
+                const float sv = upper ? bv[i] : bv[n + i];
+                const int sk = upper ? bk[i] : bk[n + i];
+                float kv = upper ? bv[n + i] : bv[i];
+                int kk = upper ? bk[n + i] : bk[i];
+                const float ov = __shfl_xor(sv, m, 64);
+                const int ok = __shfl_xor(sk, m, 64);
+                const bool take = beats(ov, ok, kv, kk);
+                bv[i] = take ? ov : kv;
+                bk[i] = take ? ok : kk;
+            }
         }
-    }
-    if (h < a.H) {
+        if (h < a.H) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int c = 2 * (lane & 31) + r, mi = c >> 4, e = c & 15;
-            const int64_t m = m0 + wm * 128 + mi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-            if (m < a.M) {
-                const int64_t b = m / a.L, t = m - b * a.L;
-                a.sel[(b * a.H + h) * a.L + t] = (int16_t)bk[r];
+            for (int r = 0; r < 2; ++r) {
+                const int c = 2 * (lane & 31) + r, mi = c >> 4, e = c & 15;
+                const int64_t m = m0 + wm * 128 + mi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (m < a.M) {
+                    const int64_t b = m / a.L, t = m - b * a.L;
+                    a.sel[(b * a.H + h) * a.L + t] = (int16_t)bk[r];
+                }
             }
         }
     }
