@@ -1,14 +1,17 @@
-"""Flash PD-SSM forward recurrence scan for AMD MI355X (gfx950).
+"""Flash PD-SSM recurrence scan for AMD MI355X (gfx950).
 
 The compute path is the C-ABI library ``libpdssm.so`` (hand-written HIP
 kernels, declared in ``include/pdssm.h``).  This module is a thin ctypes
 binding with the same function names: it only turns torch tensors into
 device pointers and the current HIP stream into a ``hipStream_t``.  Every
-step of the scan runs in the library's kernels; there is no fallback, and a
-missing library raises.
+step runs in the library's kernels; there is no fallback, and a missing
+library raises.
 
-Higher-level helpers (``scan``, ``select``, ``compose``) allocate outputs and
-the workspace with torch and call the C entry points.
+Higher-level helpers allocate outputs (and workspaces) with torch and call
+the C entry points: ``scan`` and ``scan_save`` (forward), ``scan_bwd``
+(gradients), ``router_select`` (router scores and their argmax),
+``dict_hardmax`` (index maps from dense matrices), ``decode_step`` (one
+recurrent step), ``select`` and ``compose`` (test exports).
 """
 from __future__ import annotations
 
