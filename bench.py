@@ -27,6 +27,7 @@ METRIC = "scanned tokens/sec (B·H·L) and achieved HBM GB/s vs peak, N=64 L=409
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 ROUTER_D = 2048                  # router input features per token
+MALL_BYTES = 256 << 20           # MI355X last-level cache (Infinity Cache)
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "scan_kernel_lm_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "structured_sparse_state_amd", "csrc", f)
                   for f in ("pdssm_scan.hip", "pdssm_device.h")]
@@ -49,10 +50,11 @@ def algorithmic_bytes(inp, y, xf) -> int:
     return n
 
 
-def counter_traffic(bytes_per_call: int):
-    """HBM bytes per call from the committed rocprofv3 counter summary, or
-    None when the kernel sources changed since the counters were taken."""
-    if not os.path.exists(COUNTERS_FILE):
+def counter_traffic(bytes_per_call: int, workload: str):
+    """HBM bytes per call from the committed rocprofv3 counter summary (taken
+    on the LM workload), or None for another workload or when the kernel
+    sources changed since the counters were taken."""
+    if workload != "lm" or not os.path.exists(COUNTERS_FILE):
         return None
     vals = {}
     for line in open(COUNTERS_FILE):
@@ -209,6 +211,9 @@ def main() -> int:
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the timings reported beside the forward (backward scan, dictionary "
                          "pre-compute, decode step)")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="input sets cycled through by the timed calls (0: enough sets to be "
+                         "twice the 256 MB last-level cache, at most 8)")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle over the batch for at least this long")
@@ -231,12 +236,19 @@ def main() -> int:
     xf = torch.empty((B, H, N, 2) if inp.complex else (B, H, N), device=dev, dtype=torch.float32)
     ws = pk.workspace_for(inp)
     stream = torch.cuda.current_stream()
+    # Inputs small enough to stay in the last-level cache (MALL) between calls
+    # are timed over several seeded sets in turn, so that every call reads
+    # them from HBM.
+    nrot = args.rotate if args.rotate > 0 else min(8, max(1, -(-2 * MALL_BYTES // inp.input_bytes())))
+    sets = [inp] + [gen.make_inputs(args.workload, device=dev, seed=1000 + i) for i in range(1, nrot)]
+    calls = [0]
 
     def step():
-        pk.scan(inp, workspace=ws, y=y, x_final=xf, stream=stream)
+        pk.scan(sets[calls[0] % nrot], workspace=ws, y=y, x_final=xf, stream=stream)
+        calls[0] += 1
 
-    print(f"[bench] workload {args.workload}: B={B} H={H} L={L} N={N} K={K}; warmup {args.warmup}",
-          file=sys.stderr, flush=True)
+    print(f"[bench] workload {args.workload}: B={B} H={H} L={L} N={N} K={K}; {nrot} input set(s); "
+          f"warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -258,7 +270,7 @@ def main() -> int:
     alg_bytes = algorithmic_bytes(inp, y, xf)
     avg_call_s = sum(per_call_ms) / len(per_call_ms) * 1e-3
     achieved = alg_bytes / avg_call_s / 1e9
-    traffic = counter_traffic(alg_bytes)
+    traffic = counter_traffic(alg_bytes, args.workload)
     print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (min "
           f"{min(per_call_ms) * 1e3:.1f}), {achieved:.0f} GB/s algorithmic, wall {wall:.3f} s",
           file=sys.stderr, flush=True)
@@ -319,7 +331,8 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {cfgdesc}", "B": B, "H": H, "L": L, "N": N,
-                   "K": K, "global_batch": B * H, "seq_len": L, "parallelism": "single GPU"},
+                   "K": K, "global_batch": B * H, "seq_len": L, "parallelism": "single GPU",
+                   "input_sets": nrot},
         "achieved_GBps": achieved,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
