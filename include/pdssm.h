@@ -56,6 +56,14 @@
  * PDSSM_ERR_HIP runs on the host before any HIP call.  Element values are
  * preconditions: a selection outside [0,K) or a map entry outside [0,N) is
  * clamped into range on the device (no fault, result unspecified).
+ *
+ * Empty shapes: B, H and L may be 0 (N and K may not).  Sizes and flags are
+ * still checked.  With no sequences (B*H = 0) every buffer is empty: the
+ * call returns 0 and reads none of its pointers, which may be NULL.  With
+ * sequences of no steps (L = 0) the state after no steps is the initial one,
+ * so x_final = x0 (zero without x0) is written when x_final is given; every
+ * per-step buffer and the workspace are empty and not read.  Every entry
+ * point below follows the same rule for its own sizes.
  */
 #ifndef PDSSM_H
 #define PDSSM_H
@@ -84,7 +92,7 @@ extern "C" {
 /* status codes */
 #define PDSSM_OK 0
 #define PDSSM_ERR_NULL -1      /* a required pointer is NULL */
-#define PDSSM_ERR_DIM -2       /* B,H,L < 1, L > 2^30, N not in [1,64], K not in [1,32767], or too large */
+#define PDSSM_ERR_DIM -2       /* B,H,L < 0, L > 2^30, N not in [1,64], K not in [1,32767], or too large */
 #define PDSSM_ERR_FLAGS -3     /* unknown flag bits, or a mode the call does not take */
 #define PDSSM_ERR_ALIGN -4     /* a pointer is not 16-byte aligned */
 #define PDSSM_ERR_WORKSPACE -5 /* workspace smaller than the size function returns */
@@ -154,7 +162,9 @@ int pdssm_scan_fwd_save(const void *sel_or_logits, const int32_t *dict_idx, cons
  *   c (bf16, rounded to nearest even, with PDSSM_BC_BF16, else fp32), gd in
  *   the storage of diag, gx0 fp32 [B,H,N(,2)] or NULL when not wanted.
  * Arithmetic fp32 (complex fp32), any summation order.  Workspace sized by
- * pdssm_scan_bwd_workspace_bytes.  Errors as pdssm_scan_fwd.
+ * pdssm_scan_bwd_workspace_bytes.  Errors and empty shapes as
+ * pdssm_scan_fwd; with L = 0, gx0 = gx_final (zero without it) is written
+ * when gx0 is given.
  */
 int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
                    const void *b, const void *c, const void *x_chunks, const void *gy,
@@ -163,7 +173,7 @@ int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx, const voi
                    size_t workspace_bytes, hipStream_t stream);
 
 /* Workspace bytes pdssm_scan_bwd needs (O(B*H*L*N/16), never N*N*L); 0 when
- * the arguments are invalid. */
+ * the arguments are invalid (a positive size for valid empty shapes). */
 size_t pdssm_scan_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K,
                                       uint32_t flags);
 
@@ -180,9 +190,9 @@ size_t pdssm_scan_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int32_t N
  *             flags = PDSSM_LOGITS_F32, bf16 with PDSSM_LOGITS_BF16 (no other
  *             bits); device pointer, 16-byte aligned
  *   dict_idx  int32 [H,K,N] output, device pointer, 16-byte aligned
- * Errors: PDSSM_ERR_NULL, PDSSM_ERR_DIM (H < 1, N not in [1,64], K not in
- * [1,32767]), PDSSM_ERR_FLAGS, PDSSM_ERR_ALIGN, PDSSM_ERR_HIP.  Asynchronous
- * on stream; allocates nothing.
+ * Errors: PDSSM_ERR_NULL, PDSSM_ERR_DIM (H < 0, N not in [1,64], K not in
+ * [1,32767]), PDSSM_ERR_FLAGS, PDSSM_ERR_ALIGN, PDSSM_ERR_HIP; H = 0 writes
+ * nothing.  Asynchronous on stream; allocates nothing.
  */
 int pdssm_dict_hardmax(const void *m, int32_t *dict_idx, int64_t H, int32_t K, int32_t N,
                        uint32_t flags, hipStream_t stream);
@@ -201,8 +211,9 @@ int pdssm_dict_hardmax(const void *m, int32_t *dict_idx, int64_t H, int32_t K, i
  *   x              fp32 [B,H,N(,2)] state, read and overwritten in place
  *   flags          as pdssm_scan_fwd
  * Arithmetic fp32; collisions of pi sum in any order.  All pointers are
- * device pointers, 16-byte aligned, not NULL.  Errors as pdssm_scan_fwd
- * (no workspace).  Asynchronous on stream; allocates nothing.
+ * device pointers, 16-byte aligned, not NULL (unless B*H = 0, which writes
+ * nothing).  Errors as pdssm_scan_fwd (no workspace).  Asynchronous on
+ * stream; allocates nothing.
  */
 int pdssm_decode_step(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
                       const void *b, const void *c, void *y, void *x, int64_t B, int64_t H,
@@ -221,7 +232,8 @@ int pdssm_decode_step(const void *sel_or_logits, const int32_t *dict_idx, const 
  *   u        bf16 [B,L,D] step inputs
  *   w        bf16 [H,K,D] router weights
  *   sel_out  int16 [B,H,L] output
- *   K in [1,64]; D a positive multiple of 32; flags must be 0.
+ *   K in [1,64]; D a positive multiple of 32; flags must be 0.  B, L or H
+ *   may be 0: nothing is read or written then.
  * The scores are fp32 sums in an unspecified order: where two scores are
  * within their rounding error of each other, either index may be returned.
  * All pointers are device pointers, 16-byte aligned.  Errors:
@@ -248,7 +260,9 @@ int pdssm_select(const void *sel_or_logits, int32_t *sel_out, int64_t B, int64_t
  *   pi_out  int32 [B,H,N]
  *   d_out   fp32  [B,H,N], or [B,H,N,2] with PDSSM_COMPLEX
  * flags: selection bits and PDSSM_COMPLEX.  The workspace is sized by
- * pdssm_scan_workspace_bytes with the same arguments.
+ * pdssm_scan_workspace_bytes with the same arguments.  With L = 0 the
+ * product is the identity (pi_out[j] = j, d_out[j] = 1), written without
+ * reading the inputs or the workspace.
  */
 int pdssm_compose(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
                   int32_t *pi_out, void *d_out, int64_t B, int64_t H, int64_t L, int32_t N,

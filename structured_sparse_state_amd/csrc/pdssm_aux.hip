@@ -154,14 +154,16 @@ using namespace pdssm;
 extern "C" int pdssm_dict_hardmax(const void *m, int32_t *dict_idx, int64_t H, int32_t K, int32_t N,
                                   uint32_t flags, hipStream_t stream)
 {
-    if (!m || !dict_idx)
-        return PDSSM_ERR_NULL;
     const int rc = check_dims(1, H, 1, N, K);
     if (rc != PDSSM_OK)
         return rc;
     const uint32_t mode = flags & PDSSM_SEL_MASK;
     if ((flags & ~PDSSM_SEL_MASK) || (mode != PDSSM_LOGITS_F32 && mode != PDSSM_LOGITS_BF16))
         return PDSSM_ERR_FLAGS;
+    if (H == 0)
+        return PDSSM_OK;
+    if (!m || !dict_idx)
+        return PDSSM_ERR_NULL;
     if (!aligned16(m) || !aligned16(dict_idx))
         return PDSSM_ERR_ALIGN;
     const int64_t mats = H * (int64_t)K;
@@ -177,13 +179,15 @@ extern "C" int pdssm_decode_step(const void *sel_or_logits, const int32_t *dict_
                                  const void *b, const void *c, void *y, void *x, int64_t B, int64_t H,
                                  int32_t N, int32_t K, uint32_t flags, hipStream_t stream)
 {
-    if (!sel_or_logits || !dict_idx || !diag || !b || !c || !y || !x)
-        return PDSSM_ERR_NULL;
     const int rc = check_dims(B, H, 1, N, K);
     if (rc != PDSSM_OK)
         return rc;
     if (flags & ~PDSSM_FLAGS_ALL)
         return PDSSM_ERR_FLAGS;
+    if (B == 0 || H == 0)
+        return PDSSM_OK;
+    if (!sel_or_logits || !dict_idx || !diag || !b || !c || !y || !x)
+        return PDSSM_ERR_NULL;
     const void *ptrs[] = {sel_or_logits, dict_idx, diag, b, c, y, x};
     for (const void *p : ptrs)
         if (!aligned16(p))

@@ -692,7 +692,9 @@ extern "C" size_t pdssm_scan_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L
 {
     if (check_dims(B, H, L, N, K) != PDSSM_OK || (flags & ~PDSSM_FLAGS_ALL))
         return 0;
-    return (size_t)bwd_layout(B, H, L, K).total;
+    // Never 0 (which means invalid arguments), also for empty shapes.
+    const int64_t total = bwd_layout(B, H, L, K).total;
+    return (size_t)(total > 256 ? total : 256);
 }
 
 extern "C" int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
@@ -701,14 +703,24 @@ extern "C" int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx
                               int64_t B, int64_t H, int64_t L, int32_t N, int32_t K, uint32_t flags,
                               void *workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    if (!sel_or_logits || !dict_idx || !diag || !b || !c || !x_chunks || !gy || !gb || !gc || !gd ||
-        !workspace)
-        return PDSSM_ERR_NULL;
     int rc = check_dims(B, H, L, N, K);
     if (rc != PDSSM_OK)
         return rc;
     if (flags & ~PDSSM_FLAGS_ALL)
         return PDSSM_ERR_FLAGS;
+    if (B == 0 || H == 0)
+        return PDSSM_OK;   // no sequences: nothing to read or write
+    if (L == 0) {
+        // No steps: x_final = x0, so gx0 = gx_final (or zero).
+        if (!gx0)
+            return PDSSM_OK;
+        if (!aligned16(gx0) || (gx_final && !aligned16(gx_final)))
+            return PDSSM_ERR_ALIGN;
+        return launch_state_fill(gx_final, gx0, B * H * N * ((flags & PDSSM_COMPLEX) ? 2 : 1), stream);
+    }
+    if (!sel_or_logits || !dict_idx || !diag || !b || !c || !x_chunks || !gy || !gb || !gc || !gd ||
+        !workspace)
+        return PDSSM_ERR_NULL;
     const void *ptrs[] = {sel_or_logits, dict_idx, diag, b, c, x_chunks, gy, gx_final, gb, gc, gd, gx0,
                           workspace};
     for (const void *p : ptrs)

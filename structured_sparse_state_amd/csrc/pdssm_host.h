@@ -13,5 +13,8 @@ __attribute__((visibility("hidden"))) bool aligned16(const void *p);
 __attribute__((visibility("hidden"))) int check_dims(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K);
 // PDSSM_OK for hipSuccess, else PDSSM_ERR_HIP (the HIP text goes to pdssm_strerror).
 __attribute__((visibility("hidden"))) int hip_status(hipError_t e);
+// dst[0..n) = src[0..n) (fp32), or zeros when src is NULL, on stream; nothing when n <= 0.
+__attribute__((visibility("hidden"))) int launch_state_fill(const void *src, void *dst, int64_t n,
+                                                            hipStream_t stream);
 
 }  // namespace pdssm

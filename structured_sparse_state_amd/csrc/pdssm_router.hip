@@ -298,9 +298,7 @@ using namespace pdssm;
 extern "C" int pdssm_router_select(const void *u, const void *w, int16_t *sel_out, int64_t B, int64_t L,
                                    int64_t H, int32_t K, int32_t D, uint32_t flags, hipStream_t stream)
 {
-    if (!u || !w || !sel_out)
-        return PDSSM_ERR_NULL;
-    if (B < 1 || L < 1 || H < 1 || K < 1 || K > 64 || D < kRK || (D % kRK) != 0)
+    if (B < 0 || L < 0 || H < 0 || K < 1 || K > 64 || D < kRK || (D % kRK) != 0)
         return PDSSM_ERR_DIM;
     const double tokens = (double)B * (double)L;
     const double m_tiles = (tokens + kRM - 1) / kRM, h_tiles = (double)((H + kRH - 1) / kRH);
@@ -308,6 +306,10 @@ extern "C" int pdssm_router_select(const void *u, const void *w, int16_t *sel_ou
         return PDSSM_ERR_DIM;
     if (flags != 0)
         return PDSSM_ERR_FLAGS;
+    if (B == 0 || L == 0 || H == 0)
+        return PDSSM_OK;   // no tokens or no heads: nothing to write
+    if (!u || !w || !sel_out)
+        return PDSSM_ERR_NULL;
     if (!aligned16(u) || !aligned16(w) || !aligned16(sel_out))
         return PDSSM_ERR_ALIGN;
     RouterArgs a;

@@ -1203,6 +1203,37 @@ __global__ void __launch_bounds__(64) compose_final_kernel(ComposeArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Sequences of no steps.  The state after zero steps is the initial one, and
+// the product of no step operators is the identity (pi[j] = j, d[j] = 1).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) state_fill_kernel(const float *src, float *dst, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        dst[i] = src ? src[i] : 0.f;
+}
+
+__global__ void __launch_bounds__(256) identity_op_kernel(int32_t *pi, float *d, int64_t n, int N, int nc)
+{
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) {
+        pi[e] = (int32_t)(e % N);
+        d[e * nc] = 1.f;
+        if (nc == 2)
+            d[e * nc + 1] = 0.f;
+    }
+}
+
+static unsigned fill_blocks(int64_t n) { return (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096); }
+
+int launch_state_fill(const void *src, void *dst, int64_t n, hipStream_t stream)
+{
+    if (n <= 0)
+        return PDSSM_OK;
+    hipLaunchKernelGGL(state_fill_kernel, dim3(fill_blocks(n)), dim3(256), 0, stream,
+                       static_cast<const float *>(src), static_cast<float *>(dst), n);
+    return hip_status(hipGetLastError());
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 static thread_local std::string g_err;
@@ -1217,11 +1248,11 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 int check_dims(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K)
 {
-    if (B < 1 || H < 1 || L < 1 || L > kMaxL || N < 1 || N > 64 || K < 1 || K > 32767)
+    if (B < 0 || H < 0 || L < 0 || L > kMaxL || N < 1 || N > 64 || K < 1 || K > 32767)
         return PDSSM_ERR_DIM;
     // Element counts must fit int64 and tile tickets a uint32.
     const double steps = (double)B * (double)H * (double)L;
-    if (steps * 64.0 * 8.0 > 9.0e18)
+    if (steps * 64.0 * 8.0 > 9.0e18 || (double)B * (double)H * 64.0 * 8.0 > 9.0e18)
         return PDSSM_ERR_DIM;
     const int NP = pad_states(N);
     const int64_t n_tiles = (L + scan_tile_steps(NP) - 1) / scan_tile_steps(NP);
@@ -1344,18 +1375,28 @@ extern "C" size_t pdssm_scan_workspace_bytes(int64_t B, int64_t H, int64_t L, in
 static int scan_fwd(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
                     const void *b, const void *c, void *y, void *x_final, int64_t B, int64_t H,
                     int64_t L, int32_t N, int32_t K, uint32_t flags, const void *x0,
-                    void *workspace, size_t workspace_bytes, void *x_chunks, int16_t *sel_save,
-                    hipStream_t stream)
+                    void *workspace, size_t workspace_bytes, bool save, void *x_chunks,
+                    int16_t *sel_save, hipStream_t stream)
 {
-    if (!sel_or_logits || !dict_idx || !diag || !b || !c || !y || !workspace)
-        return PDSSM_ERR_NULL;
-    if ((x_chunks && !aligned16(x_chunks)) || (sel_save && !aligned16(sel_save)))
-        return PDSSM_ERR_ALIGN;
     int rc = check_dims(B, H, L, N, K);
     if (rc != PDSSM_OK)
         return rc;
     if (flags & ~PDSSM_FLAGS_ALL)
         return PDSSM_ERR_FLAGS;
+    if (B == 0 || H == 0)
+        return PDSSM_OK;   // no sequences: nothing to read or write
+    if (L == 0) {
+        // No steps: x_final = x0 (or zero); every other buffer is empty.
+        if (!x_final)
+            return PDSSM_OK;
+        if (!aligned16(x_final) || (x0 && !aligned16(x0)))
+            return PDSSM_ERR_ALIGN;
+        return launch_state_fill(x0, x_final, B * H * N * ((flags & PDSSM_COMPLEX) ? 2 : 1), stream);
+    }
+    if (!sel_or_logits || !dict_idx || !diag || !b || !c || !y || !workspace || (save && !x_chunks))
+        return PDSSM_ERR_NULL;
+    if ((x_chunks && !aligned16(x_chunks)) || (sel_save && !aligned16(sel_save)))
+        return PDSSM_ERR_ALIGN;
     const void *ptrs[] = {sel_or_logits, dict_idx, diag, b, c, y, x_final, x0, workspace};
     for (const void *p : ptrs)
         if (p && !aligned16(p))
@@ -1424,7 +1465,7 @@ extern "C" int pdssm_scan_fwd(const void *sel_or_logits, const int32_t *dict_idx
                               hipStream_t stream)
 {
     return scan_fwd(sel_or_logits, dict_idx, diag, b, c, y, x_final, B, H, L, N, K, flags, x0,
-                    workspace, workspace_bytes, nullptr, nullptr, stream);
+                    workspace, workspace_bytes, false, nullptr, nullptr, stream);
 }
 
 extern "C" int pdssm_scan_fwd_save(const void *sel_or_logits, const int32_t *dict_idx,
@@ -1434,22 +1475,22 @@ extern "C" int pdssm_scan_fwd_save(const void *sel_or_logits, const int32_t *dic
                                    const void *x0, void *workspace, size_t workspace_bytes,
                                    hipStream_t stream)
 {
-    if (!x_chunks)
-        return PDSSM_ERR_NULL;
     return scan_fwd(sel_or_logits, dict_idx, diag, b, c, y, x_final, B, H, L, N, K, flags, x0,
-                    workspace, workspace_bytes, x_chunks, sel_out, stream);
+                    workspace, workspace_bytes, true, x_chunks, sel_out, stream);
 }
 
 extern "C" int pdssm_select(const void *sel_or_logits, int32_t *sel_out, int64_t B, int64_t H,
                             int64_t L, int32_t K, uint32_t flags, hipStream_t stream)
 {
-    if (!sel_or_logits || !sel_out)
-        return PDSSM_ERR_NULL;
     int rc = check_dims(B, H, L, 1, K);
     if (rc != PDSSM_OK)
         return rc;
     if (flags & ~PDSSM_SEL_MASK)
         return PDSSM_ERR_FLAGS;
+    if (B == 0 || H == 0 || L == 0)
+        return PDSSM_OK;
+    if (!sel_or_logits || !sel_out)
+        return PDSSM_ERR_NULL;
     if (!aligned16(sel_or_logits) || !aligned16(sel_out))
         return PDSSM_ERR_ALIGN;
     const int64_t steps = B * H * L;
@@ -1466,13 +1507,26 @@ extern "C" int pdssm_compose(const void *sel_or_logits, const int32_t *dict_idx,
                              int32_t N, int32_t K, uint32_t flags, void *workspace,
                              size_t workspace_bytes, hipStream_t stream)
 {
-    if (!sel_or_logits || !dict_idx || !diag || !pi_out || !d_out || !workspace)
-        return PDSSM_ERR_NULL;
     int rc = check_dims(B, H, L, N, K);
     if (rc != PDSSM_OK)
         return rc;
     if (flags & ~(PDSSM_SEL_MASK | PDSSM_COMPLEX))
         return PDSSM_ERR_FLAGS;
+    if (B == 0 || H == 0)
+        return PDSSM_OK;
+    if (L == 0) {
+        // The product of no steps: the identity.
+        if (!pi_out || !d_out)
+            return PDSSM_ERR_NULL;
+        if (!aligned16(pi_out) || !aligned16(d_out))
+            return PDSSM_ERR_ALIGN;
+        const int64_t n = B * H * N;
+        hipLaunchKernelGGL(identity_op_kernel, dim3(fill_blocks(n)), dim3(256), 0, stream, pi_out,
+                           static_cast<float *>(d_out), n, (int)N, (flags & PDSSM_COMPLEX) ? 2 : 1);
+        return hip_status(hipGetLastError());
+    }
+    if (!sel_or_logits || !dict_idx || !diag || !pi_out || !d_out || !workspace)
+        return PDSSM_ERR_NULL;
     const void *ptrs[] = {sel_or_logits, dict_idx, diag, pi_out, d_out, workspace};
     for (const void *p : ptrs)
         if (!aligned16(p))
@@ -1511,7 +1565,7 @@ extern "C" const char *pdssm_strerror(int status)
     switch (status) {
     case PDSSM_OK: return "success";
     case PDSSM_ERR_NULL: return "a required pointer is NULL";
-    case PDSSM_ERR_DIM: return "invalid sizes (B,H,L >= 1, N in [1,64], K in [1,32767])";
+    case PDSSM_ERR_DIM: return "invalid sizes (B,H,L >= 0, N in [1,64], K in [1,32767])";
     case PDSSM_ERR_FLAGS: return "invalid flags";
     case PDSSM_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case PDSSM_ERR_WORKSPACE: return "workspace too small";

@@ -532,7 +532,38 @@ def pin_router_select(orc):
     assert np.array_equal(orc.router_select(u, w), ref)
 
 
+def pin_empty_sequences(orc):
+    """Degenerate sizes.  With no steps the state is the initial one and the
+    product of no step operators is the identity, so x_final = x0 (zero
+    without x0), compose gives pi[j] = j with d[j] = 1, and the gradient of
+    x_final passes straight to x0; with no sequences every output is empty."""
+    for complex_ in (False, True):
+        name = "lm" if complex_ else "small"
+        inp = gen.make_inputs(name, B=2, H=3, L=0, with_x0=True, seed=77)
+        x0 = _to_f64(inp.x0)
+        if complex_:
+            x0 = x0[..., 0] + 1j * x0[..., 1]
+        y, xf = orc.scan_inputs(inp)
+        assert y.shape == (2, 3, 0) and np.array_equal(xf, x0)
+        _, xf0 = orc.scan_inputs(inp, x0=None)
+        assert np.array_equal(xf0, np.zeros_like(x0))
+        pi, d = orc.compose_inputs(inp)
+        assert np.array_equal(pi, np.broadcast_to(np.arange(inp.N, dtype=np.int32), (2, 3, inp.N)))
+        assert np.array_equal(d, np.ones_like(d))
+        gxf = np.random.default_rng(3).standard_normal(x0.shape)
+        if complex_:
+            gxf = gxf + 1j * np.random.default_rng(4).standard_normal(x0.shape)
+        gb, gc, gd, gx0 = orc.scan_bwd(inp.sel_or_logits, inp.sel_mode, inp.dict_idx, inp.diag, inp.b,
+                                       inp.c, np.zeros((2, 3, 0)), complex=complex_,
+                                       bc_bf16=inp.bc_bf16, x0=inp.x0, gxf=gxf)
+        assert gb.size == gc.size == gd.size == 0 and np.array_equal(gx0, gxf)
+        for B, H in ((0, 3), (2, 0)):
+            e = gen.make_inputs(name, B=B, H=H, L=5, with_x0=True, seed=78)
+            y, xf = orc.scan_inputs(e)
+            assert y.size == 0 and xf.size == 0
+
+
 ALL_PINS = [pin_hand_examples, pin_select_argmax, pin_dense_products, pin_compose_dense, pin_fsa,
             pin_diagonal_closed_form, pin_permutation_invariants, pin_superposition,
             pin_segment_chaining, pin_bwd_autograd, pin_bwd_finite_differences, pin_dict_hardmax,
-            pin_router_select]
+            pin_router_select, pin_empty_sequences]

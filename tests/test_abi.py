@@ -54,8 +54,8 @@ def _scan(**kw):
 def test_scan_argument_errors(lib):
     for name in ("sel", "dict_idx", "diag", "b", "c", "y", "ws"):
         assert _scan(**{name: None}) == pk.PDSSM_ERR_NULL, name
-    for bad in (dict(B=0), dict(H=-1), dict(L=0), dict(N=0), dict(N=65), dict(K=0),
-                dict(K=32768), dict(B=1 << 40, H=1 << 20)):
+    for bad in (dict(B=-1), dict(H=-1), dict(L=-1), dict(N=0), dict(N=65), dict(K=0),
+                dict(K=32768), dict(B=1 << 40, H=1 << 20), dict(B=1 << 40, H=1 << 20, L=0)):
         assert _scan(**bad) == pk.PDSSM_ERR_DIM, bad
     assert _scan(flags=0x20) == pk.PDSSM_ERR_FLAGS
     for name in ("sel", "dict_idx", "diag", "b", "c", "y", "ws", "x0", "x_final"):
@@ -64,9 +64,47 @@ def test_scan_argument_errors(lib):
     assert _scan(ws_bytes=need - 1) == pk.PDSSM_ERR_WORKSPACE
 
 
+def test_empty_shapes_need_no_buffers(lib):
+    """No sequences, or sequences of no steps, are valid calls with nothing to
+    compute: every buffer is empty, so any pointer (NULL included) is taken
+    and nothing is launched.  (With no steps and an x_final buffer the call
+    writes x_final = x0; that case runs on the GPU.)"""
+    none = dict(sel=None, dict_idx=None, diag=None, b=None, c=None, y=None, ws=None, ws_bytes=0)
+    for shape in (dict(B=0), dict(H=0), dict(B=0, H=0, L=0), dict(L=0)):
+        assert _scan(**none, **shape) == pk.PDSSM_OK, shape
+    assert _scan(**none, L=0, x_final=FAKE + 4) == pk.PDSSM_ERR_ALIGN
+    assert _scan(**none, L=0, x_final=FAKE, x0=FAKE + 4) == pk.PDSSM_ERR_ALIGN
+    s = pk.pdssm_scan_fwd_save
+    for B, H, L in ((0, 3, 100), (2, 0, 100), (2, 3, 0)):
+        assert s(None, None, None, None, None, None, None, None, None, B, H, L, 16, 8, 0, None, None,
+                 0, 0) == pk.PDSSM_OK
+        assert _bwd(sel=None, dict_idx=None, diag=None, b=None, c=None, xch=None, gy=None, gb=None,
+                    gc=None, gd=None, ws=None, ws_bytes=0, B=B, H=H, L=L) == pk.PDSSM_OK
+        assert pk.pdssm_select(None, None, B, H, L, 4, 0, 0) == pk.PDSSM_OK
+        assert pk.pdssm_scan_workspace_bytes(B, H, L, 16, 8, 0) > 0
+        assert pk.pdssm_scan_bwd_workspace_bytes(B, H, L, 16, 8, 0) > 0
+    for B, H in ((0, 3), (2, 0)):
+        assert pk.pdssm_compose(None, None, None, None, None, B, H, 8, 4, 2, 0, None, 0,
+                                0) == pk.PDSSM_OK
+        assert _dec(sel=None, dict_idx=None, diag=None, b=None, c=None, y=None, x=None, B=B,
+                    H=H) == pk.PDSSM_OK
+    assert pk.pdssm_compose(FAKE, FAKE, FAKE, None, FAKE, 1, 1, 0, 4, 2, 0, None, 0,
+                            0) == pk.PDSSM_ERR_NULL
+    assert pk.pdssm_compose(FAKE, FAKE, FAKE, FAKE + 4, FAKE, 1, 1, 0, 4, 2, 0, None, 0,
+                            0) == pk.PDSSM_ERR_ALIGN
+    assert _bwd(L=0, gx0=FAKE + 4) == pk.PDSSM_ERR_ALIGN
+    assert pk.pdssm_dict_hardmax(None, None, 0, 4, 8, pk.PDSSM_LOGITS_F32, 0) == pk.PDSSM_OK
+    for B, L, H in ((0, 100, 3), (2, 0, 3), (2, 100, 0)):
+        assert pk.pdssm_router_select(None, None, None, B, L, H, 64, 256, 0, 0) == pk.PDSSM_OK
+    # the size and flag checks still apply to empty calls
+    assert _scan(**none, B=0, N=65) == pk.PDSSM_ERR_DIM
+    assert _scan(**none, B=0, flags=0x20) == pk.PDSSM_ERR_FLAGS
+    assert pk.pdssm_router_select(None, None, None, 0, 100, 3, 64, 48, 0, 0) == pk.PDSSM_ERR_DIM
+
+
 def test_select_and_compose_argument_errors(lib):
     assert pk.pdssm_select(None, FAKE, 1, 1, 1, 4, 0, 0) == pk.PDSSM_ERR_NULL
-    assert pk.pdssm_select(FAKE, FAKE, 1, 1, 0, 4, 0, 0) == pk.PDSSM_ERR_DIM
+    assert pk.pdssm_select(FAKE, FAKE, 1, 1, -1, 4, 0, 0) == pk.PDSSM_ERR_DIM
     assert pk.pdssm_select(FAKE, FAKE, 1, 1, 1, 4, pk.PDSSM_COMPLEX, 0) == pk.PDSSM_ERR_FLAGS
     assert pk.pdssm_select(FAKE + 2, FAKE, 1, 1, 1, 4, 0, 0) == pk.PDSSM_ERR_ALIGN
     c = pk.pdssm_compose
@@ -91,7 +129,7 @@ def test_workspace_is_linear_in_length_not_quadratic_in_state(lib):
     assert ws(8, 32, 4096, 32) <= base
     inputs = 8 * 32 * 4096 * (64 * 8 + 64 * 4 * 2 + 64 * 2)
     assert base < 0.03 * inputs
-    assert pk.pdssm_scan_workspace_bytes(0, 1, 1, 1, 1, 0) == 0
+    assert pk.pdssm_scan_workspace_bytes(-1, 1, 1, 1, 1, 0) == 0
     assert pk.pdssm_scan_workspace_bytes(1, 1, 1, 1, 1, 0x40) == 0
 
 
@@ -109,7 +147,7 @@ def _bwd(**kw):
 def test_bwd_and_save_argument_errors(lib):
     for name in ("sel", "dict_idx", "diag", "b", "c", "xch", "gy", "gb", "gc", "gd", "ws"):
         assert _bwd(**{name: None}) == pk.PDSSM_ERR_NULL, name
-    for bad in (dict(B=0), dict(L=0), dict(N=65), dict(K=0)):
+    for bad in (dict(B=-1), dict(L=-1), dict(N=65), dict(K=0)):
         assert _bwd(**bad) == pk.PDSSM_ERR_DIM, bad
     assert _bwd(flags=0x20) == pk.PDSSM_ERR_FLAGS
     for name in ("sel", "diag", "xch", "gy", "gxf", "gb", "gd", "gx0", "ws"):
@@ -117,7 +155,7 @@ def test_bwd_and_save_argument_errors(lib):
     need = pk.pdssm_scan_bwd_workspace_bytes(2, 3, 100, 16, 8, pk.PDSSM_LOGITS_BF16)
     assert need > 0
     assert _bwd(ws_bytes=need - 1) == pk.PDSSM_ERR_WORKSPACE
-    assert pk.pdssm_scan_bwd_workspace_bytes(0, 1, 1, 1, 1, 0) == 0
+    assert pk.pdssm_scan_bwd_workspace_bytes(-1, 1, 1, 1, 1, 0) == 0
     s = pk.pdssm_scan_fwd_save
     assert s(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, 2, 3, 100, 16, 8, 0, None, FAKE,
              1 << 40, 0) == pk.PDSSM_ERR_NULL
@@ -140,7 +178,7 @@ def test_dict_hardmax_argument_errors(lib):
     f = pk.PDSSM_LOGITS_F32
     assert h(None, FAKE, 2, 4, 8, f, 0) == pk.PDSSM_ERR_NULL
     assert h(FAKE, None, 2, 4, 8, f, 0) == pk.PDSSM_ERR_NULL
-    for H, K, N in ((0, 4, 8), (2, 0, 8), (2, 4, 0), (2, 4, 65), (2, 32768, 8)):
+    for H, K, N in ((-1, 4, 8), (2, 0, 8), (2, 4, 0), (2, 4, 65), (2, 32768, 8)):
         assert h(FAKE, FAKE, H, K, N, f, 0) == pk.PDSSM_ERR_DIM, (H, K, N)
     for bad in (pk.PDSSM_SEL_I32, pk.PDSSM_SEL_I16, f | pk.PDSSM_COMPLEX):
         assert h(FAKE, FAKE, 2, 4, 8, bad, 0) == pk.PDSSM_ERR_FLAGS, bad
@@ -160,7 +198,7 @@ def _dec(**kw):
 def test_decode_argument_errors(lib):
     for name in ("sel", "dict_idx", "diag", "b", "c", "y", "x"):
         assert _dec(**{name: None}) == pk.PDSSM_ERR_NULL, name
-    for bad in (dict(B=0), dict(H=0), dict(N=0), dict(N=65), dict(K=0), dict(K=40000)):
+    for bad in (dict(B=-1), dict(H=-1), dict(N=0), dict(N=65), dict(K=0), dict(K=40000)):
         assert _dec(**bad) == pk.PDSSM_ERR_DIM, bad
     assert _dec(flags=0x20) == pk.PDSSM_ERR_FLAGS
     for name in ("sel", "dict_idx", "diag", "b", "c", "y", "x"):
@@ -171,7 +209,7 @@ def test_router_argument_errors(lib):
     r = pk.pdssm_router_select
     assert r(None, FAKE, FAKE, 2, 100, 3, 64, 256, 0, 0) == pk.PDSSM_ERR_NULL
     assert r(FAKE, FAKE, None, 2, 100, 3, 64, 256, 0, 0) == pk.PDSSM_ERR_NULL
-    for B, L, H, K, D in ((0, 100, 3, 64, 256), (2, 0, 3, 64, 256), (2, 100, 0, 64, 256),
+    for B, L, H, K, D in ((-1, 100, 3, 64, 256), (2, -1, 3, 64, 256), (2, 100, -1, 64, 256),
                           (2, 100, 3, 0, 256), (2, 100, 3, 65, 256), (2, 100, 3, 64, 0),
                           (2, 100, 3, 64, 48), (2, 100, 3, 64, 16)):
         assert r(FAKE, FAKE, FAKE, B, L, H, K, D, 0, 0) == pk.PDSSM_ERR_DIM, (B, L, H, K, D)
