@@ -125,6 +125,25 @@ def _event_time(fn, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps * 1e-3
 
 
+def measure_hbm_practical(nbytes: int, stream):
+    """What plain streaming kernels reach on this GPU over the same number of
+    bytes (context for the roofline fraction, whose peak stays 8 TB/s):
+    torch's row sums (read only) and an elementwise add (read + write)."""
+    import torch
+    n = (nbytes // 4) // 1024 * 1024
+    x = torch.randn(n, device="cuda:0")
+    y = torch.empty_like(x)
+    rows = x.view(-1, 1024)
+    t_read = _event_time(lambda: rows.sum(dim=1), 20, 3, stream)
+    t_rw = _event_time(lambda: torch.add(x, 1.0, out=y), 20, 3, stream)
+    del x, y, rows
+    torch.cuda.empty_cache()
+    return {"read_GBps": n * 4 / t_read / 1e9, "read_write_GBps": 2 * n * 4 / t_rw / 1e9,
+            "bytes": n * 4,
+            "note": "torch row sums (read) and elementwise add (read+write) over the same bytes "
+                    "as one scan call; the practical streaming rate on this GPU, for context"}
+
+
 def measure_aux(pk, gen, inp, stream):
     """The dictionary pre-compute and one decode step at the workload's
     shape, HIP events on the launch stream."""
@@ -210,7 +229,7 @@ def main() -> int:
                          "rocprofv3 byte counters can be scaled")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the timings reported beside the forward (backward scan, dictionary "
-                         "pre-compute, decode step)")
+                         "pre-compute, decode step, router, practical HBM rates)")
     ap.add_argument("--rotate", type=int, default=0,
                     help="input sets cycled through by the timed calls (0: enough sets to be "
                          "twice the 256 MB last-level cache, at most 8)")
@@ -286,6 +305,10 @@ def main() -> int:
 
     bwd = None if args.no_backward else measure_backward(pk, gen, inp, ws, stream, args)
     aux = None if args.no_backward else measure_aux(pk, gen, inp, stream)
+    hbm = None if args.no_backward else measure_hbm_practical(alg_bytes, stream)
+    if hbm:
+        print(f"[bench] practical HBM: read {hbm['read_GBps']:.0f} GB/s, read+write "
+              f"{hbm['read_write_GBps']:.0f} GB/s", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -340,6 +363,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "backward": bwd,
         "next_rows": aux,
+        "hbm_practical": hbm,
     }
     print(json.dumps(out))
     return 0

@@ -161,10 +161,13 @@ int pdssm_scan_fwd_save(const void *sel_or_logits, const int32_t *dict_idx, cons
  * Outputs (caller-owned, 16-byte aligned): gb and gc in the storage of b and
  *   c (bf16, rounded to nearest even, with PDSSM_BC_BF16, else fp32), gd in
  *   the storage of diag, gx0 fp32 [B,H,N(,2)] or NULL when not wanted.
- * Arithmetic fp32 (complex fp32), any summation order.  Workspace sized by
- * pdssm_scan_bwd_workspace_bytes.  Errors and empty shapes as
- * pdssm_scan_fwd; with L = 0, gx0 = gx_final (zero without it) is written
- * when gx0 is given.
+ * Arithmetic fp32 (complex fp32), any summation order: the adjoint carried
+ * between chunks of 16 steps is composed in an order that depends on timing,
+ * so repeated calls may differ in the last bits (and a bf16 output by one
+ * rounding step).  Workspace sized by pdssm_scan_bwd_workspace_bytes; as for
+ * pdssm_scan_fwd it may hold anything on entry, and two calls in flight at
+ * once need two workspaces.  Errors and empty shapes as pdssm_scan_fwd; with
+ * L = 0, gx0 = gx_final (zero without it) is written when gx0 is given.
  */
 int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
                    const void *b, const void *c, const void *x_chunks, const void *gy,
@@ -172,8 +175,10 @@ int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx, const voi
                    int64_t H, int64_t L, int32_t N, int32_t K, uint32_t flags, void *workspace,
                    size_t workspace_bytes, hipStream_t stream);
 
-/* Workspace bytes pdssm_scan_bwd needs (O(B*H*L*N/16), never N*N*L); 0 when
- * the arguments are invalid (a positive size for valid empty shapes). */
+/* Workspace bytes pdssm_scan_bwd needs: 3.5 KB (2 KB real) per 64 steps
+ * of every sequence (one carry record per 64 steps, O(B*H*L), never N*N*L),
+ * plus the dictionary's entry table; 0 when the arguments are invalid (a
+ * positive size for valid empty shapes). */
 size_t pdssm_scan_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K,
                                       uint32_t flags);
 

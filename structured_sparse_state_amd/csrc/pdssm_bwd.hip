@@ -24,12 +24,11 @@
 // gather form (M K)[j] = conj(dacc[j]) K[pacc[j]], with (pacc, dacc) the
 // forward path of source j through the chunk.  Its affine part is
 //     v_c[j] = sum_t gy_t conj(c_t[pacc_t[j]] dacc_t[j]),
-// a sum of the forward's own readout weights.  Three kernels:
-//   bwd_ops    per chunk, in parallel: (pacc, conj(dacc), v_c), by gathers.
-//   bwd_carry  per sequence: K_c for every chunk, right to left.
-//   bwd_grad   per chunk, in parallel: x over the chunk from the forward's
-//              saved carry-in (the forward's scatter step), then lambda back
-//              over it from K_c, writing gb, gc and gd.
+// a sum of the forward's own readout weights.  One kernel, bwd_fused, does
+// it all in one pass over the inputs: per chunk, (pacc, conj(dacc), v_c) and
+// x over the chunk (from the forward's saved carry-in), K_c by a decoupled
+// look-back over the chunks on its right, then lambda back over the chunk,
+// writing gb, gc and gd.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -43,7 +42,7 @@ namespace pdssm {
 constexpr int kBT = kCarryStride;   // steps per chunk (the forward saves one carry per chunk)
 constexpr int kBW = 4;              // chunk waves per workgroup
 #ifndef PDSSM_BWD_GRAD_D
-#define PDSSM_BWD_GRAD_D 4   // steps of input in flight per wave (gradient kernel)
+#define PDSSM_BWD_GRAD_D 4   // steps of b and c in flight per wave
 #endif
 
 struct BwdArgs {
@@ -60,42 +59,16 @@ struct BwdArgs {
     float *gd;          // storage of diag
     float *gx0;         // [S][N(,2)] or null
     const uint16_t *tab;   // [H][K][64] scatter entries (dict_entry)
-    int32_t *sig;       // [S*nch][64] composed map of each chunk
-    float4 *mv;         // [S*nch][64] (conj dacc, v)
-    float2 *kc;         // [S*nch][64] adjoint carried into each chunk's last step
-    int32_t *gsig;      // [S*ng][64] group operators (ng = ceil(nch / kGroup))
-    float4 *gmv;
-    float2 *gk;         // [S*ng][64] adjoint carried into each group's last chunk
-    int16_t *ksel;      // [S*L] selections picked by bwd_ops from logits (logits modes only)
+    Header *hdr;        // epoch and ticket counter
+    uint64_t *agg;      // [S*tiles][AW][64] each tile's adjoint operator, epoch-tagged words
+    uint64_t *incl;     // [S*tiles][NC][64] the adjoint each tile carries out of its first step
+    uint32_t total;     // tickets: S * tiles
+    int64_t tiles;      // tiles of kBW chunks per sequence
     int64_t H, L, S, nch;
     int N, K;
     uint32_t sel_mode;
     int y_bf16;
-    int idx32;          // chunk and sequence counts fit 31 bits: 32-bit index arithmetic
 };
-
-// Sequence and first step of chunk ch, and the sequence's head.  The
-// divisions are 32-bit when the counts allow (a 64-bit one costs a few
-// hundred instructions before the chunk's first load can go out).
-struct ChunkPos {
-    int64_t seq, t0, h;
-};
-__device__ __forceinline__ ChunkPos chunk_of(const BwdArgs &a, int64_t ch)
-{
-    ChunkPos p;
-    if (a.idx32) {
-        const uint32_t c = (uint32_t)ch, n = (uint32_t)a.nch;
-        const uint32_t sq = c / n;
-        p.seq = sq;
-        p.t0 = (int64_t)(c - sq * n) * kBT;
-        p.h = sq % (uint32_t)a.H;
-    } else {
-        p.seq = ch / a.nch;
-        p.t0 = (ch - p.seq * a.nch) * kBT;
-        p.h = p.seq % a.H;
-    }
-    return p;
-}
 
 template <bool CPLX>
 __device__ __forceinline__ void store_grad(float *p, int64_t e, cf v)
@@ -104,18 +77,6 @@ __device__ __forceinline__ void store_grad(float *p, int64_t e, cf v)
         reinterpret_cast<float2 *>(p)[e] = make_float2(v.r, v.i);
     else
         p[e] = v.r;
-}
-
-// ---------------------------------------------------------------------------
-// The scatter entries for 64 lanes (one wave per dictionary entry).
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) bwd_tab_kernel(const int32_t *dict, uint16_t *tab, int64_t entries, int N)
-{
-    const int64_t e = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e >= entries)
-        return;
-    const int lane = threadIdx.x & 63;
-    tab[e * 64 + lane] = dict_entry(dict + e * N, N, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -283,98 +244,15 @@ __device__ __forceinline__ typename std::conditional<CPLX, float2, float>::type 
 }
 
 // ---------------------------------------------------------------------------
-// bwd_ops: per chunk, lane j follows its forward path (pacc, dacc) through
-// the chunk and sums the adjoint's affine part v[j].
-// ---------------------------------------------------------------------------
-template <bool CPLX, bool BCBF>
-__global__ void __launch_bounds__(kBW * 64) bwd_ops_kernel(BwdArgs a)
-{
-    __shared__ int16_t s_sel[kBW][kBT];
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int64_t ch = (int64_t)blockIdx.x * kBW + wave;
-    if (ch >= a.S * a.nch)
-        return;
-    const ChunkPos cp = chunk_of(a, ch);
-    const int64_t seq = cp.seq, t0 = cp.t0, h = cp.h;
-    const int nv = (int)min((int64_t)kBT, a.L - t0);
-    // The chunk's d and c rows do not depend on the selection: all of them
-    // are in flight before the selections are used.
-    const bool idx = index_mode(a.sel_mode);
-    int kraw = 0;
-    if (idx)
-        kraw = sel_raw(a.sel, a.sel_mode, seq * a.L + t0, nv, lane);
-    const uint32_t gyr = chunk_gy_raw(a, seq * a.L + t0, nv, lane);
-    ChunkIO<CPLX, BCBF> io;
-    io.init(a, seq, t0, nv, h, lane);
-    using Raw = typename RawOf<CPLX, BCBF>::type;
-    cf rd[kBT];
-    Raw rc[kBT];
-#pragma unroll
-    for (int tt = 0; tt < kBT; ++tt) {
-        const int ts = min(tt, nv - 1);
-        rd[tt] = io.d(ts);
-        rc[tt] = io.raw_c(ts);
-    }
-    if (idx) {
-        sel_put(kraw, a.K, nv, s_sel[wave], lane);
-    } else {
-        wave_select<kBT>(a.sel, a.sel_mode, a.K, a.L, seq * a.L, t0, s_sel[wave], lane);
-        if (a.ksel && lane < nv)   // the gradient pass reads these instead of the K scores
-            a.ksel[seq * a.L + t0 + lane] = s_sel[wave][lane];
-    }
-    uint32_t re[kBT];
-#pragma unroll
-    for (int tt = 0; tt < kBT; ++tt)
-        re[tt] = io.ent(__builtin_amdgcn_readfirstlane((int)s_sel[wave][min(tt, nv - 1)]));
-    int pacc4 = lane * 4;
-    cf dacc = {1.f, 0.f}, v = {0.f, 0.f};
-#pragma unroll
-    for (int tt = 0; tt < kBT; ++tt) {
-        const cf d = rd[tt];
-        const Raw craw = rc[tt];
-        const uint32_t ent = re[tt];
-        if (tt < nv) {
-            const float g = gy_step(a, gyr, tt);
-            // pacc_t = pi_t[pacc_{t-1}], dacc_t = d_t[pacc_{t-1}] * dacc_{t-1}
-            const uint32_t np = bperm_a(ent & 63u, pacc4);
-            cf dd;
-            dd.r = bperm_a(d.r, pacc4);
-            dd.i = CPLX ? bperm_a(d.i, pacc4) : 0.f;
-            dacc = cmul(dd, dacc);
-            pacc4 = (int)(np << 2);
-            // readout weight g_t[j] = c_t[pacc_t[j]] dacc_t[j]; v += gy_t conj(g_t)
-            const cf cg = unpack_c<CPLX, BCBF>(bperm_raw<CPLX, BCBF>(craw, pacc4));
-            const cf w = cmul(cg, dacc);
-            v.r += g * w.r;
-            v.i -= g * w.i;
-        }
-    }
-    a.sig[ch * 64 + lane] = pacc4 >> 2;
-    a.mv[ch * 64 + lane] = make_float4(dacc.r, -dacc.i, v.r, v.i);
-}
-
-// ---------------------------------------------------------------------------
-// The carries K_c, right to left, in three shallow passes instead of one
-// chain over all chunks: compose each group of kGroup chunk operators (in
-// parallel), chain the group operators per sequence, then expand each group
-// from its carry.  An operator (sig, m, v) maps K to m[j] K[sig[j]] + v[j];
-// applying (sig1, m1, v1) after (sig2, m2, v2) -- the chunk on the left
-// after the one on its right -- gives
+// Adjoint chunk operators.  An operator (sig, m, v) maps K to
+// m[j] K[sig[j]] + v[j]; applying (sig1, m1, v1) after (sig2, m2, v2) -- the
+// chunk on the left after the one on its right -- gives
 //     sig = sig2[sig1],  m = m1 * m2[sig1],  v = m1 * v2[sig1] + v1.
 // ---------------------------------------------------------------------------
-constexpr int kGroup = 32;   // chunks per group
-
 struct GOp {
     int sig;
     cf m, v;
 };
-
-template <bool CPLX>
-__device__ __forceinline__ GOp load_op(const BwdArgs &a, const int32_t *sig, const float4 *mv, int64_t rec, int lane)
-{
-    const float4 q = mv[rec * 64 + lane];
-    return {sig[rec * 64 + lane], {q.x, CPLX ? q.y : 0.f}, {q.z, CPLX ? q.w : 0.f}};
-}
 
 // apply `left` after `right` (right = the operator of the chunks on the right)
 template <bool CPLX>
@@ -404,114 +282,81 @@ __device__ __forceinline__ cf apply_op(GOp op, cf k)
     return {t.r + op.v.r, t.i + op.v.i};
 }
 
-// One wave per group: the group's operator, its chunks composed right to left.
-template <bool CPLX>
-__global__ void __launch_bounds__(kBW * 64) bwd_group_kernel(BwdArgs a)
-{
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int64_t ng = (a.nch + kGroup - 1) / kGroup;
-    const int64_t gi = (int64_t)blockIdx.x * kBW + wave;
-    if (gi >= a.S * ng)
-        return;
-    const int64_t seq = gi / ng, g = gi - seq * ng;
-    const int64_t c0 = g * kGroup, c1 = min(c0 + kGroup, a.nch) - 1;
-    // ring slot r holds the chunk i = r (mod 4) from the right end of the group
-    GOp ring[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-        ring[r] = load_op<CPLX>(a, a.sig, a.mv, seq * a.nch + max(c1 - r, c0), lane);
-    GOp acc = ring[0];
-    for (int64_t i0 = 0; i0 <= c1 - c0; i0 += 4) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t c = c1 - (i0 + r);
-            if (c >= c0) {
-                const GOp op = ring[r];
-                ring[r] = load_op<CPLX>(a, a.sig, a.mv, seq * a.nch + max(c - 4, c0), lane);
-                acc = (i0 + r == 0) ? op : compose_left<CPLX>(op, acc);
-            }
-        }
-    }
-    a.gsig[gi * 64 + lane] = acc.sig;
-    a.gmv[gi * 64 + lane] = make_float4(acc.m.r, acc.m.i, acc.v.r, acc.v.i);
-}
-
-// One wave per sequence: the carry into each group's last chunk, right to
-// left over the groups; then gx0.
-template <bool CPLX>
-__global__ void __launch_bounds__(kBW * 64) bwd_chain_kernel(BwdArgs a)
-{
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int64_t seq = (int64_t)blockIdx.x * kBW + wave;
-    if (seq >= a.S)
-        return;
-    const int64_t ng = (a.nch + kGroup - 1) / kGroup;
-    const bool act = lane < a.N;
-    cf kk = {0.f, 0.f};
-    if (a.gxf && act)
-        kk = load_diag<CPLX>(a.gxf, seq * a.N + lane);
-    for (int64_t g = ng - 1; g >= 0; --g) {
-        a.gk[(seq * ng + g) * 64 + lane] = make_float2(kk.r, kk.i);
-        kk = apply_op<CPLX>(load_op<CPLX>(a, a.gsig, a.gmv, seq * ng + g, lane), kk);
-    }
-    if (a.gx0 && act)
-        store_grad<CPLX>(a.gx0, seq * a.N + lane, kk);
-}
-
-// One wave per group: the carry into every chunk of the group.
-template <bool CPLX>
-__global__ void __launch_bounds__(kBW * 64) bwd_expand_kernel(BwdArgs a)
-{
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int64_t ng = (a.nch + kGroup - 1) / kGroup;
-    const int64_t gi = (int64_t)blockIdx.x * kBW + wave;
-    if (gi >= a.S * ng)
-        return;
-    const int64_t seq = gi / ng, g = gi - seq * ng;
-    const int64_t c0 = g * kGroup, c1 = min(c0 + kGroup, a.nch) - 1;
-    const float2 k0 = a.gk[gi * 64 + lane];
-    cf kk = {k0.x, k0.y};
-    GOp ring[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-        ring[r] = load_op<CPLX>(a, a.sig, a.mv, seq * a.nch + max(c1 - r, c0), lane);
-    for (int64_t i0 = 0; i0 <= c1 - c0; i0 += 4) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t c = c1 - (i0 + r);
-            if (c >= c0) {
-                a.kc[(seq * a.nch + c) * 64 + lane] = make_float2(kk.r, kk.i);
-                const GOp op = ring[r];
-                ring[r] = load_op<CPLX>(a, a.sig, a.mv, seq * a.nch + max(c - 4, c0), lane);
-                kk = apply_op<CPLX>(op, kk);
-            }
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// bwd_grad: per chunk (one wave, lane = state).  The states x_t of the chunk
-// by the forward's collision-free scatter from the saved carry-in (kept in
-// registers), then lambda backwards from K_c by gathers, writing gb, gc and
-// gd.  Inputs stream through rings of D steps; the loads of both passes are
-// issued before any store of the chunk waits on them.
+// bwd_fused: the whole backward in one pass over the inputs.  Each wave owns
+// one chunk of kBT steps, a workgroup a tile of kBW consecutive chunks.
+// Workgroups take tickets in reverse time order (the last tiles of every
+// sequence first), so every tile to the right of a workgroup's tile belongs
+// to a workgroup that has started, and a workgroup only ever waits for
+// those.  A wave
+//  1. loads its chunk's rows and selections (picking them from the scores in
+//     the logits modes),
+//  2. runs forward through the chunk: the states x_t from the saved carry-in
+//     by the forward scan's collision-free scatter and, alongside, the
+//     chunk's adjoint operator (sig, m, v), which maps the adjoint carried
+//     into its last step to the one it carries out of its first:
+//     K_out[j] = m[j] K_in[sig[j]] + v[j],
+//  3. hands its operator to wave 0, which composes the tile's operator,
+//     publishes it and looks back to the right (decoupled look-back,
+//     Merrill & Garland) for the tile's K_in: it composes the operators of
+//     the tiles on its right until it meets one whose K_out is published
+//     (the sequence's last tile publishes no operator: its K_in is
+//     gx_final, so its K_out follows at once),
+//  4. (wave 0) derives every chunk's K_in from the tile's and publishes the
+//     tile's K_out (gx0 for the first tile of a sequence),
+//  5. runs backward through its chunk from K_in, writing gb, gc and gd.
+// Records are 64-bit words with the call's epoch in the upper half, as in
+// the forward scan, so a reader needs no fence; word k of every lane is
+// contiguous (word-major records).
 // ---------------------------------------------------------------------------
+template <bool CPLX>
+struct BwdRec {
+    static constexpr int NC = CPLX ? 2 : 1;
+    static constexpr int AW = 1 + 2 * NC;   // operator words per lane: sig, m.r, v.r (, m.i, v.i)
+};
+
+// Polls of one look-back before a wave gives up (each is a record read and
+// a sleep of 512 clocks, so about a second in all): far beyond any wait of a
+// correct run.  A wave that gives up sets the header's first reserved word
+// and takes a zero carry, so that the kernel always ends.
+constexpr uint32_t kBwdSpinLimit = 1u << 20;
+
 template <bool CPLX, bool BCBF>
-__global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
+__global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
 {
+    using Rec = BwdRec<CPLX>;
+    constexpr int NC = Rec::NC, AW = Rec::AW;
     __shared__ int16_t s_sel[kBW][kBT];
     __shared__ __attribute__((aligned(16))) cf s_reg[kBW][kBlocks][64];
+    __shared__ uint32_t s_ticket;
+    __shared__ int s_osig[kBW][64];   // each wave's chunk operator, then each wave's carry
+    __shared__ cf s_om[kBW][64];
+    __shared__ cf s_ov[kBW][64];
+    __shared__ cf s_k[kBW][64];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int64_t ch = (int64_t)blockIdx.x * kBW + wave;
-    if (ch >= a.S * a.nch)
-        return;
-    const ChunkPos cp = chunk_of(a, ch);
-    const int64_t seq = cp.seq, t0 = cp.t0, h = cp.h;
-    const int nv = (int)min((int64_t)kBT, a.L - t0);
-    const int N = a.N;
+    if (threadIdx.x == 0)
+        s_ticket = atomicAdd(&a.hdr->ticket, 1u);
 #pragma unroll
     for (int r = kRegions; r < 2 * kRegions; ++r)
         s_reg[wave][r][lane] = cf{0.f, 0.f};
+    __syncthreads();
+    // Ticket u -> (tile from the right, sequence), tile-major over sequences.
+    const uint32_t u = __builtin_amdgcn_readfirstlane(s_ticket);
+    const uint32_t S32 = (uint32_t)a.S;
+    const uint32_t tile = u / S32, seq32 = u - tile * S32;
+    if (u >= a.total)
+        return;
+    // The sequence's first tile may have fewer than kBW chunks: a wave without
+    // one runs chunk 0's loads and arithmetic to no effect (its operator is
+    // the identity and it stores nothing), so that it meets the barriers.
+    const int64_t c_own = a.nch - 1 - ((int64_t)tile * kBW + wave);
+    const bool has = c_own >= 0;
+    const int64_t c = has ? c_own : 0;
+    const uint32_t epoch = a.hdr->epoch;
+    const int64_t seq = seq32, t0 = c * kBT, h = seq32 % (uint32_t)a.H;
+    const int64_t rec = seq * a.nch + c;
+    const int nv = (int)min((int64_t)kBT, a.L - t0);
+    const int N = a.N;
     char *const regp = reinterpret_cast<char *>(&s_reg[wave][0][0]);
     const char *const rowbase = regp + lane * (int)sizeof(cf);
 
@@ -521,44 +366,26 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
     using Stored = typename IO::Stored;
     IO io;
     io.init(a, seq, t0, nv, h, lane);
-    // selections: the forward's (index modes) or the ones the operator pass
-    // picked from the scores
-    const void *ssrc = a.ksel ? static_cast<const void *>(a.ksel) : a.sel;
-    const uint32_t smode = a.ksel ? PDSSM_SEL_I16 : a.sel_mode;
-    const int kraw = sel_raw(ssrc, smode, seq * a.L + t0, nv, lane);
+    const bool idx = index_mode(a.sel_mode);
+    const int kraw = idx ? sel_raw(a.sel, a.sel_mode, seq * a.L + t0, nv, lane) : 0;
     const uint32_t gyr = chunk_gy_raw(a, seq * a.L + t0, nv, lane);
-    auto gy_at = [&](int tt) { return gy_step(a, gyr, tt); };
     auto sel_at = [&](int ts) { return __builtin_amdgcn_readfirstlane((int)s_sel[wave][ts]); };
-    const int64_t e0 = (seq * a.L + t0) * N;
-    const uint64_t rows = (uint64_t)nv * (uint64_t)N;
-    const __amdgpu_buffer_rsrc_t ogb = make_rsrc(reinterpret_cast<Stored *>(a.gb) + e0, rows * sizeof(Stored));
-    const __amdgpu_buffer_rsrc_t ogc = make_rsrc(reinterpret_cast<Stored *>(a.gc) + e0, rows * sizeof(Stored));
-    const __amdgpu_buffer_rsrc_t ogd = make_rsrc(reinterpret_cast<DRaw *>(a.gd) + e0, rows * sizeof(DRaw));
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(reinterpret_cast<const DRaw *>(a.xch) + ch * N, (uint64_t)N * sizeof(DRaw));
 
+    // ---- 1. loads: every d row of the chunk (kept for both passes), the
+    // first D rows of b and c, the carry-in state; then the selections.
     constexpr int D = PDSSM_BWD_GRAD_D;
-    cf rd[D];
-    Raw rv[D];   // b in the forward pass, c in the backward pass
+    cf ds[kBT];
+#pragma unroll
+    for (int tt = 0; tt < kBT; ++tt)
+        ds[tt] = io.d(min(tt, nv - 1));
+    Raw rb[D], rc[D];
     uint32_t re[D];
-
-    // ---- x over the chunk: x_t = P_t (d_t * x_{t-1}) + b_t.  The first
-    // rows of d and b are in flight before the selections are read.
-    auto fetch_db = [&](int tt) {
-        const int ts = min(tt, nv - 1);
-        rd[tt % D] = io.d(ts);
-        rv[tt % D] = io.raw_b(ts);
-    };
-    auto fetch_f = [&](int tt) {
-        fetch_db(tt);
-        re[tt % D] = io.ent(sel_at(min(tt, nv - 1)));
-    };
 #pragma unroll
-    for (int tt = 0; tt < D; ++tt)
-        fetch_db(tt);
-    sel_put(kraw, a.K, nv, s_sel[wave], lane);
-#pragma unroll
-    for (int tt = 0; tt < D; ++tt)
-        re[tt % D] = io.ent(sel_at(min(tt, nv - 1)));
+    for (int tt = 0; tt < D; ++tt) {
+        rb[tt] = io.raw_b(min(tt, nv - 1));
+        rc[tt] = io.raw_c(min(tt, nv - 1));
+    }
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xch + rec * N * NC, (uint64_t)N * sizeof(DRaw));
     cf xin;
     {
         const DRaw v = bload<DRaw>(rx, io.vd, 0);
@@ -567,67 +394,192 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
         else
             xin = {v, 0.f};
     }
-    cf xs[kBT];   // x_t, and d_t and pi_t (four 6-bit maps a word) for the reverse pass
-    cf ds[kBT];
+    if (idx)
+        sel_put(kraw, a.K, nv, s_sel[wave], lane);
+    else
+        wave_select<kBT>(a.sel, a.sel_mode, a.K, a.L, seq * a.L, t0, s_sel[wave], lane);
+#pragma unroll
+    for (int tt = 0; tt < D; ++tt)
+        re[tt] = io.ent(sel_at(min(tt, nv - 1)));
+
+    // ---- 2. forward through the chunk: x_t, and the adjoint operator.
+    // Lane j follows the chunk-start source j: pacc (byte address) is where
+    // it sits after step t, dacc its factor; the readout weight of step t is
+    // g_t[j] = c_t[pacc_t[j]] dacc_t[j] and v = sum_t gy_t conj(g_t).
+    cf xs[kBT];
+    Raw cs[kBT];
     uint32_t pis[kBT / 4] = {};
     cf x = xin;
+    int pacc4 = lane * 4;
+    cf dacc = {1.f, 0.f}, v = {0.f, 0.f};
 #pragma unroll
     for (int tt = 0; tt < kBT; ++tt) {
-        const cf d = rd[tt % D];
-        const cf bb = unpack_c<CPLX, BCBF>(rv[tt % D]);
+        const cf d = ds[tt];
+        const Raw braw = rb[tt % D], craw = rc[tt % D];
         const uint32_t ent = re[tt % D];
-        if (tt + D < kBT)
-            fetch_f(tt + D);
-        ds[tt] = d;
+        if (tt + D < kBT) {
+            const int ts = min(tt + D, nv - 1);
+            rb[tt % D] = io.raw_b(ts);
+            rc[tt % D] = io.raw_c(ts);
+            re[tt % D] = io.ent(sel_at(ts));
+        }
         pis[tt / 4] |= (ent & 63u) << (8 * (tt % 4));
+        cs[tt] = craw;
         if (tt < nv) {
-            const cf v = cmul(d, x);
+            // the operator: gathers at the previous position (no dependence on x)
+            const uint32_t np = bperm_a(ent & 63u, pacc4);
+            cf dd;
+            dd.r = bperm_a(d.r, pacc4);
+            dd.i = CPLX ? bperm_a(d.i, pacc4) : 0.f;
+            // x_t = P_t (d_t * x_{t-1}) + b_t by the rank-region scatter
+            const cf vv = cmul(d, x);
             const uint32_t slot = entry_slot(ent);
-            *static_cast<float2 *>(__builtin_assume_aligned(regp + slot, 8)) = make_float2(v.r, v.i);
+            *static_cast<float2 *>(__builtin_assume_aligned(regp + slot, 8)) = make_float2(vv.r, vv.i);
             lds_order();
             if (__any(slot >= kSpareOff)) {
                 if (slot >= kSpareOff) {
                     cf *o = reinterpret_cast<cf *>(regp + (slot - kSpareOff));
-                    lds_add(&o->r, v.r);
+                    lds_add(&o->r, vv.r);
                     if constexpr (CPLX)
-                        lds_add(&o->i, v.i);
+                        lds_add(&o->i, vv.i);
                 }
                 lds_order();
             }
             const char *rowp = rowbase + entry_row(ent);
-            cf sum = bb;
+            cf sum = unpack_c<CPLX, BCBF>(braw);
 #pragma unroll
             for (int r = 0; r < kRegions; ++r) {
-                const float2 u = *static_cast<const float2 *>(__builtin_assume_aligned(rowp + r * kRegionBytes, 8));
-                sum.r += u.x;
-                sum.i += u.y;
+                const float2 q = *static_cast<const float2 *>(__builtin_assume_aligned(rowp + r * kRegionBytes, 8));
+                sum.r += q.x;
+                sum.i += q.y;
             }
             lds_order();
             x = sum;
+            dacc = cmul(dd, dacc);
+            pacc4 = (int)(np << 2);
+            const float g = gy_step(a, gyr, tt);
+            const cf cg = unpack_c<CPLX, BCBF>(bperm_raw<CPLX, BCBF>(craw, pacc4));
+            const cf w = cmul(cg, dacc);
+            v.r += g * w.r;
+            v.i -= g * w.i;
         }
         xs[tt] = x;
     }
+    // ---- 3. the tile's carries.  The waves' operators meet in LDS; wave 0
+    // composes the tile's operator (the leftmost chunk's applied last), looks
+    // back over the tiles on the right for the adjoint carried into the tile,
+    // and hands every wave the adjoint carried into its chunk.
+    s_osig[wave][lane] = has ? (pacc4 >> 2) : lane;
+    s_om[wave][lane] = has ? cf{dacc.r, -dacc.i} : cf{1.f, 0.f};
+    s_ov[wave][lane] = has ? v : cf{0.f, 0.f};
+    __syncthreads();
+    if (wave == 0) {
+        auto op_of = [&](int w) { return GOp{s_osig[w][lane], s_om[w][lane], s_ov[w][lane]}; };
+        const int64_t seq_rec = seq * a.tiles, trec = seq_rec + tile;
+        cf K = {0.f, 0.f};
+        if (tile == 0) {
+            if (a.gxf && lane < N)
+                K = load_diag<CPLX>(a.gxf, seq * N + lane);   // the adjoint after the last step
+        } else {
+            GOp tagg = op_of(0);
+#pragma unroll
+            for (int w = 1; w < kBW; ++w)
+                tagg = compose_left<CPLX>(op_of(w), tagg);
+            // words: sig, m.r, v.r (, m.i, v.i)
+            uint64_t *const aw_own = a.agg + trec * (AW * 64);
+            put_word(aw_own + lane, (uint32_t)tagg.sig, epoch);
+            put_word(aw_own + 64 + lane, __float_as_uint(tagg.m.r), epoch);
+            put_word(aw_own + 128 + lane, __float_as_uint(tagg.v.r), epoch);
+            if constexpr (CPLX) {
+                put_word(aw_own + 192 + lane, __float_as_uint(tagg.m.i), epoch);
+                put_word(aw_own + 256 + lane, __float_as_uint(tagg.v.i), epoch);
+            }
+            GOp acc = {lane, {1.f, 0.f}, {0.f, 0.f}};   // the tiles tile-1 .. j+1, composed
+            int64_t j = tile - 1;
+            uint32_t spins = 0;
+            while (true) {
+                const uint64_t *iw = a.incl + (seq_rec + j) * (NC * 64);
+                const uint64_t *aw = a.agg + (seq_rec + j) * (AW * 64);
+                // Probe one word of tile j's carry-out (lane 0) and of its
+                // operator (lane 1; the sequence's last tile publishes none);
+                // read a whole record only once its probe word has landed.
+                uint32_t pw = 0;
+                bool pr = false;
+                if (lane == 0)
+                    pr = get_word(iw, epoch, pw);
+                else if (lane == 1 && j > 0)
+                    pr = get_word(aw, epoch, pw);
+                const uint64_t ready = __ballot(pr);
+                if (ready & 1) {
+                    uint32_t p0 = 0, p1 = 0;
+                    bool ok = get_word(iw + lane, epoch, p0);
+                    if constexpr (CPLX)
+                        ok = get_word(iw + 64 + lane, epoch, p1) && ok;
+                    if (__all(ok)) {
+                        K = apply_op<CPLX>(acc, cf{__uint_as_float(p0), CPLX ? __uint_as_float(p1) : 0.f});
+                        break;
+                    }
+                } else if (ready & 2) {
+                    uint32_t q[5] = {0u, 0u, 0u, 0u, 0u};
+                    bool okb = true;
+#pragma unroll
+                    for (int k = 0; k < AW; ++k)
+                        okb = get_word(aw + k * 64 + lane, epoch, q[k]) && okb;
+                    if (__all(okb)) {
+                        GOp opj;
+                        opj.sig = (int)min(q[0], 63u);
+                        opj.m = {__uint_as_float(q[1]), CPLX ? __uint_as_float(q[3]) : 0.f};
+                        opj.v = {__uint_as_float(q[2]), CPLX ? __uint_as_float(q[4]) : 0.f};
+                        acc = compose_left<CPLX>(acc, opj);
+                        --j;
+                        continue;
+                    }
+                }
+                if (++spins > kBwdSpinLimit) {
+                    if (lane == 0)
+                        __hip_atomic_store(&a.hdr->reserved0[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(8);
+            }
+        }
+        // ---- 4. every chunk's carry, then the tile's carry-out (gx0 for
+        // the sequence's first tile)
+#pragma unroll
+        for (int w = 0; w < kBW; ++w) {
+            const GOp ow = op_of(w);
+            s_k[w][lane] = K;
+            K = apply_op<CPLX>(ow, K);
+        }
+        if (tile + 1 < a.tiles) {
+            uint64_t *const iw_own = a.incl + trec * (NC * 64);
+            put_word(iw_own + lane, __float_as_uint(K.r), epoch);
+            if constexpr (CPLX)
+                put_word(iw_own + 64 + lane, __float_as_uint(K.i), epoch);
+        } else if (a.gx0 && lane < N) {
+            store_grad<CPLX>(a.gx0, seq * N + lane, K);
+        }
+    }
+    __syncthreads();
+    if (!has)
+        return;
+    const cf K = s_k[wave][lane];
 
-    // ---- lambda back over the chunk, from the carried part K_c
-    auto fetch_b = [&](int u) {   // u-th step from the end: step 15 - u, clamped into the chunk
-        const int ts = min(kBT - 1 - u, nv - 1);
-        rv[u % D] = io.raw_c(max(ts, 0));
-    };
+    // ---- 5. backward through the chunk from K, writing the gradients
+    const int64_t e0 = (seq * a.L + t0) * N;
+    const uint64_t rows = (uint64_t)nv * (uint64_t)N;
+    const __amdgpu_buffer_rsrc_t ogb = make_rsrc(reinterpret_cast<Stored *>(a.gb) + e0, rows * sizeof(Stored));
+    const __amdgpu_buffer_rsrc_t ogc = make_rsrc(reinterpret_cast<Stored *>(a.gc) + e0, rows * sizeof(Stored));
+    const __amdgpu_buffer_rsrc_t ogd = make_rsrc(reinterpret_cast<DRaw *>(a.gd) + e0, rows * sizeof(DRaw));
+    cf lc = K;   // A_{t+1}^H lambda_{t+1}, the part carried into step t
 #pragma unroll
-    for (int u = 0; u < D; ++u)
-        fetch_b(u);
-    const float2 k0 = a.kc[ch * 64 + lane];
-    cf lc = {k0.x, k0.y};   // A_{t+1}^H lambda_{t+1}, the part carried into step t
-#pragma unroll
-    for (int u = 0; u < kBT; ++u) {
-        const int tt = kBT - 1 - u;
+    for (int q = 0; q < kBT; ++q) {
+        const int tt = kBT - 1 - q;
         const cf d = ds[tt];
-        const cf cv = unpack_c<CPLX, BCBF>(rv[u % D]);
+        const cf cv = unpack_c<CPLX, BCBF>(cs[tt]);
         const uint32_t ent = pis[tt / 4] >> (8 * (tt % 4));
-        if (u + D < kBT)
-            fetch_b(u + D);
         if (tt < nv) {
-            const float g = gy_at(tt);
+            const float g = gy_step(a, gyr, tt);
             const cf lam = {lc.r + g * cv.r, lc.i - g * cv.i};
             const int pi4 = (int)((ent & 63u) << 2);
             cf lg;
@@ -649,38 +601,24 @@ __global__ void __launch_bounds__(kBW * 64) bwd_grad_kernel(BwdArgs a)
 // Host side.
 // ---------------------------------------------------------------------------
 struct BwdLayout {
-    int64_t nch, S, tab_bytes, sig_bytes, mv_bytes, kc_bytes, grp_bytes, ksel_bytes, total;
+    int64_t nch, S, tiles, tab_bytes, agg_bytes, incl_bytes, total;
 };
 
-static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t L, int32_t K)
+// Workspace: header | entry table [H][K][64] | operator records | carry records.
+static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t L, int32_t K, uint32_t flags)
 {
     BwdLayout lo;
+    const int nc = (flags & PDSSM_COMPLEX) ? 2 : 1;
     lo.S = B * H;
     lo.nch = (L + kBT - 1) / kBT;
-    const int64_t chunks = lo.S * lo.nch;
+    lo.tiles = (lo.nch + kBW - 1) / kBW;
+    const int64_t recs = lo.S * lo.tiles;
     auto up = [](int64_t n) { return (n + 255) / 256 * 256; };
     lo.tab_bytes = up(H * (int64_t)K * 64 * 2);
-    lo.sig_bytes = up(chunks * 64 * 4);
-    lo.mv_bytes = up(chunks * 64 * 16);
-    lo.kc_bytes = up(chunks * 64 * 8);
-    const int64_t groups = lo.S * ((lo.nch + kGroup - 1) / kGroup);
-    lo.grp_bytes = up(groups * 64 * 4) + up(groups * 64 * 16) + up(groups * 64 * 8);
-    lo.ksel_bytes = up(lo.S * L * 2);
-    lo.total = lo.tab_bytes + lo.sig_bytes + lo.mv_bytes + lo.kc_bytes + lo.grp_bytes + lo.ksel_bytes;
+    lo.agg_bytes = up(recs * 64 * (1 + 2 * nc) * 8);
+    lo.incl_bytes = up(recs * 64 * nc * 8);
+    lo.total = (int64_t)sizeof(Header) + lo.tab_bytes + lo.agg_bytes + lo.incl_bytes;
     return lo;
-}
-
-template <bool CPLX, bool BCBF>
-static void launch_bwd(const BwdArgs &a, hipStream_t st)
-{
-    const int64_t chunks = a.S * a.nch;
-    const dim3 blk(kBW * 64);
-    hipLaunchKernelGGL((bwd_ops_kernel<CPLX, BCBF>), dim3((unsigned)((chunks + kBW - 1) / kBW)), blk, 0, st, a);
-    const int64_t groups = a.S * ((a.nch + kGroup - 1) / kGroup);
-    hipLaunchKernelGGL((bwd_group_kernel<CPLX>), dim3((unsigned)((groups + kBW - 1) / kBW)), blk, 0, st, a);
-    hipLaunchKernelGGL((bwd_chain_kernel<CPLX>), dim3((unsigned)((a.S + kBW - 1) / kBW)), blk, 0, st, a);
-    hipLaunchKernelGGL((bwd_expand_kernel<CPLX>), dim3((unsigned)((groups + kBW - 1) / kBW)), blk, 0, st, a);
-    hipLaunchKernelGGL((bwd_grad_kernel<CPLX, BCBF>), dim3((unsigned)((chunks + kBW - 1) / kBW)), blk, 0, st, a);
 }
 
 }  // namespace pdssm
@@ -692,9 +630,7 @@ extern "C" size_t pdssm_scan_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L
 {
     if (check_dims(B, H, L, N, K) != PDSSM_OK || (flags & ~PDSSM_FLAGS_ALL))
         return 0;
-    // Never 0 (which means invalid arguments), also for empty shapes.
-    const int64_t total = bwd_layout(B, H, L, K).total;
-    return (size_t)(total > 256 ? total : 256);
+    return (size_t)bwd_layout(B, H, L, K, flags).total;
 }
 
 extern "C" int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
@@ -726,11 +662,13 @@ extern "C" int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx
     for (const void *p : ptrs)
         if (p && !aligned16(p))
             return PDSSM_ERR_ALIGN;
-    const BwdLayout lo = bwd_layout(B, H, L, K);
+    const BwdLayout lo = bwd_layout(B, H, L, K, flags);
     if (workspace_bytes < (size_t)lo.total)
         return PDSSM_ERR_WORKSPACE;
+    if ((double)lo.S * (double)lo.tiles > 4.0e9)
+        return PDSSM_ERR_DIM;   // tickets are 32-bit
 
-    BwdArgs a;
+    BwdArgs a = {};
     a.sel = sel_or_logits;
     a.dict = dict_idx;
     a.diag = static_cast<const float *>(diag);
@@ -744,37 +682,36 @@ extern "C" int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx
     a.gd = static_cast<float *>(gd);
     a.gx0 = static_cast<float *>(gx0);
     char *w = static_cast<char *>(workspace);
-    a.tab = reinterpret_cast<uint16_t *>(w);
-    a.sig = reinterpret_cast<int32_t *>(w + lo.tab_bytes);
-    a.mv = reinterpret_cast<float4 *>(w + lo.tab_bytes + lo.sig_bytes);
-    a.kc = reinterpret_cast<float2 *>(w + lo.tab_bytes + lo.sig_bytes + lo.mv_bytes);
-    {
-        char *gw = w + lo.tab_bytes + lo.sig_bytes + lo.mv_bytes + lo.kc_bytes;
-        const int64_t groups = lo.S * ((lo.nch + kGroup - 1) / kGroup);
-        auto up = [](int64_t n) { return (n + 255) / 256 * 256; };
-        a.gsig = reinterpret_cast<int32_t *>(gw);
-        a.gmv = reinterpret_cast<float4 *>(gw + up(groups * 64 * 4));
-        a.gk = reinterpret_cast<float2 *>(gw + up(groups * 64 * 4) + up(groups * 64 * 16));
-    }
-    const bool logits = (flags & PDSSM_SEL_MASK) == PDSSM_LOGITS_F32 || (flags & PDSSM_SEL_MASK) == PDSSM_LOGITS_BF16;
-    a.ksel = logits ? reinterpret_cast<int16_t *>(w + lo.total - lo.ksel_bytes) : nullptr;
+    a.hdr = reinterpret_cast<Header *>(w);
+    uint16_t *tab = reinterpret_cast<uint16_t *>(w + sizeof(Header));
+    a.tab = tab;
+    a.agg = reinterpret_cast<uint64_t *>(w + sizeof(Header) + lo.tab_bytes);
+    a.incl = reinterpret_cast<uint64_t *>(w + sizeof(Header) + lo.tab_bytes + lo.agg_bytes);
     a.H = H;
     a.L = L;
     a.S = lo.S;
     a.nch = lo.nch;
+    a.total = (uint32_t)(lo.S * lo.tiles);
+    a.tiles = lo.tiles;
     a.N = N;
     a.K = K;
     a.sel_mode = flags & PDSSM_SEL_MASK;
     a.y_bf16 = (flags & PDSSM_Y_BF16) ? 1 : 0;
-    a.idx32 = (lo.S * lo.nch < ((int64_t)1 << 31) && H < ((int64_t)1 << 31)) ? 1 : 0;
 
-    const int64_t entries = H * (int64_t)K;
-    hipLaunchKernelGGL(bwd_tab_kernel, dim3((unsigned)((entries + 3) / 4)), dim3(256), 0, stream, dict_idx,
-                       const_cast<uint16_t *>(a.tab), entries, N);
+    // New epoch and ticket, the entry table; on first use every record is cleared.
+    rc = launch_prep(a.hdr, a.agg, (lo.agg_bytes + lo.incl_bytes) / 16, dict_idx, tab, H * (int64_t)K, N, 64,
+                     stream);
+    if (rc != PDSSM_OK)
+        return rc;
     const bool cplx = flags & PDSSM_COMPLEX, bcbf = flags & PDSSM_BC_BF16;
-    if (cplx)
-        bcbf ? launch_bwd<true, true>(a, stream) : launch_bwd<true, false>(a, stream);
+    const dim3 grid(a.total), blk(kBW * 64);
+    if (cplx && bcbf)
+        hipLaunchKernelGGL((bwd_fused_kernel<true, true>), grid, blk, 0, stream, a);
+    else if (cplx)
+        hipLaunchKernelGGL((bwd_fused_kernel<true, false>), grid, blk, 0, stream, a);
+    else if (bcbf)
+        hipLaunchKernelGGL((bwd_fused_kernel<false, true>), grid, blk, 0, stream, a);
     else
-        bcbf ? launch_bwd<false, true>(a, stream) : launch_bwd<false, false>(a, stream);
+        hipLaunchKernelGGL((bwd_fused_kernel<false, false>), grid, blk, 0, stream, a);
     return hip_status(hipGetLastError());
 }

@@ -1224,6 +1224,15 @@ __global__ void __launch_bounds__(256) identity_op_kernel(int32_t *pi, float *d,
 
 static unsigned fill_blocks(int64_t n) { return (unsigned)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096); }
 
+int launch_prep(Header *hdr, void *recs, int64_t n16, const int32_t *dict, uint16_t *tab, int64_t entries,
+                int N, int NP, hipStream_t stream)
+{
+    const int64_t blocks = 1 + (entries + kPrepThreads / 64 - 1) / (kPrepThreads / 64);
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)blocks), dim3(kPrepThreads), 0, stream, hdr, nullptr,
+                       (int64_t)0, static_cast<uint4 *>(recs), n16, dict, tab, entries, N, NP);
+    return hip_status(hipGetLastError());
+}
+
 int launch_state_fill(const void *src, void *dst, int64_t n, hipStream_t stream)
 {
     if (n <= 0)
