@@ -54,7 +54,10 @@ def check_save(orc, inp, label):
     y1, _ = pk.scan(g)
     y2, xf2, xch, sel = pk.scan_save(g, want_sel=True)
     torch.cuda.synchronize()
-    assert torch.equal(y1, y2), f"{label}: y differs with the carries kept"
+    # the same scan; the tiles' carries may compose in another order (the
+    # look-back depends on timing), so y agrees to rounding
+    lim = 2.0 ** -7 if y1.dtype == torch.bfloat16 else 1e-5
+    assert seq_rel_err(y_to_np(y1), y_to_np(y2)) <= lim, f"{label}: y differs with the carries kept"
     ref_sel = orc.select(inp.sel_or_logits, inp.sel_mode, inp.K)
     assert np.array_equal(sel.cpu().numpy().astype(np.int64), ref_sel.astype(np.int64)), \
         f"{label}: saved selections differ from the oracle's"

@@ -21,6 +21,7 @@ import torch
 import oracle
 import structured_sparse_state_amd as pk
 from structured_sparse_state_amd import inputs as gen
+from tests.gpu_common import seq_rel_err, y_to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -116,4 +117,6 @@ def test_router_feeds_scan(orc):
     y, _ = pk.scan(g)
     y_ref, _ = pk.scan(inp.to(DEV))
     torch.cuda.synchronize()
-    assert torch.equal(y, y_ref)
+    # the same selections give the same scan, to rounding (the tiles'
+    # carries may compose in another order from call to call)
+    assert seq_rel_err(y_to_np(y), y_to_np(y_ref)) <= 2.0 ** -7
