@@ -170,8 +170,24 @@ def measure_aux(pk, gen, inp, stream):
     t_dec = _event_time(dec, 200, 20, stream)
 
     # Router scores + argmax from the step inputs (D = 2048 features per
-    # token), only the int16 selections written.
+    # token), only the int16 selections written; the fused kernel takes up
+    # to 64 scores per head.
     D = ROUTER_D
+    if K > 64:
+        dec_bytes = sum(t.numel() * t.element_size() for t in (sel, d, b, c, y)) + 2 * x.numel() * 4
+        print(f"[bench] dict hardmax {t_hm * 1e6:.1f} us ({hm_bytes / t_hm / 1e9:.0f} GB/s); decode step "
+              f"{t_dec * 1e6:.2f} us ({B * H / t_dec:.3g} tokens/s); router: K={K} > 64, not run",
+              file=sys.stderr, flush=True)
+        return {
+            "dict_hardmax": {"us_per_call": t_hm * 1e6, "shape": f"H={H} K={K} N={N} fp32",
+                             "algorithmic_bytes_per_call": hm_bytes,
+                             "achieved_GBps": hm_bytes / t_hm / 1e9,
+                             "frac": hm_bytes / t_hm / 1e9 / HBM_PEAK_GBS},
+            "decode_step": {"us_per_call": t_dec * 1e6, "tokens_per_s": B * H / t_dec,
+                            "shape": f"B={B} H={H} N={N} K={K}, one step per sequence",
+                            "algorithmic_bytes_per_call": dec_bytes},
+            "router_select": None,
+        }
     ru, rw = gen.make_router_inputs(B, inp.L, H, K, D, seed=4, device=dev)
     rsel = pk.router_select(ru, rw, stream=stream)
     # The matrix cores reach their sustained clock only after a while of
