@@ -117,51 +117,100 @@ __device__ __forceinline__ typename RawOf<CPLX, BCBF>::type bperm_raw(typename R
         return bperm_a(v, addr);
 }
 
-template <bool CPLX, bool BCBF>
+// A wave holds G = 64 / NP chunks (lane group g = lane / NP runs the g-th,
+// lane i = lane % NP its state i).  The resources start at the wave's first
+// row; a lane's rows lie at its chunk's offset from there.  Steps are
+// clamped into the sequence: with one chunk per wave by the wave-uniform
+// row offset, with several by the lane's own offset.
+template <int NP, bool CPLX, bool BCBF>
 struct ChunkIO {
+    static constexpr int G = 64 / NP;
     using DRaw = typename std::conditional<CPLX, float2, float>::type;
     using Stored = typename std::conditional<BCBF, typename std::conditional<CPLX, uint32_t, uint16_t>::type,
                                              DRaw>::type;
     __amdgpu_buffer_rsrc_t rd, rb, rc, rt;
     uint32_t vd, vs, vt;   // lane offsets (bytes) into diag-like, b/c-like rows and the entry table
-    int N;
+    int N, last;           // last: the lane's last valid row, counted from the wave's first
+    int rel;               // the lane's first row, counted from the wave's first
+    bool act;
 
-    __device__ void init(const BwdArgs &a, int64_t seq, int64_t t0, int nv, int64_t h, int lane)
+    __device__ void init(const BwdArgs &a, int64_t seq, int64_t tw, int64_t t0, int64_t h, int i)
     {
         N = a.N;
-        const int64_t e0 = (seq * a.L + t0) * a.N;   // first element of the chunk
-        const uint64_t rows = (uint64_t)nv * (uint64_t)a.N;
+        const int64_t e0 = (seq * a.L + tw) * a.N;   // first element of the wave's rows
+        const uint64_t rows = (uint64_t)(a.L - tw) * (uint64_t)a.N;
         rd = make_rsrc(reinterpret_cast<const DRaw *>(a.diag) + e0, rows * sizeof(DRaw));
         rb = make_rsrc(reinterpret_cast<const Stored *>(a.b) + e0, rows * sizeof(Stored));
         rc = make_rsrc(reinterpret_cast<const Stored *>(a.c) + e0, rows * sizeof(Stored));
-        rt = make_rsrc(a.tab + h * (int64_t)a.K * 64, (uint64_t)a.K * 64 * 2);
-        const bool act = lane < a.N;
-        vd = act ? (uint32_t)(lane * sizeof(DRaw)) : kOffLane;
-        vs = act ? (uint32_t)(lane * sizeof(Stored)) : kOffLane;
-        vt = (uint32_t)(lane * 2);   // the table has all 64 lanes (padding maps to itself)
+        rt = make_rsrc(a.tab + h * (int64_t)a.K * NP, (uint64_t)a.K * NP * 2);
+        act = i < a.N;
+        rel = (int)(t0 - tw);
+        last = (int)(a.L - 1 - tw);
+        vd = act ? (uint32_t)(i * sizeof(DRaw)) : kOffLane;
+        vs = act ? (uint32_t)(i * sizeof(Stored)) : kOffLane;
+        vt = (uint32_t)(i * 2);   // the table has all NP lanes (padding maps to itself)
     }
-    __device__ cf d(int tt) const
+    // byte offsets of step tt of the lane's chunk (ts: the same step clamped
+    // into the chunk, used with one chunk per wave)
+    template <typename V>
+    __device__ void offs(int tt, int ts, uint32_t base, uint32_t &voff, uint32_t &soff) const
     {
-        const DRaw v = bload<DRaw>(rd, vd, (uint32_t)(tt * N * (int)sizeof(DRaw)));
+        if constexpr (G == 1) {
+            voff = base;
+            soff = (uint32_t)(ts * N * (int)sizeof(V));
+        } else {
+            voff = act ? base + (uint32_t)(min(rel + tt, last) * N * (int)sizeof(V)) : kOffLane;
+            soff = 0;
+        }
+    }
+    __device__ cf d(int tt, int ts) const
+    {
+        uint32_t vo, so;
+        offs<DRaw>(tt, ts, vd, vo, so);
+        const DRaw v = bload<DRaw>(rd, vo, so);
         if constexpr (CPLX)
             return {v.x, v.y};
         else
             return {v, 0.f};
     }
-    __device__ typename RawOf<CPLX, BCBF>::type raw_b(int tt) const
+    __device__ typename RawOf<CPLX, BCBF>::type raw_b(int tt, int ts) const
     {
-        return (typename RawOf<CPLX, BCBF>::type)bload<Stored>(rb, vs, (uint32_t)(tt * N * (int)sizeof(Stored)));
+        uint32_t vo, so;
+        offs<Stored>(tt, ts, vs, vo, so);
+        return (typename RawOf<CPLX, BCBF>::type)bload<Stored>(rb, vo, so);
     }
-    __device__ typename RawOf<CPLX, BCBF>::type raw_c(int tt) const
+    __device__ typename RawOf<CPLX, BCBF>::type raw_c(int tt, int ts) const
     {
-        return (typename RawOf<CPLX, BCBF>::type)bload<Stored>(rc, vs, (uint32_t)(tt * N * (int)sizeof(Stored)));
+        uint32_t vo, so;
+        offs<Stored>(tt, ts, vs, vo, so);
+        return (typename RawOf<CPLX, BCBF>::type)bload<Stored>(rc, vo, so);
     }
-    __device__ uint32_t ent(int k) const { return bload<uint16_t>(rt, vt, (uint32_t)(k * 128)); }
+    // the entry of dictionary entry k for this lane (k wave-uniform when G == 1)
+    __device__ uint32_t ent(int k) const
+    {
+        if constexpr (G == 1)
+            return bload<uint16_t>(rt, vt, (uint32_t)(k * NP * 2));
+        else
+            return bload<uint16_t>(rt, vt + (uint32_t)(k * NP * 2), 0);
+    }
+    // the store offsets of step tt (inside the sequence) of the lane's chunk
+    template <typename V>
+    __device__ void store_offs(int tt, uint32_t base, uint32_t &voff, uint32_t &soff) const
+    {
+        if constexpr (G == 1) {
+            voff = base;
+            soff = (uint32_t)(tt * N * (int)sizeof(V));
+        } else {
+            voff = act ? base + (uint32_t)((rel + tt) * N * (int)sizeof(V)) : kOffLane;
+            soff = 0;
+        }
+    }
 };
 
-// The chunk's 16 upstream gradients gy as stored (fp32 bits, or bf16 bits in
-// the low half), one per lane (lanes 0..nv-1).  They are converted where a
-// step uses them, so that the load stays in flight meanwhile.
+// The wave's upstream gradients gy as stored (fp32 bits, or bf16 bits in
+// the low half), one step per lane (lanes 0..nv-1 of the wave's steps).
+// They are converted where a step uses them, so that the load stays in
+// flight meanwhile.
 __device__ __forceinline__ uint32_t chunk_gy_raw(const BwdArgs &a, int64_t step0, int nv, int lane)
 {
     const int l = min(lane, nv - 1);
@@ -170,9 +219,16 @@ __device__ __forceinline__ uint32_t chunk_gy_raw(const BwdArgs &a, int64_t step0
     return reinterpret_cast<const uint32_t *>(a.gy)[step0 + l];
 }
 
-__device__ __forceinline__ float gy_step(const BwdArgs &a, uint32_t raw, int tt)
+// gy of step s of the wave's steps (s wave-uniform with one chunk per wave,
+// else per lane)
+template <int G>
+__device__ __forceinline__ float gy_step(const BwdArgs &a, uint32_t raw, int s)
 {
-    const uint32_t r = (uint32_t)__builtin_amdgcn_readlane((int)raw, tt);
+    uint32_t r;
+    if constexpr (G == 1)
+        r = (uint32_t)__builtin_amdgcn_readlane((int)raw, s);
+    else
+        r = bperm_a(raw, s * 4);
     return __uint_as_float(a.y_bf16 ? r << 16 : r);
 }
 
@@ -192,9 +248,10 @@ __device__ __forceinline__ int sel_raw(const void *src, uint32_t mode, int64_t r
                                  : reinterpret_cast<const int16_t *>(src)[row + lane];
 }
 
+template <int WS>
 __device__ __forceinline__ void sel_put(int k, int K, int nv, int16_t *out, int lane)
 {
-    if (lane < kBT)
+    if (lane < WS)
         out[lane] = (int16_t)(lane < nv ? (int)min((unsigned)k, (unsigned)(K - 1)) : 0);
 }
 
@@ -220,7 +277,7 @@ __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, V v, uint32_t v
 
 // A gradient in the raw storage of b or c (bf16 rounded to nearest even, or fp32).
 template <bool CPLX, bool BCBF>
-__device__ __forceinline__ typename ChunkIO<CPLX, BCBF>::Stored pack_vec(cf v)
+__device__ __forceinline__ typename ChunkIO<64, CPLX, BCBF>::Stored pack_vec(cf v)
 {
     if constexpr (BCBF) {
         if constexpr (CPLX)
@@ -321,19 +378,22 @@ struct BwdRec {
 // and takes a zero carry, so that the kernel always ends.
 constexpr uint32_t kBwdSpinLimit = 1u << 20;
 
-template <bool CPLX, bool BCBF>
+template <int NP, bool CPLX, bool BCBF>
 __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
 {
     using Rec = BwdRec<CPLX>;
     constexpr int NC = Rec::NC, AW = Rec::AW;
-    __shared__ int16_t s_sel[kBW][kBT];
+    constexpr int G = 64 / NP, TC = kBW * G, WS = G * kBT;   // chunks per wave, per tile; steps per wave
+    static_assert(G >= 1 && WS <= 64, "one step of the wave per lane");
+    __shared__ int16_t s_sel[kBW][WS];
     __shared__ __attribute__((aligned(16))) cf s_reg[kBW][kBlocks][64];
     __shared__ uint32_t s_ticket;
-    __shared__ int s_osig[kBW][64];   // each wave's chunk operator, then each wave's carry
+    __shared__ int s_osig[kBW][64];   // each chunk's operator (group g of wave w at [w][g*NP..]), then its carry
     __shared__ cf s_om[kBW][64];
     __shared__ cf s_ov[kBW][64];
     __shared__ cf s_k[kBW][64];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int g = (G == 1) ? 0 : lane / NP, i = (G == 1) ? lane : lane % NP, gbase = g * NP;
     if (threadIdx.x == 0)
         s_ticket = atomicAdd(&a.hdr->ticket, 1u);
 #pragma unroll
@@ -346,58 +406,72 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
     const uint32_t tile = u / S32, seq32 = u - tile * S32;
     if (u >= a.total)
         return;
-    // The sequence's first tile may have fewer than kBW chunks: a wave without
-    // one runs chunk 0's loads and arithmetic to no effect (its operator is
-    // the identity and it stores nothing), so that it meets the barriers.
-    const int64_t c_own = a.nch - 1 - ((int64_t)tile * kBW + wave);
+    // The tile's chunks from the right: wave w holds the G chunks from
+    // c_w on (group g the g-th, in time order).  The sequence's first tile
+    // may have fewer than TC chunks: a lane group without one runs chunk 0's
+    // loads and arithmetic to no effect (its operator is the identity and it
+    // stores nothing), so that its wave meets the barriers.
+    const int64_t c_w = a.nch - 1 - (int64_t)tile * TC - (int64_t)wave * G - (G - 1);
+    const int64_t c_own = c_w + g;
     const bool has = c_own >= 0;
     const int64_t c = has ? c_own : 0;
+    const int64_t tw = (c_w > 0 ? c_w : 0) * kBT;   // the wave's first step
     const uint32_t epoch = a.hdr->epoch;
     const int64_t seq = seq32, t0 = c * kBT, h = seq32 % (uint32_t)a.H;
-    const int64_t rec = seq * a.nch + c;
-    const int nv = (int)min((int64_t)kBT, a.L - t0);
+    const int nv = (int)min((int64_t)kBT, a.L - t0);             // steps of the lane's chunk
+    const int nvw = (int)min((int64_t)WS, a.L - tw);             // steps of the wave
+    const int sofs = (int)(t0 - tw);                             // the chunk's first step in the wave's
     const int N = a.N;
-    char *const regp = reinterpret_cast<char *>(&s_reg[wave][0][0]);
-    const char *const rowbase = regp + lane * (int)sizeof(cf);
+    char *const regp = reinterpret_cast<char *>(&s_reg[wave][0][0]) + gbase * (int)sizeof(cf);
+    const char *const rowbase = regp + i * (int)sizeof(cf);
 
-    using IO = ChunkIO<CPLX, BCBF>;
+    using IO = ChunkIO<NP, CPLX, BCBF>;
     using Raw = typename RawOf<CPLX, BCBF>::type;
     using DRaw = typename IO::DRaw;
     using Stored = typename IO::Stored;
     IO io;
-    io.init(a, seq, t0, nv, h, lane);
+    io.init(a, seq, tw, t0, h, i);
     const bool idx = index_mode(a.sel_mode);
-    const int kraw = idx ? sel_raw(a.sel, a.sel_mode, seq * a.L + t0, nv, lane) : 0;
-    const uint32_t gyr = chunk_gy_raw(a, seq * a.L + t0, nv, lane);
-    auto sel_at = [&](int ts) { return __builtin_amdgcn_readfirstlane((int)s_sel[wave][ts]); };
+    const int kraw = idx ? sel_raw(a.sel, a.sel_mode, seq * a.L + tw, nvw, lane) : 0;
+    const uint32_t gyr = chunk_gy_raw(a, seq * a.L + tw, nvw, lane);
+    // the selection of step ts of the lane's chunk
+    auto sel_at = [&](int ts) {
+        if constexpr (G == 1)
+            return __builtin_amdgcn_readfirstlane((int)s_sel[wave][ts]);
+        else
+            return (int)s_sel[wave][sofs + ts];
+    };
 
-    // ---- 1. loads: every d row of the chunk (kept for both passes), the
-    // first D rows of b and c, the carry-in state; then the selections.
+    // ---- 1. loads: every d row of the chunk (kept for both passes) and
+    // every c row (kept for the operator and the backward pass), the first D
+    // rows of b, the carry-in state; then the selections.
     constexpr int D = PDSSM_BWD_GRAD_D;
     cf ds[kBT];
+    Raw cs[kBT];
 #pragma unroll
-    for (int tt = 0; tt < kBT; ++tt)
-        ds[tt] = io.d(min(tt, nv - 1));
-    Raw rb[D], rc[D];
+    for (int tt = 0; tt < kBT; ++tt) {
+        ds[tt] = io.d(tt, min(tt, nv - 1));
+        cs[tt] = io.raw_c(tt, min(tt, nv - 1));
+    }
+    Raw rb[D];
     uint32_t re[D];
 #pragma unroll
-    for (int tt = 0; tt < D; ++tt) {
-        rb[tt] = io.raw_b(min(tt, nv - 1));
-        rc[tt] = io.raw_c(min(tt, nv - 1));
-    }
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.xch + rec * N * NC, (uint64_t)N * sizeof(DRaw));
-    cf xin;
-    {
-        const DRaw v = bload<DRaw>(rx, io.vd, 0);
-        if constexpr (CPLX)
+    for (int tt = 0; tt < D; ++tt)
+        rb[tt] = io.raw_b(tt, min(tt, nv - 1));
+    cf xin = {0.f, 0.f};
+    if (i < N) {
+        const int64_t xe = (seq * a.nch + c) * N + i;
+        if constexpr (CPLX) {
+            const float2 v = reinterpret_cast<const float2 *>(a.xch)[xe];
             xin = {v.x, v.y};
-        else
-            xin = {v, 0.f};
+        } else {
+            xin = {a.xch[xe], 0.f};
+        }
     }
     if (idx)
-        sel_put(kraw, a.K, nv, s_sel[wave], lane);
+        sel_put<WS>(kraw, a.K, nvw, s_sel[wave], lane);
     else
-        wave_select<kBT>(a.sel, a.sel_mode, a.K, a.L, seq * a.L, t0, s_sel[wave], lane);
+        wave_select<WS>(a.sel, a.sel_mode, a.K, a.L, seq * a.L, tw, s_sel[wave], lane);
 #pragma unroll
     for (int tt = 0; tt < D; ++tt)
         re[tt] = io.ent(sel_at(min(tt, nv - 1)));
@@ -407,7 +481,6 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
     // it sits after step t, dacc its factor; the readout weight of step t is
     // g_t[j] = c_t[pacc_t[j]] dacc_t[j] and v = sum_t gy_t conj(g_t).
     cf xs[kBT];
-    Raw cs[kBT];
     uint32_t pis[kBT / 4] = {};
     cf x = xin;
     int pacc4 = lane * 4;
@@ -415,16 +488,14 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
 #pragma unroll
     for (int tt = 0; tt < kBT; ++tt) {
         const cf d = ds[tt];
-        const Raw braw = rb[tt % D], craw = rc[tt % D];
+        const Raw braw = rb[tt % D], craw = cs[tt];
         const uint32_t ent = re[tt % D];
         if (tt + D < kBT) {
             const int ts = min(tt + D, nv - 1);
-            rb[tt % D] = io.raw_b(ts);
-            rc[tt % D] = io.raw_c(ts);
+            rb[tt % D] = io.raw_b(tt + D, ts);
             re[tt % D] = io.ent(sel_at(ts));
         }
         pis[tt / 4] |= (ent & 63u) << (8 * (tt % 4));
-        cs[tt] = craw;
         if (tt < nv) {
             // the operator: gathers at the previous position (no dependence on x)
             const uint32_t np = bperm_a(ent & 63u, pacc4);
@@ -456,35 +527,41 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
             lds_order();
             x = sum;
             dacc = cmul(dd, dacc);
-            pacc4 = (int)(np << 2);
-            const float g = gy_step(a, gyr, tt);
+            pacc4 = (int)((np + gbase) << 2);
+            const float gq = gy_step<G>(a, gyr, (G == 1) ? tt : sofs + tt);
             const cf cg = unpack_c<CPLX, BCBF>(bperm_raw<CPLX, BCBF>(craw, pacc4));
             const cf w = cmul(cg, dacc);
-            v.r += g * w.r;
-            v.i -= g * w.i;
+            v.r += gq * w.r;
+            v.i -= gq * w.i;
         }
         xs[tt] = x;
     }
-    // ---- 3. the tile's carries.  The waves' operators meet in LDS; wave 0
+
+    // ---- 3. the tile's carries.  The chunks' operators meet in LDS; wave 0
     // composes the tile's operator (the leftmost chunk's applied last), looks
     // back over the tiles on the right for the adjoint carried into the tile,
-    // and hands every wave the adjoint carried into its chunk.
-    s_osig[wave][lane] = has ? (pacc4 >> 2) : lane;
+    // and hands every chunk the adjoint carried into it.  Chunk k of the tile
+    // (from the right) is group G-1-(k mod G) of wave k / G; wave 0 works on
+    // NP-lane operators, its lane groups all holding the same copy.
+    s_osig[wave][lane] = has ? ((pacc4 >> 2) - gbase) : i;
     s_om[wave][lane] = has ? cf{dacc.r, -dacc.i} : cf{1.f, 0.f};
     s_ov[wave][lane] = has ? v : cf{0.f, 0.f};
     __syncthreads();
     if (wave == 0) {
-        auto op_of = [&](int w) { return GOp{s_osig[w][lane], s_om[w][lane], s_ov[w][lane]}; };
+        auto op_of = [&](int k) {
+            const int w = k / G, at = (G - 1 - k % G) * NP + i;
+            return GOp{s_osig[w][at], s_om[w][at], s_ov[w][at]};
+        };
         const int64_t seq_rec = seq * a.tiles, trec = seq_rec + tile;
         cf K = {0.f, 0.f};
         if (tile == 0) {
-            if (a.gxf && lane < N)
-                K = load_diag<CPLX>(a.gxf, seq * N + lane);   // the adjoint after the last step
+            if (a.gxf && i < N)
+                K = load_diag<CPLX>(a.gxf, seq * N + i);   // the adjoint after the last step
         } else {
             GOp tagg = op_of(0);
 #pragma unroll
-            for (int w = 1; w < kBW; ++w)
-                tagg = compose_left<CPLX>(op_of(w), tagg);
+            for (int k = 1; k < TC; ++k)
+                tagg = compose_left<CPLX>(op_of(k), tagg);
             // words: sig, m.r, v.r (, m.i, v.i)
             uint64_t *const aw_own = a.agg + trec * (AW * 64);
             put_word(aw_own + lane, (uint32_t)tagg.sig, epoch);
@@ -494,7 +571,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
                 put_word(aw_own + 192 + lane, __float_as_uint(tagg.m.i), epoch);
                 put_word(aw_own + 256 + lane, __float_as_uint(tagg.v.i), epoch);
             }
-            GOp acc = {lane, {1.f, 0.f}, {0.f, 0.f}};   // the tiles tile-1 .. j+1, composed
+            GOp acc = {i, {1.f, 0.f}, {0.f, 0.f}};   // the tiles tile-1 .. j+1, composed
             int64_t j = tile - 1;
             uint32_t spins = 0;
             while (true) {
@@ -527,7 +604,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
                         okb = get_word(aw + k * 64 + lane, epoch, q[k]) && okb;
                     if (__all(okb)) {
                         GOp opj;
-                        opj.sig = (int)min(q[0], 63u);
+                        opj.sig = (int)min(q[0], (uint32_t)(NP - 1));
                         opj.m = {__uint_as_float(q[1]), CPLX ? __uint_as_float(q[3]) : 0.f};
                         opj.v = {__uint_as_float(q[2]), CPLX ? __uint_as_float(q[4]) : 0.f};
                         acc = compose_left<CPLX>(acc, opj);
@@ -546,10 +623,11 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
         // ---- 4. every chunk's carry, then the tile's carry-out (gx0 for
         // the sequence's first tile)
 #pragma unroll
-        for (int w = 0; w < kBW; ++w) {
-            const GOp ow = op_of(w);
-            s_k[w][lane] = K;
-            K = apply_op<CPLX>(ow, K);
+        for (int k = 0; k < TC; ++k) {
+            const GOp ok = op_of(k);
+            if (lane < NP)
+                s_k[k / G][(G - 1 - k % G) * NP + lane] = K;
+            K = apply_op<CPLX>(ok, K);
         }
         if (tile + 1 < a.tiles) {
             uint64_t *const iw_own = a.incl + trec * (NC * 64);
@@ -561,13 +639,17 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
         }
     }
     __syncthreads();
-    if (!has)
-        return;
+    if (G == 1 && !has)
+        return;   // the whole wave is idle
+    // With several chunks per wave an idle lane group stays to the end: the
+    // other groups gather their upstream gradients from its lanes.  Its
+    // stores are dropped.
+    io.act = io.act && has;
     const cf K = s_k[wave][lane];
 
     // ---- 5. backward through the chunk from K, writing the gradients
-    const int64_t e0 = (seq * a.L + t0) * N;
-    const uint64_t rows = (uint64_t)nv * (uint64_t)N;
+    const int64_t e0 = (seq * a.L + tw) * N;
+    const uint64_t rows = (uint64_t)nvw * (uint64_t)N;
     const __amdgpu_buffer_rsrc_t ogb = make_rsrc(reinterpret_cast<Stored *>(a.gb) + e0, rows * sizeof(Stored));
     const __amdgpu_buffer_rsrc_t ogc = make_rsrc(reinterpret_cast<Stored *>(a.gc) + e0, rows * sizeof(Stored));
     const __amdgpu_buffer_rsrc_t ogd = make_rsrc(reinterpret_cast<DRaw *>(a.gd) + e0, rows * sizeof(DRaw));
@@ -579,19 +661,20 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
         const cf cv = unpack_c<CPLX, BCBF>(cs[tt]);
         const uint32_t ent = pis[tt / 4] >> (8 * (tt % 4));
         if (tt < nv) {
-            const float g = gy_step(a, gyr, tt);
-            const cf lam = {lc.r + g * cv.r, lc.i - g * cv.i};
-            const int pi4 = (int)((ent & 63u) << 2);
+            const float gq = gy_step<G>(a, gyr, (G == 1) ? tt : sofs + tt);
+            const cf lam = {lc.r + gq * cv.r, lc.i - gq * cv.i};
+            const int pi4 = (int)(((ent & 63u) + gbase) << 2);
             cf lg;
             lg.r = bperm_a(lam.r, pi4);
             lg.i = CPLX ? bperm_a(lam.i, pi4) : 0.f;
             const cf xt = xs[tt];
             const cf xp = (tt > 0) ? xs[tt > 0 ? tt - 1 : 0] : xin;
-            const uint32_t rs = (uint32_t)(tt * N * (int)sizeof(Stored));
-            bstore<Stored>(ogb, pack_vec<CPLX, BCBF>(lam), io.vs, rs);
-            bstore<Stored>(ogc, pack_vec<CPLX, BCBF>(cf{g * xt.r, -g * xt.i}), io.vs, rs);
-            bstore<DRaw>(ogd, pack_d<CPLX>(cf{xp.r * lg.r + xp.i * lg.i, xp.r * lg.i - xp.i * lg.r}), io.vd,
-                         (uint32_t)(tt * N * (int)sizeof(DRaw)));
+            uint32_t vo, so;
+            io.template store_offs<Stored>(tt, io.vs, vo, so);
+            bstore<Stored>(ogb, pack_vec<CPLX, BCBF>(lam), vo, so);
+            bstore<Stored>(ogc, pack_vec<CPLX, BCBF>(cf{gq * xt.r, -gq * xt.i}), vo, so);
+            io.template store_offs<DRaw>(tt, io.vd, vo, so);
+            bstore<DRaw>(ogd, pack_d<CPLX>(cf{xp.r * lg.r + xp.i * lg.i, xp.r * lg.i - xp.i * lg.r}), vo, so);
             lc = {d.r * lg.r + d.i * lg.i, d.r * lg.i - d.i * lg.r};
         }
     }
@@ -601,24 +684,44 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
 // Host side.
 // ---------------------------------------------------------------------------
 struct BwdLayout {
+    int NP;
     int64_t nch, S, tiles, tab_bytes, agg_bytes, incl_bytes, total;
 };
 
-// Workspace: header | entry table [H][K][64] | operator records | carry records.
-static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t L, int32_t K, uint32_t flags)
+// Lanes per chunk: N padded to 16, 32 or 64 (a wave runs 64 / NP chunks).
+static int bwd_lanes(int N) { return N <= 16 ? 16 : N <= 32 ? 32 : 64; }
+
+// Workspace: header | entry table [H][K][NP] | operator records | carry records.
+static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K, uint32_t flags)
 {
     BwdLayout lo;
     const int nc = (flags & PDSSM_COMPLEX) ? 2 : 1;
+    lo.NP = bwd_lanes(N);
     lo.S = B * H;
     lo.nch = (L + kBT - 1) / kBT;
-    lo.tiles = (lo.nch + kBW - 1) / kBW;
+    const int64_t tc = (int64_t)kBW * (64 / lo.NP);   // chunks per tile
+    lo.tiles = (lo.nch + tc - 1) / tc;
     const int64_t recs = lo.S * lo.tiles;
     auto up = [](int64_t n) { return (n + 255) / 256 * 256; };
-    lo.tab_bytes = up(H * (int64_t)K * 64 * 2);
+    lo.tab_bytes = up(H * (int64_t)K * lo.NP * 2);
     lo.agg_bytes = up(recs * 64 * (1 + 2 * nc) * 8);
     lo.incl_bytes = up(recs * 64 * nc * 8);
     lo.total = (int64_t)sizeof(Header) + lo.tab_bytes + lo.agg_bytes + lo.incl_bytes;
     return lo;
+}
+
+template <int NP>
+static void launch_fused(const BwdArgs &a, bool cplx, bool bcbf, hipStream_t st)
+{
+    const dim3 grid(a.total), blk(kBW * 64);
+    if (cplx && bcbf)
+        hipLaunchKernelGGL((bwd_fused_kernel<NP, true, true>), grid, blk, 0, st, a);
+    else if (cplx)
+        hipLaunchKernelGGL((bwd_fused_kernel<NP, true, false>), grid, blk, 0, st, a);
+    else if (bcbf)
+        hipLaunchKernelGGL((bwd_fused_kernel<NP, false, true>), grid, blk, 0, st, a);
+    else
+        hipLaunchKernelGGL((bwd_fused_kernel<NP, false, false>), grid, blk, 0, st, a);
 }
 
 }  // namespace pdssm
@@ -630,7 +733,7 @@ extern "C" size_t pdssm_scan_bwd_workspace_bytes(int64_t B, int64_t H, int64_t L
 {
     if (check_dims(B, H, L, N, K) != PDSSM_OK || (flags & ~PDSSM_FLAGS_ALL))
         return 0;
-    return (size_t)bwd_layout(B, H, L, K, flags).total;
+    return (size_t)bwd_layout(B, H, L, N, K, flags).total;
 }
 
 extern "C" int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
@@ -662,7 +765,7 @@ extern "C" int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx
     for (const void *p : ptrs)
         if (p && !aligned16(p))
             return PDSSM_ERR_ALIGN;
-    const BwdLayout lo = bwd_layout(B, H, L, K, flags);
+    const BwdLayout lo = bwd_layout(B, H, L, N, K, flags);
     if (workspace_bytes < (size_t)lo.total)
         return PDSSM_ERR_WORKSPACE;
     if ((double)lo.S * (double)lo.tiles > 4.0e9)
@@ -699,19 +802,15 @@ extern "C" int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx
     a.y_bf16 = (flags & PDSSM_Y_BF16) ? 1 : 0;
 
     // New epoch and ticket, the entry table; on first use every record is cleared.
-    rc = launch_prep(a.hdr, a.agg, (lo.agg_bytes + lo.incl_bytes) / 16, dict_idx, tab, H * (int64_t)K, N, 64,
+    rc = launch_prep(a.hdr, a.agg, (lo.agg_bytes + lo.incl_bytes) / 16, dict_idx, tab, H * (int64_t)K, N, lo.NP,
                      stream);
     if (rc != PDSSM_OK)
         return rc;
     const bool cplx = flags & PDSSM_COMPLEX, bcbf = flags & PDSSM_BC_BF16;
-    const dim3 grid(a.total), blk(kBW * 64);
-    if (cplx && bcbf)
-        hipLaunchKernelGGL((bwd_fused_kernel<true, true>), grid, blk, 0, stream, a);
-    else if (cplx)
-        hipLaunchKernelGGL((bwd_fused_kernel<true, false>), grid, blk, 0, stream, a);
-    else if (bcbf)
-        hipLaunchKernelGGL((bwd_fused_kernel<false, true>), grid, blk, 0, stream, a);
-    else
-        hipLaunchKernelGGL((bwd_fused_kernel<false, false>), grid, blk, 0, stream, a);
+    switch (lo.NP) {
+    case 16: launch_fused<16>(a, cplx, bcbf, stream); break;
+    case 32: launch_fused<32>(a, cplx, bcbf, stream); break;
+    default: launch_fused<64>(a, cplx, bcbf, stream); break;
+    }
     return hip_status(hipGetLastError());
 }
