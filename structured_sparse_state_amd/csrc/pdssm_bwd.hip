@@ -40,7 +40,10 @@
 namespace pdssm {
 
 constexpr int kBT = kCarryStride;   // steps per chunk (the forward saves one carry per chunk)
-constexpr int kBW = 4;              // chunk waves per workgroup
+#ifndef PDSSM_BWD_W
+#define PDSSM_BWD_W 4   // chunk waves per workgroup (one tile)
+#endif
+constexpr int kBW = PDSSM_BWD_W;
 #ifndef PDSSM_BWD_GRAD_D
 #define PDSSM_BWD_GRAD_D 4   // steps of b and c in flight per wave
 #endif
