@@ -141,7 +141,10 @@ struct ChunkIO {
     {
         N = a.N;
         const int64_t e0 = (seq * a.L + tw) * a.N;   // first element of the wave's rows
-        const uint64_t rows = (uint64_t)(a.L - tw) * (uint64_t)a.N;
+        // The wave's rows only (at most 64 steps): padding lanes' offsets
+        // (kOffLane, 2 GiB) must stay beyond the range.
+        const int64_t wrows = (a.L - tw < (int64_t)(G * kBT)) ? a.L - tw : (int64_t)(G * kBT);
+        const uint64_t rows = (uint64_t)wrows * (uint64_t)a.N;
         rd = make_rsrc(reinterpret_cast<const DRaw *>(a.diag) + e0, rows * sizeof(DRaw));
         rb = make_rsrc(reinterpret_cast<const Stored *>(a.b) + e0, rows * sizeof(Stored));
         rc = make_rsrc(reinterpret_cast<const Stored *>(a.c) + e0, rows * sizeof(Stored));
