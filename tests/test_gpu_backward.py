@@ -195,3 +195,35 @@ def test_bwd_linear_in_upstream(orc):
         ref = (a + 2 * b).double()
         err = ((c.double() - ref).abs().max() / ref.abs().max()).item()
         assert err < 1e-5, err
+
+
+def test_bwd_rows_beyond_2gib(orc):
+    """One sequence whose rows span more than 2 GiB, with padding lanes
+    (N = 33 in 64 lanes, complex fp32 rows, 8.3M steps): the padding lanes'
+    accesses must stay dropped however long the sequence.  The last steps'
+    gradients against the oracle: its forward over the prefix gives the state
+    before them, its backward over them the gradients."""
+    N, L, M = 33, 8_300_000, 1024
+    say(f"[case] bwd rows beyond 2 GiB: N={N} L={L}")
+    g = gen.make_inputs("long", B=1, H=1, L=L, N=N, seed=77, device=DEV)
+    gy, gxf = gen.make_grads(g, seed=3)
+    _, _, xch = pk.scan_save(g)
+    gb, gc, gd, gx0 = pk.scan_bwd(g, xch, gy, gxf)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(gb).all()) and bool(torch.isfinite(gd).all())
+    host = g.to("cpu")
+    cut = L - M
+    _, x_cut = orc.scan(host.sel_or_logits[:, :, :cut], host.sel_mode, host.dict_idx, host.diag[:, :, :cut],
+                        host.b[:, :, :cut], host.c[:, :, :cut], complex=True, bc_bf16=False, nthreads=8)
+    say("  oracle prefix forward done")
+    x0 = np.stack([x_cut.real, x_cut.imag], axis=-1).astype(np.float32)
+    ref = orc.scan_bwd(host.sel_or_logits[:, :, cut:], host.sel_mode, host.dict_idx, host.diag[:, :, cut:],
+                       host.b[:, :, cut:], host.c[:, :, cut:], gy[:, :, cut:].cpu(), complex=True,
+                       bc_bf16=False, x0=x0, gxf=x_to_np(gxf, True))
+    tol = tol_of(g)
+    for name, got, r in zip(("gb", "gc", "gd"), (gb, gc, gd), ref[:3]):
+        e = per_seq_err(grad_to_np(got[:, :, cut:], True), r)
+        say(f"  tail {name} error {e:.2e}")
+        assert e <= tol, (name, e)
+    del g, host, gb, gc, gd, gx0, xch
+    torch.cuda.empty_cache()
