@@ -66,7 +66,7 @@ struct BwdArgs {
     uint64_t *agg;      // [S*tiles][AW][64] each tile's adjoint operator, epoch-tagged words
     uint64_t *incl;     // [S*tiles][NC][64] the adjoint each tile carries out of its first step
     uint32_t total;     // tickets: S * tiles
-    int64_t tiles;      // tiles of kBW chunks per sequence
+    int64_t tiles;      // tiles per sequence (kBW * 64 / NP chunks each)
     int64_t H, L, S, nch;
     int N, K;
     uint32_t sel_mode;
@@ -346,12 +346,13 @@ __device__ __forceinline__ cf apply_op(GOp op, cf k)
 }
 
 // ---------------------------------------------------------------------------
-// bwd_fused: the whole backward in one pass over the inputs.  Each wave owns
-// one chunk of kBT steps, a workgroup a tile of kBW consecutive chunks.
+// bwd_fused: the whole backward in one pass over the inputs.  A lane group
+// of NP lanes owns one chunk of kBT steps (64 / NP chunks per wave), a
+// workgroup a tile of kBW * 64 / NP consecutive chunks.
 // Workgroups take tickets in reverse time order (the last tiles of every
 // sequence first), so every tile to the right of a workgroup's tile belongs
 // to a workgroup that has started, and a workgroup only ever waits for
-// those.  A wave
+// those.  Each lane group
 //  1. loads its chunk's rows and selections (picking them from the scores in
 //     the logits modes),
 //  2. runs forward through the chunk: the states x_t from the saved carry-in
