@@ -82,10 +82,6 @@ constexpr int kScanD = PDSSM_SCAN_D;   // steps of inputs in flight per lane (re
 static_assert(kScanW >= 1 && kScanW <= 32, "chunk waves post into a 32-bit mask");
 static_assert(kScanT == kCarryStride, "the saved carries are one per chunk of the backward scan");
 constexpr int kDictLdsMax = 32768;   // bytes of the head's entry table kept in LDS
-#ifndef PDSSM_POLL_TICKS
-#define PDSSM_POLL_TICKS 80
-#endif
-constexpr uint64_t kPollTicks = PDSSM_POLL_TICKS;   // look-back loads are used this long (realtime ticks, 10 ns) after issue
 // The carry wave's nap between polls (s_sleep units of 64 clocks): it shares
 // its SIMD with chunk waves, so it should not spin.
 #ifndef PDSSM_CARRY_NAP
@@ -198,10 +194,13 @@ __device__ __forceinline__ typename RawVec<CPLX, BCBF>::type bperm_raw(typename 
 // e), INCL = the state after the tile.
 //
 // LookBack gathers the carry into a tile: (bpi, bd, be) = tiles j+1 ..
-// tile-1 composed (latest last); it ends at the first INCL found.  Each
-// poll reads one word of tile j's INCL (lane 0) and of its AGG (lane 1); a
-// record is read whole only once that word is from this call, and read
-// again if any of its words is not yet.
+// tile-1 composed (latest last); it ends at the first INCL found.  One
+// attempt reads tile j's INCL and AGG records whole, in one round trip (two
+// and five words per lane), and takes the INCL if every word of it is from
+// this call, else the AGG if every word of that is; otherwise it tries the
+// same tile again.  The carry wave issues no store while an attempt is in
+// flight: on this GPU one counter tracks loads and stores alike, so waiting
+// for the attempt's loads would also wait for the stores to complete.
 // ---------------------------------------------------------------------------
 template <int NP, bool CPLX>
 struct LookBack {
@@ -211,11 +210,6 @@ struct LookBack {
     int bpi = 0;
     cf bd = {1.f, 0.f}, be = {0.f, 0.f}, xin = {0.f, 0.f};
     bool done = false;
-    // Loads in flight: 0 none, 1 the two poll words, 2 tile j's INCL, 3 its
-    // AGG; they are used once kPollTicks have passed (or when asked to wait).
-    int phase = 0;
-    uint64_t t_issue = 0;
-    uint64_t w[1 + 2 * NC];
 
     __device__ void start(const ScanArgs &a, int64_t tile, int64_t sq, int lane)
     {
@@ -226,7 +220,6 @@ struct LookBack {
         xin = {0.f, 0.f};
         j = tile - 1;
         done = tile == 0;
-        phase = 0;
         if (done && a.x0 && lane < a.N)
             xin = load_diag<CPLX>(a.x0, sq * a.N + lane);
     }
@@ -236,90 +229,52 @@ struct LookBack {
         return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __device__ static bool from(uint64_t word, uint32_t epoch) { return (uint32_t)(word >> 32) == epoch; }
+    __device__ static float val(uint64_t word) { return __uint_as_float((uint32_t)word); }
 
-    // Advance by at most one action; true when it made progress (found the
-    // INCL or took an AGG).  With wait == false it never waits on a load.
-    __device__ bool poll(const ScanArgs &a, uint32_t epoch, int lane, cf *scr, bool wait)
+    // One attempt; true when it made progress (found the INCL or took an AGG).
+    __device__ bool attempt(const ScanArgs &a, uint32_t epoch, int lane, cf *scr)
     {
         if (done)
             return false;
         const bool act = lane < NP;
+        const bool has_agg = j > 0;   // tile 0 publishes no AGG (it knows its carry)
         const int64_t rj = j * a.S + seq;
         const uint64_t *iw = a.incl + rj * IW;
         const uint64_t *aw = a.agg + rj * AW;
-        if (phase == 0) {
-            // One word of tile j's INCL (lane 0) and of its AGG (lane 1).
-            w[0] = 0;
-            if (lane == 0)
-                w[0] = load(iw);
-            else if (lane == 1 && j > 0)
-                w[0] = load(aw);
-            phase = 1;
-            t_issue = __builtin_amdgcn_s_memrealtime();
-            return false;
-        }
-        if (!wait && __builtin_amdgcn_s_memrealtime() - t_issue < kPollTicks)
-            return false;
-        if (phase == 1) {
-            const uint64_t ready = __ballot((lane == 0 || (lane == 1 && j > 0)) && from(w[0], epoch));
-            if (ready & 1) {
-                // The whole INCL record.
-                if (act) {
-                    w[0] = load(iw + lane * NC);
-                    if constexpr (CPLX)
-                        w[1] = load(iw + lane * NC + 1);
-                }
-                phase = 2;
-            } else if (ready & 2) {
-                // The whole AGG record.
-                if (act) {
-                    w[0] = load(aw + lane);
-                    w[1] = load(aw + NP + lane * NC);
-                    w[2] = load(aw + NP + NP * NC + lane * NC);
-                    if constexpr (CPLX) {
-                        w[3] = load(aw + NP + lane * NC + 1);
-                        w[4] = load(aw + NP + NP * NC + lane * NC + 1);
-                    }
-                }
-                phase = 3;
-            } else {
-                phase = 0;
-                return false;
-            }
-            t_issue = __builtin_amdgcn_s_memrealtime();
-            return false;
-        }
-        if (phase == 2) {
-            bool ok = true;
-            cf X = {0.f, 0.f};
-            if (act) {
-                ok = from(w[0], epoch);
-                if constexpr (CPLX)
-                    ok = ok && from(w[1], epoch);
-                X = {__uint_as_float((uint32_t)w[0]), CPLX ? __uint_as_float((uint32_t)w[1]) : 0.f};
-            }
-            phase = 0;
-            if (__all(ok)) {
-                xin = scatter_add<CPLX>(scr, lane, 0, bpi, cmul(bd, X), be);
-                done = true;
-                return true;
-            }
-            return false;
-        }
-        // phase == 3: an AGG record
-        bool ok = true;
-        int p = lane;
-        cf d = {1.f, 0.f}, e = {0.f, 0.f};
+        // Words of other calls never match the epoch, so lanes that load
+        // nothing start from a word that cannot pass for a loaded one.
+        uint64_t i0 = 0, i1 = 0, a0 = 0, a1 = 0, a2 = 0, a3 = 0, a4 = 0;
         if (act) {
-            ok = from(w[0], epoch) && from(w[1], epoch) && from(w[2], epoch);
+            i0 = load(iw + lane * NC);
             if constexpr (CPLX)
-                ok = ok && from(w[3], epoch) && from(w[4], epoch);
-            p = (int)min((uint32_t)w[0], (uint32_t)(NP - 1));
-            d = {__uint_as_float((uint32_t)w[1]), CPLX ? __uint_as_float((uint32_t)w[3]) : 0.f};
-            e = {__uint_as_float((uint32_t)w[2]), CPLX ? __uint_as_float((uint32_t)w[4]) : 0.f};
+                i1 = load(iw + lane * NC + 1);
+            if (has_agg) {
+                a0 = load(aw + lane);
+                a1 = load(aw + NP + lane * NC);
+                a2 = load(aw + NP + NP * NC + lane * NC);
+                if constexpr (CPLX) {
+                    a3 = load(aw + NP + lane * NC + 1);
+                    a4 = load(aw + NP + NP * NC + lane * NC + 1);
+                }
+            }
         }
-        phase = 0;
-        if (__all(ok)) {
+        const bool iok = !act || (from(i0, epoch) && (!CPLX || from(i1, epoch)));
+        if (__all(iok)) {
+            const cf X = {act ? val(i0) : 0.f, (CPLX && act) ? val(i1) : 0.f};
+            xin = scatter_add<CPLX>(scr, lane, 0, bpi, cmul(bd, X), be);
+            done = true;
+            return true;
+        }
+        const bool aok = !act || (from(a0, epoch) && from(a1, epoch) && from(a2, epoch) &&
+                                  (!CPLX || (from(a3, epoch) && from(a4, epoch))));
+        if (has_agg && __all(aok)) {
+            int p = lane;
+            cf d = {1.f, 0.f}, e = {0.f, 0.f};
+            if (act) {
+                p = (int)min((uint32_t)a0, (uint32_t)(NP - 1));
+                d = {val(a1), CPLX ? val(a3) : 0.f};
+                e = {val(a2), CPLX ? val(a4) : 0.f};
+            }
             // acc <- acc o agg_j  (acc is later in time)
             const int npi = bperm(bpi, p);
             cf gd;
@@ -336,14 +291,15 @@ struct LookBack {
     }
 };
 
-// Publish a tile's AGG record (tile > 0 only; tile 0 knows its carry).
+// Publish a tile's AGG record (tile > 0 only; tile 0 knows its carry); `i`
+// is the state the calling lane holds, and only lanes with `act` store.
 template <int NP, bool CPLX>
-__device__ void publish_agg(const ScanArgs &a, int64_t tile, int64_t seq, uint32_t epoch, int lane, int api,
-                            cf ad, cf ae)
+__device__ void publish_agg(const ScanArgs &a, int64_t tile, int64_t seq, uint32_t epoch, int lane, bool act,
+                            int api, cf ad, cf ae)
 {
     constexpr int NC = CPLX ? 2 : 1;
     uint64_t *aw = a.agg + (tile * a.S + seq) * agg_words<NP, CPLX>();
-    if (lane < NP) {
+    if (act) {
         put_word(aw + lane, (uint32_t)api, epoch);
         put_word(aw + NP + lane * NC, __float_as_uint(ad.r), epoch);
         put_word(aw + NP + NP * NC + lane * NC, __float_as_uint(ae.r), epoch);
@@ -435,6 +391,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
     __shared__ float s_q[TILE];   // per step: sum_j Re(c_t[j] x_loc_t[j]), until the correction
     __shared__ uint32_t s_next;   // ticket published by the carry wave
     __shared__ uint32_t s_ready;  // bit w: chunk wave w has posted its inclusive prefixes
+    __shared__ uint32_t s_known;  // 1 + index (in this workgroup) of the last tile whose carry is known
 
     // Tile indices, sequences and heads fit 32 bits (the host checks).
     const uint32_t S32 = (uint32_t)a.S, H32 = (uint32_t)a.H;
@@ -484,6 +441,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         if (lane == 0) {
             s_next = cur;
             s_ready = 0;
+            s_known = 0;
         }
         const uint32_t epoch = a.hdr->epoch;
         __syncthreads();   // (P) first ticket published
@@ -509,7 +467,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         cf *scr = s_cscr;
         bool have_prev = false;
         LookBack<NP, CPLX> lb;
-        while (true) {
+        for (uint32_t iter = 1;; ++iter) {
             // The next ticket; its value is needed only at (B).
             uint32_t tk = 0;
             if (lane == 0)
@@ -521,14 +479,18 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             // ---- a4 while the chunk waves run their local pass and chain
             // their prefixes: look back for the carry into this tile, which
             // depends only on earlier tiles, until every chunk wave has
-            // posted (then the aggregate is known).
+            // posted (then the aggregate is known).  Once the carry is known
+            // the tile needs no AGG record: the last chunk wave of the chain
+            // publishes one only while s_known is behind.
             while (!lb.done) {
                 const uint32_t posted = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile uint32_t *>(&s_ready));
                 if (posted == (1u << W) - 1u)
                     break;
-                if (!lb.poll(a, epoch, lane, scr, false))
+                if (!lb.attempt(a, epoch, lane, scr))
                     __builtin_amdgcn_s_sleep(PDSSM_CARRY_NAP);
             }
+            if (lb.done && lane == 0)
+                *reinterpret_cast<volatile uint32_t *>(&s_known) = iter;
             const uint32_t nxt = __builtin_amdgcn_readfirstlane(tk);
             if (lane == 0)
                 s_next = nxt;
@@ -557,23 +519,20 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             // head keeps its table).
             if (more && !pinned)
                 stage_table(nxt);
+            // ---- a4, second part: the carry if it is still unknown (the
+            // tile's AGG record is out), then the state after the tile.
+            while (!lb.done)
+                if (!lb.attempt(a, epoch, lane, scr))
+                    __builtin_amdgcn_s_sleep(PDSSM_CARRY_NAP);
+            // The next table has landed (it was staged before (B)), then the
+            // state after the tile goes out, then the previous tile's
+            // outputs; the stores need not complete here.
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            publish_incl<NP, CPLX>(a, tile, seq, epoch, lane, ppi, pd, pe, lb.xin, scr);
             if (have_prev)
 #pragma unroll
                 for (int w = 0; w < W; ++w)
                     store_y(w, yv[w]);
-            // ---- a4, second part: publish the tile's aggregate if the carry
-            // is still unknown (so later tiles need not wait for it), then the
-            // state after the tile.
-            if (!lb.done) {
-                publish_agg<NP, CPLX>(a, tile, seq, epoch, lane, ppi, pd, pe);
-                while (!lb.done)
-                    if (!lb.poll(a, epoch, lane, scr, true) && lb.phase == 0)
-                        __builtin_amdgcn_s_sleep(PDSSM_CARRY_NAP);
-            }
-            // The next table has landed (it was staged before (B)), then the
-            // state after the tile goes out; its stores need not complete here.
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            publish_incl<NP, CPLX>(a, tile, seq, epoch, lane, ppi, pd, pe, lb.xin, scr);
             s_xin[lane] = lb.xin;
             __syncthreads();   // (C) carry ready, next table staged
             __syncthreads();   // (D) chunk waves have read the prefixes and the carry
@@ -622,6 +581,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
     const int L = (int)a.L;   // steps fit 31 bits (the host checks)
     int64_t row0 = 0;         // index of the sequence's first step
     uint32_t cseq = 0;        // the sequence
+    uint32_t ctile = 0;       // the tile
     int tw0 = 0, wrow = 0;    // the wave's first step; the first buffer row
     bool full = false;        // every chunk of the wave lies inside the sequence
     uint32_t h = 0;
@@ -648,6 +608,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         decode(u, tile, seq);
         h = __builtin_amdgcn_readfirstlane(seq % H32);
         cseq = seq;
+        ctile = tile;
         row0 = (int64_t)seq * a.L;
         tw0 = (int)tile * TILE + chunk_pos(wave) * G * T;
         full = tw0 + G * T <= L;
@@ -704,12 +665,13 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
     uint32_t cur = __builtin_amdgcn_readfirstlane(s_next);
     if (cur >= total)
         return;
+    const uint32_t epoch = __builtin_amdgcn_readfirstlane(a.hdr->epoch);
     issue_scores(cur);
     issue_inputs();
     select();
     __syncthreads();   // (Q) first table and selections ready
 
-    while (true) {
+    for (uint32_t iter = 1;; ++iter) {
         const Lanes q = lanes();
         // ---- a2 + chunk-local a3: recurrence from zero state, and the
         // prefix operator of the chunk: source j of the chunk start sits at
@@ -722,7 +684,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         const int cw0 = tw0;                // the wave's first step
         const int tc0 = cw0 + q.g * T;      // first step of the chunk
         const int64_t y0 = row0 + cw0;      // y index of the wave's first step
-        const uint32_t seq0 = cseq;
+        const uint32_t seq0 = cseq, tile0 = ctile;
         const int nvalid = max(0, min(T, L - tc0));
         // The same bound, re-derived where it is tested again, so that the
         // compiler does not keep one test's outcome alive across blocks.
@@ -878,6 +840,8 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             __builtin_amdgcn_s_setprio(PDSSM_CARRY_PRIO);
             int ppi = 0;
             cf pd = {1.f, 0.f}, pe = {0.f, 0.f};
+            int api = opi;   // this lane's posted prefix (its group's last)
+            cf ad = dacc, ae = x;
             if (pos > 0) {
                 const uint32_t need = 1u << wave_at(pos - 1);
                 const int ps = wave_at(pos - 1) * 64 + (G - 1) * NP + q.i;
@@ -918,12 +882,24 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                     s_pi[slot] = rpi;
                     s_d[slot] = rd;
                     s_e[slot] = re;
+                    api = rpi;
+                    ad = rd;
+                    ae = re;
                 }
                 lds_order();
             }
             if (q.ln == 0)
                 __hip_atomic_fetch_or(&s_ready, 1u << wave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             __builtin_amdgcn_s_setprio(0);
+            // The last prefix of the tile is its aggregate.  While the
+            // tile's carry is unknown, later tiles may need it: publish the
+            // AGG record (its stores complete while this wave has nothing to
+            // wait for).
+            if (pos == W - 1 && tile0 > 0 && tile0 + 1 < a.n_tiles) {
+                const uint32_t known = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile uint32_t *>(&s_known));
+                if (known != iter)
+                    publish_agg<NP, CPLX>(a, tile0, seq0, epoch, q.i, q.g == G - 1, api, ad, ae);
+            }
         }
         __syncthreads();   // (B) all chunk operators taken, next ticket published
         const uint32_t nxt = __builtin_amdgcn_readfirstlane(s_next);
@@ -1003,11 +979,12 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         }
         if (!more)
             return;
-        // The next tile's first input steps (its scores have been in flight
-        // since (B)); issuing them only now keeps their registers free
-        // through the readout.
-        issue_inputs();
+        // The selection of the next tile (its scores have been in flight
+        // since (B)), then its first input steps: issued only now, they keep
+        // their registers free through the readout, and the selection's wait
+        // for the scores does not also wait for them.
         select();
+        issue_inputs();
         cur = nxt;
     }
 }
