@@ -226,11 +226,22 @@ def measure_aux(pk, gen, inp, stream):
 
 
 def cpu_threads() -> int:
+    """Every core this process may run on."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+    return max(1, n)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main() -> int:
@@ -252,6 +263,9 @@ def main() -> int:
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle over the batch for at least this long")
+    ap.add_argument("--settle-seconds", type=float, default=1.5,
+                    help="untimed scan calls for this long before the warm-up calls, so the GPU "
+                         "reaches its sustained clock whatever the warm-up count")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -283,7 +297,16 @@ def main() -> int:
         calls[0] += 1
 
     print(f"[bench] workload {args.workload}: B={B} H={H} L={L} N={N} K={K}; {nrot} input set(s); "
-          f"warmup {args.warmup}", file=sys.stderr, flush=True)
+          f"settle {args.settle_seconds} s, warmup {args.warmup}", file=sys.stderr, flush=True)
+    # Clock settle: the GPU needs a while under load to reach its sustained
+    # clock; without this phase the timed calls depend on the warm-up count.
+    settle_calls = 0
+    t_end = time.perf_counter() + args.settle_seconds
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            step()
+        settle_calls += 20
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -298,6 +321,9 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_call_ms = [ev[s].elapsed_time(ev[s + 1]) for s in range(args.steps)]
+    sorted_ms = sorted(per_call_ms)
+    median_us = sorted_ms[len(sorted_ms) // 2] * 1e3
+    min_us = sorted_ms[0] * 1e3
     total_ms = ev[0].elapsed_time(ev[-1])
     ms_per_step = total_ms / args.steps
     tokens = B * H * L
@@ -306,8 +332,8 @@ def main() -> int:
     avg_call_s = sum(per_call_ms) / len(per_call_ms) * 1e-3
     achieved = alg_bytes / avg_call_s / 1e9
     traffic = counter_traffic(alg_bytes, args.workload)
-    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (min "
-          f"{min(per_call_ms) * 1e3:.1f}), {achieved:.0f} GB/s algorithmic, wall {wall:.3f} s",
+    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (median {median_us:.1f}, min "
+          f"{min_us:.1f}), {achieved:.0f} GB/s algorithmic, wall {wall:.3f} s",
           file=sys.stderr, flush=True)
 
     if args.copy_calibration:
@@ -341,9 +367,10 @@ def main() -> int:
         times.sort()
         med = times[len(times) // 2]
         cpu = {"value": tokens / med, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "nproc": os.cpu_count(), "cpu_model": cpu_model(),
                "sample": f"the whole {args.workload} batch (B={B} H={H} L={L} N={N}), fp64 "
-                         f"sequential oracle, OpenMP over the {B * H} sequences, median of "
-                         f"{len(times)} runs ({med:.3f} s each)"}
+                         f"sequential oracle, OpenMP over the {B * H} sequences on every core "
+                         f"the process may use, median of {len(times)} runs ({med:.3f} s each)"}
         best = med
         print(f"[bench] cpu oracle: {best:.2f} s on {threads} threads", file=sys.stderr, flush=True)
 
@@ -364,6 +391,10 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "us_per_call_median": median_us,
+        "us_per_call_min": min_us,
+        "settle_s": args.settle_seconds,
+        "settle_calls": settle_calls,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -164,10 +164,14 @@ int pdssm_scan_fwd_save(const void *sel_or_logits, const int32_t *dict_idx, cons
  * Arithmetic fp32 (complex fp32), any summation order: the adjoint carried
  * between chunks of 16 steps is composed in an order that depends on timing,
  * so repeated calls may differ in the last bits (and a bf16 output by one
- * rounding step).  Workspace sized by pdssm_scan_bwd_workspace_bytes; as for
- * pdssm_scan_fwd it may hold anything on entry, and two calls in flight at
- * once need two workspaces.  Errors and empty shapes as pdssm_scan_fwd; with
- * L = 0, gx0 = gx_final (zero without it) is written when gx0 is given.
+ * rounding step).  The adjoint carried between tiles is waited for without
+ * a time bound, as the forward's carry is: a workgroup takes its tile ticket
+ * when it starts and only waits for tiles of earlier tickets, so the call
+ * always completes and never uses a partial carry.  Workspace sized by
+ * pdssm_scan_bwd_workspace_bytes; as for pdssm_scan_fwd it may hold anything
+ * on entry, and two calls in flight at once need two workspaces.  Errors and
+ * empty shapes as pdssm_scan_fwd; with L = 0, gx0 = gx_final (zero without
+ * it) is written when gx0 is given.
  */
 int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
                    const void *b, const void *c, const void *x_chunks, const void *gy,

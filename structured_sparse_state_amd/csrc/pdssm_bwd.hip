@@ -379,12 +379,6 @@ struct BwdRec {
     static constexpr int AW = 1 + 2 * NC;   // operator words per lane: sig, m.r, v.r (, m.i, v.i)
 };
 
-// Polls of one look-back before a wave gives up (each is a record read and
-// a sleep of 512 clocks, so about a second in all): far beyond any wait of a
-// correct run.  A wave that gives up sets the header's first reserved word
-// and takes a zero carry, so that the kernel always ends.
-constexpr uint32_t kBwdSpinLimit = 1u << 20;
-
 template <int NP, bool CPLX, bool BCBF>
 __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
 {
@@ -580,7 +574,10 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
             }
             GOp acc = {i, {1.f, 0.f}, {0.f, 0.f}};   // the tiles tile-1 .. j+1, composed
             int64_t j = tile - 1;
-            uint32_t spins = 0;
+            // The look-back waits without a bound, as the forward's does: a
+            // workgroup takes its ticket when it starts, so every record it
+            // waits for belongs to a workgroup that has started and will
+            // publish it.
             while (true) {
                 const uint64_t *iw = a.incl + (seq_rec + j) * (NC * 64);
                 const uint64_t *aw = a.agg + (seq_rec + j) * (AW * 64);
@@ -618,11 +615,6 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
                         --j;
                         continue;
                     }
-                }
-                if (++spins > kBwdSpinLimit) {
-                    if (lane == 0)
-                        __hip_atomic_store(&a.hdr->reserved0[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    break;
                 }
                 __builtin_amdgcn_s_sleep(8);
             }

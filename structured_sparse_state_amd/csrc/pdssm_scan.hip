@@ -452,11 +452,13 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         __syncthreads();   // (Q) first table and selections ready
 
         // Store output v of the previous tile, which chunk wave w staged in
-        // s_y (lane = step of the wave's chunks).
+        // s_y (step j * 64 + lane of the wave's chunks: a wave holds G * T
+        // steps, 16 to 128, so up to two per lane).
+        constexpr int YR = (G * T + 63) / 64;
         int64_t py0 = 0, pt0 = 0;   // the previous tile: y index and step of its first output
-        auto store_y = [&](int w, float v) {
-            const int k = chunk_pos(w) * G * T + lane;   // step within the tile
-            if (lane < G * T && pt0 + k < a.L) {
+        auto store_y = [&](int w, int j, float v) {
+            const int k = chunk_pos(w) * G * T + j * 64 + lane;   // step within the tile
+            if (j * 64 + lane < G * T && pt0 + k < a.L) {
                 if (a.y_bf16)
                     reinterpret_cast<uint16_t *>(a.y)[py0 + k] = f32_to_bf16_rne(v);
                 else
@@ -498,10 +500,9 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             if (lane == 0)
                 s_ready = 0;
             const bool more = nxt < total;
-            // The tile's aggregate: the inclusive prefix of its last chunk;
-            // and the previous tile's outputs, final in s_y since the chunk
-            // waves posted.  Both are read before the table copy starts (the
-            // compiler would make LDS reads wait for it).
+            // The tile's aggregate: the inclusive prefix of its last chunk,
+            // read before the table copy starts (the compiler would make LDS
+            // reads wait for it).
             int ppi = lane;
             cf pd = {1.f, 0.f}, pe = {0.f, 0.f};
             if (act) {
@@ -510,10 +511,6 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                 pd = s_d[as];
                 pe = s_e[as];
             }
-            float yv[W];
-#pragma unroll
-            for (int w = 0; w < W; ++w)
-                yv[w] = (lane < G * T) ? s_y[w * G * T + lane] : 0.f;
             // Every chunk wave is past its local pass, the only reader of the
             // entry table: stage the next tile's (a workgroup serving one
             // head keeps its table).
@@ -525,14 +522,17 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                 if (!lb.attempt(a, epoch, lane, scr))
                     __builtin_amdgcn_s_sleep(PDSSM_CARRY_NAP);
             // The next table has landed (it was staged before (B)), then the
-            // state after the tile goes out, then the previous tile's
-            // outputs; the stores need not complete here.
+            // state after the tile goes out, then the previous tile's outputs
+            // (final in s_y since the chunk waves posted; rewritten only after
+            // (D)); the stores need not complete here.
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             publish_incl<NP, CPLX>(a, tile, seq, epoch, lane, ppi, pd, pe, lb.xin, scr);
             if (have_prev)
-#pragma unroll
                 for (int w = 0; w < W; ++w)
-                    store_y(w, yv[w]);
+#pragma unroll
+                    for (int j = 0; j < YR; ++j)
+                        if (j * 64 + lane < G * T)
+                            store_y(w, j, s_y[w * G * T + j * 64 + lane]);
             s_xin[lane] = lb.xin;
             __syncthreads();   // (C) carry ready, next table staged
             __syncthreads();   // (D) chunk waves have read the prefixes and the carry

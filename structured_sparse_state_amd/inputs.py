@@ -318,3 +318,40 @@ def make_grads(inp: ScanInputs, *, seed: int = 0, with_gx_final: bool = True, de
         tail = (inp.N, 2) if inp.complex else (inp.N,)
         gxf = torch.randn((inp.B, inp.H) + tail, generator=g, device=device, dtype=torch.float32)
     return gy, gxf
+
+
+def make_adversarial_scores(B: int, H: int, L: int, K: int, *, bf16: bool, seed: int = 71,
+                            device="cpu") -> torch.Tensor:
+    """Router scores [B, H, L, K] that exercise every rule of the hard
+    selection, in fp32 or bf16 (every value is exact in both):
+
+    * small integers in [-3, 3], so most rows hold exact ties at their maximum;
+    * rows whose maximum is a -0 / +0 pair (every other score negative);
+    * rows with one NaN, and rows with two or three NaNs;
+    * rows with +inf at one or two places and -inf elsewhere in the row;
+    * rows that are -inf throughout.
+
+    Each step draws its row kind and the positions it uses from the seeded
+    generator; nothing here depends on how the selection is computed."""
+    g = _gen(device, seed)
+    v = torch.randint(-3, 4, (B, H, L, K), generator=g, device=device).to(torch.float32)
+    kind = torch.randint(0, 10, (B, H, L, 1), generator=g, device=device)
+    pos = torch.randint(0, K, (B, H, L, 3), generator=g, device=device)
+    cols = torch.arange(K, device=device).view(1, 1, 1, K)
+    at = [cols == pos[..., i:i + 1] for i in range(3)]
+    nan, inf = float("nan"), float("inf")
+    # kind 3: all negative except a -0 (first drawn place) and a +0 (second)
+    neg = -(v.abs() + 1.0)
+    zero_row = torch.where(at[1], torch.zeros_like(v), neg)
+    zero_row = torch.where(at[0], torch.full_like(v, -0.0), zero_row)
+    v = torch.where(kind == 3, zero_row, v)
+    # kind 4: one NaN; kind 5: up to three NaNs
+    v = torch.where((kind == 4) & at[0], torch.full_like(v, nan), v)
+    several = (kind == 5) & (at[0] | at[1] | at[2])
+    v = torch.where(several, torch.full_like(v, nan), v)
+    # kind 6: +inf at up to two places, -inf at a third (unless it is one of them)
+    v = torch.where((kind == 6) & at[2], torch.full_like(v, -inf), v)
+    v = torch.where((kind == 6) & (at[0] | at[1]), torch.full_like(v, inf), v)
+    # kind 7: -inf throughout
+    v = torch.where(kind == 7, torch.full_like(v, -inf), v)
+    return v.to(torch.bfloat16) if bf16 else v

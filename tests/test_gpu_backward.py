@@ -124,6 +124,11 @@ BWD_SHAPES = [
     (5, 33, 7, gen.SEL_I16, True, True, False),
     (8, 129, 4, gen.LOGITS_F32, False, False, False),
     (16, 513, 16, gen.SEL_I32, True, False, False),
+    # N in 17..32: two chunks per wave; L not a multiple of 16 leaves a
+    # partial last chunk, and waves with one idle and one active lane group.
+    (20, 129, 12, gen.LOGITS_BF16, True, True, True),
+    (32, 149, 9, gen.SEL_I32, False, False, False),
+    (24, 405, 40, gen.LOGITS_F32, True, False, False),
     (33, 129, 12, gen.LOGITS_BF16, True, True, True),
     (47, 2000, 33, gen.SEL_I32, True, False, False),
     (64, 17, 64, gen.LOGITS_BF16, True, True, True),

@@ -132,6 +132,16 @@ def test_shapes(orc, N, L, K, mode, cplx, bcbf, ybf):
         run_and_compare(orc, inp, f"shape N={N} L={L} K={K} x0={with_x0}")
 
 
+@pytest.mark.parametrize("N,mode", [(5, gen.LOGITS_F32), (8, gen.SEL_I32), (16, gen.LOGITS_BF16)])
+def test_many_tiles_per_workgroup(orc, N, mode):
+    """Several times more tiles than resident workgroups, so every workgroup
+    runs many tiles in turn and hands each tile's outputs to its carry wave
+    (at N <= 8 a wave holds 128 steps, two per lane)."""
+    inp = gen.make_inputs("tiny", B=16, H=16, L=8000, N=N, K=8, sel_mode=mode, dmin=0.8, dmax=1.0,
+                          with_x0=True, seed=600 + N)
+    run_and_compare(orc, inp, f"many tiles per workgroup N={N}")
+
+
 def test_more_heads_than_workgroups(orc):
     """More heads than resident workgroups: one ticket stream for all
     sequences even though each head's table fits in LDS."""

@@ -80,3 +80,25 @@ def test_upstream_gradients():
     gy2, _ = gen.make_grads(inp, seed=2)
     assert torch.equal(gy, gy2)
     assert gen.make_grads(inp, seed=2, with_gx_final=False)[1] is None
+
+
+def test_adversarial_scores_cover_every_rule():
+    """The adversarial router scores hold ties, -0/+0 maxima, NaNs, +inf and
+    all -inf rows, and every value is exact in bf16."""
+    v = gen.make_adversarial_scores(2, 2, 500, 16, bf16=False, seed=3)
+    assert v.shape == (2, 2, 500, 16) and v.dtype == torch.float32
+    a = v.numpy()
+    assert np.isnan(a).any(-1).sum() > 20
+    assert (np.isnan(a).sum(-1) >= 2).sum() > 5          # several NaNs in one row
+    assert np.isposinf(a).any(-1).sum() > 20
+    assert np.isneginf(a).all(-1).sum() > 20             # whole rows of -inf
+    negzero = (a == 0) & np.signbit(a)
+    assert negzero.any(-1).sum() > 20
+    finite = np.where(np.isfinite(a), a, 0)
+    assert np.array_equal(finite, np.round(finite))      # small integers: exact ties
+    vb = gen.make_adversarial_scores(2, 2, 500, 16, bf16=True, seed=3)
+    assert vb.dtype == torch.bfloat16
+    back = vb.float().numpy()
+    same = (back == a) | (np.isnan(back) & np.isnan(a))
+    num = ~np.isnan(a)
+    assert same.all() and np.array_equal(np.signbit(back[num]), np.signbit(a[num]))
