@@ -97,6 +97,7 @@ extern "C" {
 #define PDSSM_ERR_ALIGN -4     /* a pointer is not 16-byte aligned */
 #define PDSSM_ERR_WORKSPACE -5 /* workspace smaller than the size function returns */
 #define PDSSM_ERR_HIP -6       /* a HIP launch failed; pdssm_strerror gives the HIP text */
+#define PDSSM_ERR_SCRATCH -7   /* pdssm_scan_fwd_noalloc: the sizes need more than its scratch holds */
 
 /*
  * The forward scan (all five steps of the path: selection, per-step P D
@@ -118,6 +119,25 @@ int pdssm_scan_fwd(const void *sel_or_logits, const int32_t *dict_idx, const voi
  * flags; 0 when the arguments are invalid. */
 size_t pdssm_scan_workspace_bytes(int64_t B, int64_t H, int64_t L, int32_t N, int32_t K,
                                   uint32_t flags);
+
+/*
+ * pdssm_scan_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same operation, arguments and errors, without the workspace.  Its
+ * workspace is a 64 MiB array of device memory held by the library on every
+ * GPU it runs on until the process ends (enough for B*H*L*N up to about
+ * 10^8 complex steps at N = 64; pdssm_scan_workspace_bytes gives the need).
+ * Sizes whose workspace would not fit return PDSSM_ERR_SCRATCH before any HIP
+ * call.  The call allocates nothing (no hipMalloc or allocating library
+ * routine); it finds the array's device address once per device.  Every
+ * call on one GPU shares that GPU's array: calls that overlap in time on the
+ * same GPU (on different streams, or from different host threads) race and
+ * give undefined results; calls in sequence on one stream are safe.
+ */
+int pdssm_scan_fwd_noalloc(const void *sel_or_logits, const int32_t *dict_idx, const void *diag,
+                           const void *b, const void *c, void *y, void *x_final, int64_t B,
+                           int64_t H, int64_t L, int32_t N, int32_t K, uint32_t flags,
+                           const void *x0, hipStream_t stream);
 
 /*
  * pdssm_scan_fwd that also keeps what pdssm_scan_bwd needs: the state just

@@ -44,6 +44,7 @@ PDSSM_ERR_FLAGS = -3
 PDSSM_ERR_ALIGN = -4
 PDSSM_ERR_WORKSPACE = -5
 PDSSM_ERR_HIP = -6
+PDSSM_ERR_SCRATCH = -7
 
 SEL_FLAG = {"sel_i32": PDSSM_SEL_I32, "sel_i16": PDSSM_SEL_I16,
             "logits_f32": PDSSM_LOGITS_F32, "logits_bf16": PDSSM_LOGITS_BF16}
@@ -69,6 +70,8 @@ def library() -> ctypes.CDLL:
                                 ctypes.c_size_t)
         lib.pdssm_scan_fwd.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, U32, P, P, SZ, P]
         lib.pdssm_scan_fwd.restype = ctypes.c_int
+        lib.pdssm_scan_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, U32, P, P]
+        lib.pdssm_scan_fwd_noalloc.restype = ctypes.c_int
         lib.pdssm_scan_workspace_bytes.argtypes = [I64, I64, I64, I32, I32, U32]
         lib.pdssm_scan_workspace_bytes.restype = SZ
         lib.pdssm_select.argtypes = [P, P, I64, I64, I64, I32, U32, P]
@@ -128,6 +131,13 @@ def pdssm_scan_fwd(sel_or_logits, dict_idx, diag, b, c, y, x_final, B, H, L, N, 
     return library().pdssm_scan_fwd(_ptr(sel_or_logits), _ptr(dict_idx), _ptr(diag), _ptr(b),
                                     _ptr(c), _ptr(y), _ptr(x_final), B, H, L, N, K, flags,
                                     _ptr(x0), _ptr(workspace), workspace_bytes, _stream(stream))
+
+
+def pdssm_scan_fwd_noalloc(sel_or_logits, dict_idx, diag, b, c, y, x_final, B, H, L, N, K, flags,
+                           x0, stream=None) -> int:
+    return library().pdssm_scan_fwd_noalloc(_ptr(sel_or_logits), _ptr(dict_idx), _ptr(diag), _ptr(b),
+                                            _ptr(c), _ptr(y), _ptr(x_final), B, H, L, N, K, flags,
+                                            _ptr(x0), _stream(stream))
 
 
 def pdssm_scan_workspace_bytes(B, H, L, N, K, flags) -> int:
@@ -233,6 +243,23 @@ def scan(inp, *, workspace: Optional[torch.Tensor] = None, want_x_final: bool = 
                          x_final if want_x_final else None, inp.B, inp.H, inp.L, inp.N, inp.K,
                          flags_of(inp), x0t, workspace, workspace.numel(), stream))
     return y, (x_final if want_x_final else None)
+
+
+def scan_noalloc(inp, *, y: Optional[torch.Tensor] = None, x_final: Optional[torch.Tensor] = None,
+                 stream=None):
+    """pdssm_scan_fwd_noalloc on a batch (the library's own device scratch in
+    place of a workspace); returns (y, x_final).  Output tensors passed in are
+    written in place, so the call itself allocates nothing."""
+    dev = inp.diag.device
+    if y is None:
+        y = torch.empty((inp.B, inp.H, inp.L), device=dev,
+                        dtype=torch.bfloat16 if inp.y_bf16 else torch.float32)
+    if x_final is None:
+        shape = (inp.B, inp.H, inp.N, 2) if inp.complex else (inp.B, inp.H, inp.N)
+        x_final = torch.empty(shape, device=dev, dtype=torch.float32)
+    check(pdssm_scan_fwd_noalloc(inp.sel_or_logits, inp.dict_idx, inp.diag, inp.b, inp.c, y, x_final,
+                                 inp.B, inp.H, inp.L, inp.N, inp.K, flags_of(inp), inp.x0, stream))
+    return y, x_final
 
 
 CARRY_STRIDE = 16   # steps per saved chunk carry (include/pdssm.h)

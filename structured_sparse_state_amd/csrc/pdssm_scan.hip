@@ -26,6 +26,7 @@
 
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <type_traits>
 
@@ -1346,6 +1347,45 @@ static void dispatch_compose(const ComposeArgs &a, bool cplx, hipStream_t st)
     }
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free forward scan: one file-scope device array
+// that every GPU the library runs on holds (its own copy) until the process
+// ends.  Host code uses the array's device address, found once per device
+// with hipGetSymbolAddress: the array's name on the host is only a stand-in.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch[kMaxDevices];
+
+static int scratch_address(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices) {
+        g_err = "device index beyond the allocation-free scratch table";
+        return PDSSM_ERR_HIP;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return hip_status(e);
+        if (!p) {
+            g_err = "hipGetSymbolAddress gave no address for the scratch array";
+            return PDSSM_ERR_HIP;
+        }
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return PDSSM_OK;
+}
+
 }  // namespace pdssm
 
 using namespace pdssm;
@@ -1454,6 +1494,29 @@ extern "C" int pdssm_scan_fwd(const void *sel_or_logits, const int32_t *dict_idx
                     workspace, workspace_bytes, false, nullptr, nullptr, stream);
 }
 
+extern "C" int pdssm_scan_fwd_noalloc(const void *sel_or_logits, const int32_t *dict_idx,
+                                      const void *diag, const void *b, const void *c, void *y,
+                                      void *x_final, int64_t B, int64_t H, int64_t L, int32_t N,
+                                      int32_t K, uint32_t flags, const void *x0, hipStream_t stream)
+{
+    int rc = check_dims(B, H, L, N, K);
+    if (rc != PDSSM_OK)
+        return rc;
+    if (flags & ~PDSSM_FLAGS_ALL)
+        return PDSSM_ERR_FLAGS;
+    if (B == 0 || H == 0 || L == 0)   // touches no workspace
+        return scan_fwd(sel_or_logits, dict_idx, diag, b, c, y, x_final, B, H, L, N, K, flags, x0,
+                        nullptr, 0, false, nullptr, nullptr, stream);
+    if ((size_t)layout_of(B, H, L, N, K, flags).total > kScratchBytes)
+        return PDSSM_ERR_SCRATCH;
+    void *ws = nullptr;
+    rc = scratch_address(&ws);
+    if (rc != PDSSM_OK)
+        return rc;
+    return scan_fwd(sel_or_logits, dict_idx, diag, b, c, y, x_final, B, H, L, N, K, flags, x0, ws,
+                    kScratchBytes, false, nullptr, nullptr, stream);
+}
+
 extern "C" int pdssm_scan_fwd_save(const void *sel_or_logits, const int32_t *dict_idx,
                                    const void *diag, const void *b, const void *c, void *y,
                                    void *x_final, void *x_chunks, int16_t *sel_out, int64_t B,
@@ -1557,6 +1620,8 @@ extern "C" const char *pdssm_strerror(int status)
     case PDSSM_ERR_FLAGS: return "invalid flags";
     case PDSSM_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case PDSSM_ERR_WORKSPACE: return "workspace too small";
+    case PDSSM_ERR_SCRATCH:
+        return "the sizes need more workspace than the allocation-free entry point's 64 MiB scratch";
     case PDSSM_ERR_HIP: return g_err.empty() ? "HIP error" : g_err.c_str();
     default: return "unknown status";
     }

@@ -19,7 +19,7 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"pdssm_scan_fwd", "pdssm_scan_workspace_bytes", "pdssm_select",
                           "pdssm_compose", "pdssm_strerror", "pdssm_scan_fwd_save",
                           "pdssm_scan_bwd", "pdssm_scan_bwd_workspace_bytes", "pdssm_dict_hardmax",
-                          "pdssm_decode_step", "pdssm_router_select"}
+                          "pdssm_decode_step", "pdssm_router_select", "pdssm_scan_fwd_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -216,3 +216,16 @@ def test_router_argument_errors(lib):
     assert r(FAKE, FAKE, FAKE, 2, 100, 3, 64, 256, 1, 0) == pk.PDSSM_ERR_FLAGS
     assert r(FAKE + 2, FAKE, FAKE, 2, 100, 3, 64, 256, 0, 0) == pk.PDSSM_ERR_ALIGN
     assert r(FAKE, FAKE, FAKE + 2, 2, 100, 3, 64, 256, 0, 0) == pk.PDSSM_ERR_ALIGN
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """The allocation-free forward checks its fixed scratch on the host, before
+    any HIP call: the very-long workload needs more than it holds."""
+    flags = pk.PDSSM_LOGITS_BF16 | pk.PDSSM_COMPLEX | pk.PDSSM_BC_BF16 | pk.PDSSM_Y_BF16
+    need = pk.pdssm_scan_workspace_bytes(2, 64, 131072, 64, 128, flags)
+    assert need > 64 << 20
+    rc = pk.pdssm_scan_fwd_noalloc(16, 16, 16, 16, 16, 16, 16, 2, 64, 131072, 64, 128, flags, None, 0)
+    assert rc == pk.PDSSM_ERR_SCRATCH
+    assert "scratch" in pk.pdssm_strerror(rc)
+    assert pk.pdssm_scan_fwd_noalloc(16, 16, 16, 16, 16, 16, 16, 1, 1, 8, 65, 4, 0, None, 0) == pk.PDSSM_ERR_DIM
+    assert pk.pdssm_scan_fwd_noalloc(16, 16, 16, 16, 16, 16, 16, 1, 1, 8, 8, 4, 0x100, None, 0) == pk.PDSSM_ERR_FLAGS
