@@ -95,6 +95,8 @@ def measure_backward(pk, gen, inp, ws, stream, args):
 
     t_bwd = timed(lambda: pk.scan_bwd(inp, xch, gy, gxf, workspace=bws, stream=stream, out=out,
                                       sel=sel))
+    t_bwd_det = timed(lambda: pk.scan_bwd(inp, xch, gy, gxf, workspace=bws, stream=stream, out=out,
+                                          sel=sel, deterministic=True))
     t_save = timed(lambda: pk.scan_save(inp, workspace=ws, stream=stream, want_sel=True))
     ins = (sel, inp.dict_idx, inp.diag, inp.b, inp.c, inp.x0, xch, gy, gxf)
     alg = sum(t.numel() * t.element_size() for t in ins + tuple(out) if t is not None)
@@ -105,6 +107,7 @@ def measure_backward(pk, gen, inp, ws, stream, args):
             "algorithmic_bytes_per_call": alg, "achieved_GBps": alg / t_bwd / 1e9,
             "frac": alg / t_bwd / 1e9 / HBM_PEAK_GBS, "steps": steps,
             "fwd_save_us_per_call": t_save * 1e6,
+            "deterministic_us_per_call": t_bwd_det * 1e6,
             "note": "pdssm_scan_bwd: gradients of b, c, diag, x0 from dy and dx_final, fed "
                     "with the forward's saved chunk carries and int16 selections; algorithmic "
                     "bytes = every input read once and every gradient written once"}
@@ -345,7 +348,28 @@ def main() -> int:
         print(f"[bench] copy calibration: 3 x {src.numel()} bytes copied", file=sys.stderr, flush=True)
         del src, dst
 
+    # PDSSM_DETERMINISTIC: the same calls, timed the same way, with and
+    # without the flag.
+    def det_step(det):
+        def f():
+            pk.scan(sets[calls[0] % nrot], workspace=ws, y=y, x_final=xf, stream=stream,
+                    deterministic=det)
+            calls[0] += 1
+        return f
+
+    det_steps = max(20, args.steps // 2)
+    t_def = _event_time(det_step(False), det_steps, 10, stream)
+    t_det = _event_time(det_step(True), det_steps, 10, stream)
+    det = {"fwd_us_per_call": t_def * 1e6, "fwd_deterministic_us_per_call": t_det * 1e6,
+           "fwd_cost": t_det / t_def - 1.0, "steps": det_steps}
+    print(f"[bench] deterministic forward: {t_det * 1e6:.1f} us vs {t_def * 1e6:.1f} us "
+          f"({100 * (t_det / t_def - 1):+.1f}%)", file=sys.stderr, flush=True)
+
     bwd = None if args.no_backward else measure_backward(pk, gen, inp, ws, stream, args)
+    if bwd:
+        det["bwd_us_per_call"] = bwd["us_per_call"]
+        det["bwd_deterministic_us_per_call"] = bwd["deterministic_us_per_call"]
+        det["bwd_cost"] = bwd["deterministic_us_per_call"] / bwd["us_per_call"] - 1.0
     aux = None if args.no_backward else measure_aux(pk, gen, inp, stream)
     hbm = None if args.no_backward else measure_hbm_practical(alg_bytes, stream)
     if hbm:
@@ -409,6 +433,7 @@ def main() -> int:
                      "algorithmic_bytes_per_call": alg_bytes},
         "cpu_baseline": cpu,
         "backward": bwd,
+        "deterministic": det,
         "next_rows": aux,
         "hbm_practical": hbm,
     }

@@ -87,7 +87,14 @@ extern "C" {
 #define PDSSM_COMPLEX 0x4u /* diag, b, c, x0, x_final complex (re,im pairs) */
 #define PDSSM_BC_BF16 0x8u /* b and c stored as bf16 (else fp32) */
 #define PDSSM_Y_BF16 0x10u /* y stored as bf16 (else fp32) */
-#define PDSSM_FLAGS_ALL 0x1Fu
+/* Bitwise reproducible results (pdssm_scan_fwd and its variants, and
+ * pdssm_scan_bwd): the carry into every tile of steps is taken from the
+ * tile just before it, once that tile's own carry is known, so the same
+ * operations run in the same order on every call.  Without it a tile may
+ * compose the carry from the records of several earlier tiles, whichever are
+ * ready first, which changes the fp32 rounding order from call to call. */
+#define PDSSM_DETERMINISTIC 0x20u
+#define PDSSM_FLAGS_ALL 0x3Fu
 
 /* status codes */
 #define PDSSM_OK 0

@@ -15,6 +15,7 @@ recurrent step), ``select`` and ``compose`` (test exports).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import re
@@ -35,7 +36,8 @@ PDSSM_SEL_MASK = 0x3
 PDSSM_COMPLEX = 0x4
 PDSSM_BC_BF16 = 0x8
 PDSSM_Y_BF16 = 0x10
-PDSSM_FLAGS_ALL = 0x1F
+PDSSM_DETERMINISTIC = 0x20
+PDSSM_FLAGS_ALL = 0x3F
 
 PDSSM_OK = 0
 PDSSM_ERR_NULL = -1
@@ -58,44 +60,66 @@ class PdssmError(RuntimeError):
         self.status = status
 
 
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950); there is no fallback path")
+    lib = ctypes.CDLL(path)
+    P, I64, I32, U32, SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32,
+                            ctypes.c_size_t)
+    lib.pdssm_scan_fwd.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, U32, P, P, SZ, P]
+    lib.pdssm_scan_fwd.restype = ctypes.c_int
+    lib.pdssm_scan_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, U32, P, P]
+    lib.pdssm_scan_fwd_noalloc.restype = ctypes.c_int
+    lib.pdssm_scan_workspace_bytes.argtypes = [I64, I64, I64, I32, I32, U32]
+    lib.pdssm_scan_workspace_bytes.restype = SZ
+    lib.pdssm_select.argtypes = [P, P, I64, I64, I64, I32, U32, P]
+    lib.pdssm_select.restype = ctypes.c_int
+    lib.pdssm_compose.argtypes = [P, P, P, P, P, I64, I64, I64, I32, I32, U32, P, SZ, P]
+    lib.pdssm_compose.restype = ctypes.c_int
+    lib.pdssm_scan_fwd_save.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I32, I32, U32, P,
+                                        P, SZ, P]
+    lib.pdssm_scan_fwd_save.restype = ctypes.c_int
+    lib.pdssm_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I32, I32, U32,
+                                   P, SZ, P]
+    lib.pdssm_scan_bwd.restype = ctypes.c_int
+    lib.pdssm_scan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I32, I32, U32]
+    lib.pdssm_scan_bwd_workspace_bytes.restype = SZ
+    lib.pdssm_strerror.argtypes = [ctypes.c_int]
+    lib.pdssm_strerror.restype = ctypes.c_char_p
+    lib.pdssm_dict_hardmax.argtypes = [P, P, I64, I32, I32, U32, P]
+    lib.pdssm_dict_hardmax.restype = ctypes.c_int
+    lib.pdssm_decode_step.argtypes = [P, P, P, P, P, P, P, I64, I64, I32, I32, U32, P]
+    lib.pdssm_decode_step.restype = ctypes.c_int
+    lib.pdssm_router_select.argtypes = [P, P, P, I64, I64, I64, I32, I32, U32, P]
+    lib.pdssm_router_select.restype = ctypes.c_int
+    return lib
+
+
 def library() -> ctypes.CDLL:
     """The loaded HIP library (raises if it has not been built)."""
     global _LIB
     if _LIB is None:
-        if not os.path.exists(LIBRARY):
-            raise RuntimeError(f"{LIBRARY} is missing: build it with __graft_entry__.build() "
-                               "(hipcc --offload-arch=gfx950); there is no fallback path")
-        lib = ctypes.CDLL(LIBRARY)
-        P, I64, I32, U32, SZ = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32,
-                                ctypes.c_size_t)
-        lib.pdssm_scan_fwd.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, U32, P, P, SZ, P]
-        lib.pdssm_scan_fwd.restype = ctypes.c_int
-        lib.pdssm_scan_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, I64, I64, I64, I32, I32, U32, P, P]
-        lib.pdssm_scan_fwd_noalloc.restype = ctypes.c_int
-        lib.pdssm_scan_workspace_bytes.argtypes = [I64, I64, I64, I32, I32, U32]
-        lib.pdssm_scan_workspace_bytes.restype = SZ
-        lib.pdssm_select.argtypes = [P, P, I64, I64, I64, I32, U32, P]
-        lib.pdssm_select.restype = ctypes.c_int
-        lib.pdssm_compose.argtypes = [P, P, P, P, P, I64, I64, I64, I32, I32, U32, P, SZ, P]
-        lib.pdssm_compose.restype = ctypes.c_int
-        lib.pdssm_scan_fwd_save.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, I32, I32, U32, P,
-                                            P, SZ, P]
-        lib.pdssm_scan_fwd_save.restype = ctypes.c_int
-        lib.pdssm_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, I64, I64, I64, I32, I32, U32,
-                                       P, SZ, P]
-        lib.pdssm_scan_bwd.restype = ctypes.c_int
-        lib.pdssm_scan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I32, I32, U32]
-        lib.pdssm_scan_bwd_workspace_bytes.restype = SZ
-        lib.pdssm_strerror.argtypes = [ctypes.c_int]
-        lib.pdssm_strerror.restype = ctypes.c_char_p
-        lib.pdssm_dict_hardmax.argtypes = [P, P, I64, I32, I32, U32, P]
-        lib.pdssm_dict_hardmax.restype = ctypes.c_int
-        lib.pdssm_decode_step.argtypes = [P, P, P, P, P, P, P, I64, I64, I32, I32, U32, P]
-        lib.pdssm_decode_step.restype = ctypes.c_int
-        lib.pdssm_router_select.argtypes = [P, P, P, I64, I64, I64, I32, I32, U32, P]
-        lib.pdssm_router_select.restype = ctypes.c_int
-        _LIB = lib
+        _LIB = _load(LIBRARY)
     return _LIB
+
+
+_VARIANTS = {}
+
+
+@contextlib.contextmanager
+def variant(name: str):
+    """Route every call in the block through the test build ``name`` of the
+    library (``libpdssm_<name>.so``, see build_lib.VARIANTS)."""
+    global _LIB
+    if name not in _VARIANTS:
+        _VARIANTS[name] = _load(os.path.join(HERE, f"libpdssm_{name}.so"))
+    saved = library()
+    _LIB = _VARIANTS[name]
+    try:
+        yield _LIB
+    finally:
+        _LIB = saved
 
 
 def header_functions() -> list:
@@ -207,8 +231,10 @@ def check(status: int) -> None:
 # L, N, K), all tensors on the GPU.
 # ---------------------------------------------------------------------------
 
-def flags_of(inp) -> int:
+def flags_of(inp, deterministic: bool = False) -> int:
     f = SEL_FLAG[inp.sel_mode]
+    if deterministic:
+        f |= PDSSM_DETERMINISTIC
     if inp.complex:
         f |= PDSSM_COMPLEX
     if inp.bc_bf16:
@@ -227,8 +253,9 @@ def workspace_for(inp, device=None) -> torch.Tensor:
 
 def scan(inp, *, workspace: Optional[torch.Tensor] = None, want_x_final: bool = True,
          y: Optional[torch.Tensor] = None, x_final: Optional[torch.Tensor] = None, stream=None,
-         x0="from_inputs"):
-    """Run pdssm_scan_fwd on a batch; returns (y, x_final or None)."""
+         x0="from_inputs", deterministic: bool = False):
+    """Run pdssm_scan_fwd on a batch; returns (y, x_final or None).
+    ``deterministic`` sets PDSSM_DETERMINISTIC (bitwise reproducible)."""
     dev = inp.diag.device
     if y is None:
         y = torch.empty((inp.B, inp.H, inp.L), device=dev,
@@ -241,12 +268,12 @@ def scan(inp, *, workspace: Optional[torch.Tensor] = None, want_x_final: bool = 
     x0t = inp.x0 if isinstance(x0, str) else x0
     check(pdssm_scan_fwd(inp.sel_or_logits, inp.dict_idx, inp.diag, inp.b, inp.c, y,
                          x_final if want_x_final else None, inp.B, inp.H, inp.L, inp.N, inp.K,
-                         flags_of(inp), x0t, workspace, workspace.numel(), stream))
+                         flags_of(inp, deterministic), x0t, workspace, workspace.numel(), stream))
     return y, (x_final if want_x_final else None)
 
 
 def scan_noalloc(inp, *, y: Optional[torch.Tensor] = None, x_final: Optional[torch.Tensor] = None,
-                 stream=None):
+                 stream=None, deterministic: bool = False):
     """pdssm_scan_fwd_noalloc on a batch (the library's own device scratch in
     place of a workspace); returns (y, x_final).  Output tensors passed in are
     written in place, so the call itself allocates nothing."""
@@ -258,14 +285,16 @@ def scan_noalloc(inp, *, y: Optional[torch.Tensor] = None, x_final: Optional[tor
         shape = (inp.B, inp.H, inp.N, 2) if inp.complex else (inp.B, inp.H, inp.N)
         x_final = torch.empty(shape, device=dev, dtype=torch.float32)
     check(pdssm_scan_fwd_noalloc(inp.sel_or_logits, inp.dict_idx, inp.diag, inp.b, inp.c, y, x_final,
-                                 inp.B, inp.H, inp.L, inp.N, inp.K, flags_of(inp), inp.x0, stream))
+                                 inp.B, inp.H, inp.L, inp.N, inp.K, flags_of(inp, deterministic), inp.x0,
+                                 stream))
     return y, x_final
 
 
 CARRY_STRIDE = 16   # steps per saved chunk carry (include/pdssm.h)
 
 
-def scan_save(inp, *, workspace: Optional[torch.Tensor] = None, stream=None, want_sel: bool = False):
+def scan_save(inp, *, workspace: Optional[torch.Tensor] = None, stream=None, want_sel: bool = False,
+              deterministic: bool = False):
     """pdssm_scan_fwd_save on a batch: (y, x_final, x_chunks), plus the int16
     selections [B,H,L] when want_sel."""
     dev = inp.diag.device
@@ -279,7 +308,8 @@ def scan_save(inp, *, workspace: Optional[torch.Tensor] = None, stream=None, wan
         workspace = workspace_for(inp)
     sel = torch.empty((inp.B, inp.H, inp.L), device=dev, dtype=torch.int16) if want_sel else None
     check(pdssm_scan_fwd_save(inp.sel_or_logits, inp.dict_idx, inp.diag, inp.b, inp.c, y, x_final,
-                              x_chunks, sel, inp.B, inp.H, inp.L, inp.N, inp.K, flags_of(inp), inp.x0,
+                              x_chunks, sel, inp.B, inp.H, inp.L, inp.N, inp.K,
+                              flags_of(inp, deterministic), inp.x0,
                               workspace, workspace.numel(), stream))
     if want_sel:
         return y, x_final, x_chunks, sel
@@ -294,7 +324,8 @@ def bwd_workspace_for(inp, device=None) -> torch.Tensor:
 
 
 def scan_bwd(inp, x_chunks, gy, gx_final=None, *, want_gx0: bool = True,
-             workspace: Optional[torch.Tensor] = None, stream=None, out=None, sel=None):
+             workspace: Optional[torch.Tensor] = None, stream=None, out=None, sel=None,
+             deterministic: bool = False):
     """pdssm_scan_bwd on a batch: (gb, gc, gd, gx0 or None), in the storage
     of b, c, diag and x0.  ``sel``: the forward's saved int16 selections
     (scan_save(want_sel=True)), used in place of the inputs' scores.  ``out``
@@ -311,7 +342,7 @@ def scan_bwd(inp, x_chunks, gy, gx_final=None, *, want_gx0: bool = True,
         gx0 = torch.empty((inp.B, inp.H) + tail, device=dev, dtype=torch.float32) if want_gx0 else None
     if workspace is None:
         workspace = bwd_workspace_for(inp)
-    flags = flags_of(inp)
+    flags = flags_of(inp, deterministic)
     if sel is not None:
         flags = (flags & ~PDSSM_SEL_MASK) | PDSSM_SEL_I16
     check(pdssm_scan_bwd(inp.sel_or_logits if sel is None else sel, inp.dict_idx, inp.diag, inp.b,

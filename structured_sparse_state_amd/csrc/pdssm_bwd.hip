@@ -71,6 +71,7 @@ struct BwdArgs {
     int N, K;
     uint32_t sel_mode;
     int y_bf16;
+    int det;            // PDSSM_DETERMINISTIC: the carry only from the tile just after
 };
 
 template <bool CPLX>
@@ -404,7 +405,12 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
     // Ticket u -> (tile from the right, sequence), tile-major over sequences.
     const uint32_t u = __builtin_amdgcn_readfirstlane(s_ticket);
     const uint32_t S32 = (uint32_t)a.S;
+#ifdef PDSSM_TEST_TICKET_REMAP
+    // Test build: the sequences of a tile row are handed out in reverse.
+    const uint32_t tile = u / S32, seq32 = S32 - 1u - (u - tile * S32);
+#else
     const uint32_t tile = u / S32, seq32 = u - tile * S32;
+#endif
     if (u >= a.total)
         return;
     // The tile's chunks from the right: wave w holds the G chunks from
@@ -563,14 +569,18 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
 #pragma unroll
             for (int k = 1; k < TC; ++k)
                 tagg = compose_left<CPLX>(op_of(k), tagg);
-            // words: sig, m.r, v.r (, m.i, v.i)
-            uint64_t *const aw_own = a.agg + trec * (AW * 64);
-            put_word(aw_own + lane, (uint32_t)tagg.sig, epoch);
-            put_word(aw_own + 64 + lane, __float_as_uint(tagg.m.r), epoch);
-            put_word(aw_own + 128 + lane, __float_as_uint(tagg.v.r), epoch);
-            if constexpr (CPLX) {
-                put_word(aw_own + 192 + lane, __float_as_uint(tagg.m.i), epoch);
-                put_word(aw_own + 256 + lane, __float_as_uint(tagg.v.i), epoch);
+            // words: sig, m.r, v.r (, m.i, v.i); with PDSSM_DETERMINISTIC no
+            // tile reads them (each takes only the carry of the tile just
+            // after it), so none are written.
+            if (!a.det) {
+                uint64_t *const aw_own = a.agg + trec * (AW * 64);
+                put_word(aw_own + lane, (uint32_t)tagg.sig, epoch);
+                put_word(aw_own + 64 + lane, __float_as_uint(tagg.m.r), epoch);
+                put_word(aw_own + 128 + lane, __float_as_uint(tagg.v.r), epoch);
+                if constexpr (CPLX) {
+                    put_word(aw_own + 192 + lane, __float_as_uint(tagg.m.i), epoch);
+                    put_word(aw_own + 256 + lane, __float_as_uint(tagg.v.i), epoch);
+                }
             }
             GOp acc = {i, {1.f, 0.f}, {0.f, 0.f}};   // the tiles tile-1 .. j+1, composed
             int64_t j = tile - 1;
@@ -588,7 +598,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
                 bool pr = false;
                 if (lane == 0)
                     pr = get_word(iw, epoch, pw);
-                else if (lane == 1 && j > 0)
+                else if (lane == 1 && j > 0 && !a.det)
                     pr = get_word(aw, epoch, pw);
                 const uint64_t ready = __ballot(pr);
                 if (ready & 1) {
@@ -798,6 +808,7 @@ extern "C" int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx
     a.N = N;
     a.K = K;
     a.sel_mode = flags & PDSSM_SEL_MASK;
+    a.det = (flags & PDSSM_DETERMINISTIC) ? 1 : 0;
     a.y_bf16 = (flags & PDSSM_Y_BF16) ? 1 : 0;
 
     // New epoch and ticket, the entry table; on first use every record is cleared.

@@ -62,6 +62,7 @@ struct ScanArgs {
     int N, K;
     uint32_t sel_mode;
     int y_bf16;
+    int det;        // PDSSM_DETERMINISTIC: the carry only from the tile just before
     int dict_lds;   // the head's entry table fits in LDS
     const uint16_t *tab;   // [H][K][NP]: dict_entry() of every source (see prep_kernel)
 };
@@ -238,7 +239,7 @@ struct LookBack {
         if (done)
             return false;
         const bool act = lane < NP;
-        const bool has_agg = j > 0;   // tile 0 publishes no AGG (it knows its carry)
+        const bool has_agg = j > 0 && !a.det;   // tile 0 publishes no AGG (it knows its carry)
         const int64_t rj = j * a.S + seq;
         const uint64_t *iw = a.incl + rj * IW;
         const uint64_t *aw = a.agg + rj * AW;
@@ -268,6 +269,8 @@ struct LookBack {
         }
         const bool aok = !act || (from(a0, epoch) && from(a1, epoch) && from(a2, epoch) &&
                                   (!CPLX || (from(a3, epoch) && from(a4, epoch))));
+        // With PDSSM_DETERMINISTIC only the INCL of the tile just before is
+        // taken, so the carry is formed the same way on every call.
         if (has_agg && __all(aok)) {
             int p = lane;
             cf d = {1.f, 0.f}, e = {0.f, 0.f};
@@ -398,15 +401,27 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
     const uint32_t S32 = (uint32_t)a.S, H32 = (uint32_t)a.H;
     // Ticket u -> (tile, sequence): tile-major over all sequences, or, with
     // per-head tickets, over the sequences b * H + hp of this workgroup's head.
+    // PDSSM_TEST_TICKET_REMAP (a test build) reverses the order in which
+    // the sequences of a tile row are handed out and the heads workgroups
+    // serve; every tile still follows the tiles before it in its sequence.
     const bool pinned = a.ctr != nullptr;
-    const uint32_t hp = pinned ? (uint32_t)blockIdx.x % H32 : 0u;
     const uint32_t per = pinned ? S32 / H32 : S32;
     const uint32_t total = pinned ? a.total_head : a.total;
+#ifdef PDSSM_TEST_TICKET_REMAP
+    const uint32_t hp = pinned ? H32 - 1u - (uint32_t)blockIdx.x % H32 : 0u;
+    auto decode = [&](uint32_t u, uint32_t &tile, uint32_t &seq) {
+        tile = __builtin_amdgcn_readfirstlane(u / per);
+        const uint32_t r = per - 1u - (u - tile * per);
+        seq = pinned ? r * H32 + hp : r;
+    };
+#else
+    const uint32_t hp = pinned ? (uint32_t)blockIdx.x % H32 : 0u;
     auto decode = [&](uint32_t u, uint32_t &tile, uint32_t &seq) {
         tile = __builtin_amdgcn_readfirstlane(u / per);
         const uint32_t r = u - tile * per;
         seq = pinned ? r * H32 + hp : r;
     };
+#endif
     const int N = a.N, K = a.K;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -896,7 +911,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             // tile's carry is unknown, later tiles may need it: publish the
             // AGG record (its stores complete while this wave has nothing to
             // wait for).
-            if (pos == W - 1 && tile0 > 0 && tile0 + 1 < a.n_tiles) {
+            if (pos == W - 1 && tile0 > 0 && tile0 + 1 < a.n_tiles && !a.det) {
                 const uint32_t known = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile uint32_t *>(&s_known));
                 if (known != iter)
                     publish_agg<NP, CPLX>(a, tile0, seq0, epoch, q.i, q.g == G - 1, api, ad, ae);
@@ -1460,6 +1475,7 @@ static int scan_fwd(const void *sel_or_logits, const int32_t *dict_idx, const vo
     a.K = K;
     a.sel_mode = flags & PDSSM_SEL_MASK;
     a.y_bf16 = (flags & PDSSM_Y_BF16) ? 1 : 0;
+    a.det = (flags & PDSSM_DETERMINISTIC) ? 1 : 0;
     a.dict_lds = ((int64_t)K * lo.NP * 2 <= kDictLdsMax) ? 1 : 0;
 
     const int64_t rec_bytes = lo.agg_bytes + lo.incl_bytes;

@@ -7,6 +7,7 @@ import re
 import pytest
 
 import structured_sparse_state_amd as pk
+from structured_sparse_state_amd import build_lib
 
 
 @pytest.fixture(scope="module")
@@ -22,6 +23,18 @@ def test_exports_every_declared_function(lib):
                           "pdssm_decode_step", "pdssm_router_select", "pdssm_scan_fwd_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("name", sorted(build_lib.VARIANTS))
+def test_test_builds_export_the_same_functions(name):
+    """The test builds (other chunking, reversed ticket order) load through
+    the binding's variant switch and export every declared function."""
+    with pk.variant(name) as v:
+        assert pk.library() is v
+        for n in pk.header_functions():
+            assert hasattr(v, n), n
+        assert pk.pdssm_scan_workspace_bytes(1, 1, 100, 8, 4, 0) > 0
+    assert pk.library() is not v
 
 
 def test_header_constants_match_binding():
@@ -57,7 +70,7 @@ def test_scan_argument_errors(lib):
     for bad in (dict(B=-1), dict(H=-1), dict(L=-1), dict(N=0), dict(N=65), dict(K=0),
                 dict(K=32768), dict(B=1 << 40, H=1 << 20), dict(B=1 << 40, H=1 << 20, L=0)):
         assert _scan(**bad) == pk.PDSSM_ERR_DIM, bad
-    assert _scan(flags=0x20) == pk.PDSSM_ERR_FLAGS
+    assert _scan(flags=0x40) == pk.PDSSM_ERR_FLAGS
     for name in ("sel", "dict_idx", "diag", "b", "c", "y", "ws", "x0", "x_final"):
         assert _scan(**{name: FAKE + 4}) == pk.PDSSM_ERR_ALIGN, name
     need = pk.pdssm_scan_workspace_bytes(2, 3, 100, 16, 8, pk.PDSSM_LOGITS_BF16)
@@ -98,7 +111,7 @@ def test_empty_shapes_need_no_buffers(lib):
         assert pk.pdssm_router_select(None, None, None, B, L, H, 64, 256, 0, 0) == pk.PDSSM_OK
     # the size and flag checks still apply to empty calls
     assert _scan(**none, B=0, N=65) == pk.PDSSM_ERR_DIM
-    assert _scan(**none, B=0, flags=0x20) == pk.PDSSM_ERR_FLAGS
+    assert _scan(**none, B=0, flags=0x40) == pk.PDSSM_ERR_FLAGS
     assert pk.pdssm_router_select(None, None, None, 0, 100, 3, 64, 48, 0, 0) == pk.PDSSM_ERR_DIM
 
 
@@ -149,7 +162,7 @@ def test_bwd_and_save_argument_errors(lib):
         assert _bwd(**{name: None}) == pk.PDSSM_ERR_NULL, name
     for bad in (dict(B=-1), dict(L=-1), dict(N=65), dict(K=0)):
         assert _bwd(**bad) == pk.PDSSM_ERR_DIM, bad
-    assert _bwd(flags=0x20) == pk.PDSSM_ERR_FLAGS
+    assert _bwd(flags=0x40) == pk.PDSSM_ERR_FLAGS
     for name in ("sel", "diag", "xch", "gy", "gxf", "gb", "gd", "gx0", "ws"):
         assert _bwd(**{name: FAKE + 4}) == pk.PDSSM_ERR_ALIGN, name
     need = pk.pdssm_scan_bwd_workspace_bytes(2, 3, 100, 16, 8, pk.PDSSM_LOGITS_BF16)
@@ -200,7 +213,7 @@ def test_decode_argument_errors(lib):
         assert _dec(**{name: None}) == pk.PDSSM_ERR_NULL, name
     for bad in (dict(B=-1), dict(H=-1), dict(N=0), dict(N=65), dict(K=0), dict(K=40000)):
         assert _dec(**bad) == pk.PDSSM_ERR_DIM, bad
-    assert _dec(flags=0x20) == pk.PDSSM_ERR_FLAGS
+    assert _dec(flags=0x40) == pk.PDSSM_ERR_FLAGS
     for name in ("sel", "dict_idx", "diag", "b", "c", "y", "x"):
         assert _dec(**{name: FAKE + 4}) == pk.PDSSM_ERR_ALIGN, name
 
