@@ -89,10 +89,16 @@ extern "C" {
 #define PDSSM_Y_BF16 0x10u /* y stored as bf16 (else fp32) */
 /* Bitwise reproducible results (pdssm_scan_fwd and its variants, and
  * pdssm_scan_bwd): the carry into every tile of steps is taken from the
- * tile just before it, once that tile's own carry is known, so the same
- * operations run in the same order on every call.  Without it a tile may
- * compose the carry from the records of several earlier tiles, whichever are
- * ready first, which changes the fp32 rounding order from call to call. */
+ * tile just before it (just after it, in the backward), once that tile's own
+ * carry is known, so the same operations run in the same order on every
+ * call.  Without the flag the library takes the carry the same way when the
+ * batch holds enough sequences to keep the device busy (at most 12 resident
+ * workgroups per sequence in the forward, 4 in the backward), which is also
+ * the faster way there.  With fewer sequences a tile may compose its carry
+ * from the records of several earlier tiles, whichever are ready first,
+ * which changes the fp32 rounding order from call to call; there the flag
+ * is slower, as the carry advances along a sequence by about one tile per
+ * microsecond. */
 #define PDSSM_DETERMINISTIC 0x20u
 #define PDSSM_FLAGS_ALL 0x3Fu
 

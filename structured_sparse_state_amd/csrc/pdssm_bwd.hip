@@ -71,7 +71,7 @@ struct BwdArgs {
     int N, K;
     uint32_t sel_mode;
     int y_bf16;
-    int det;            // PDSSM_DETERMINISTIC: the carry only from the tile just after
+    int strict;         // the carry only from the tile just after (no aggregate records)
 };
 
 template <bool CPLX>
@@ -572,7 +572,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
             // words: sig, m.r, v.r (, m.i, v.i); with PDSSM_DETERMINISTIC no
             // tile reads them (each takes only the carry of the tile just
             // after it), so none are written.
-            if (!a.det) {
+            if (!a.strict) {
                 uint64_t *const aw_own = a.agg + trec * (AW * 64);
                 put_word(aw_own + lane, (uint32_t)tagg.sig, epoch);
                 put_word(aw_own + 64 + lane, __float_as_uint(tagg.m.r), epoch);
@@ -598,7 +598,7 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
                 bool pr = false;
                 if (lane == 0)
                     pr = get_word(iw, epoch, pw);
-                else if (lane == 1 && j > 0 && !a.det)
+                else if (lane == 1 && j > 0 && !a.strict)
                     pr = get_word(aw, epoch, pw);
                 const uint64_t ready = __ballot(pr);
                 if (ready & 1) {
@@ -719,18 +719,50 @@ static BwdLayout bwd_layout(int64_t B, int64_t H, int64_t L, int32_t N, int32_t 
     return lo;
 }
 
-template <int NP>
-static void launch_fused(const BwdArgs &a, bool cplx, bool bcbf, hipStream_t st)
+// Aggregate records let a tile's carry skip ahead of unfinished tiles, at the
+// cost of writing and polling them.  When the device holds up to this many
+// workgroups per sequence, the plain chain (each tile waits for the tile just
+// after it) keeps up with the tiles being worked on, and is used.  A link of
+// the backward's chain is slower than the forward's (its look-back composes
+// and publishes more words per lane), hence a lower bound than the forward's.
+#ifndef PDSSM_BWD_STRICT_WGS_PER_SEQ
+#define PDSSM_BWD_STRICT_WGS_PER_SEQ 4
+#endif
+constexpr int64_t kStrictWgsPerSeq = PDSSM_BWD_STRICT_WGS_PER_SEQ;
+
+template <int NP, bool CPLX, bool BCBF>
+static hipError_t launch_fused_t(BwdArgs a, hipStream_t st)
 {
-    const dim3 grid(a.total), blk(kBW * 64);
-    if (cplx && bcbf)
-        hipLaunchKernelGGL((bwd_fused_kernel<NP, true, true>), grid, blk, 0, st, a);
-    else if (cplx)
-        hipLaunchKernelGGL((bwd_fused_kernel<NP, true, false>), grid, blk, 0, st, a);
-    else if (bcbf)
-        hipLaunchKernelGGL((bwd_fused_kernel<NP, false, true>), grid, blk, 0, st, a);
-    else
-        hipLaunchKernelGGL((bwd_fused_kernel<NP, false, false>), grid, blk, 0, st, a);
+    // Resident workgroups per device, cached per device.
+    static thread_local int c_dev = -1, c_wgs = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev != c_dev) {
+        int per_cu = 0, cus = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_fused_kernel<NP, CPLX, BCBF>, kBW * 64, 0);
+        if (e != hipSuccess)
+            return e;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess)
+            return e;
+        c_wgs = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+        c_dev = dev;
+    }
+    const int64_t in_flight = (int64_t)a.total < c_wgs ? (int64_t)a.total : c_wgs;
+    if (in_flight <= kStrictWgsPerSeq * a.S)
+        a.strict = 1;
+    hipLaunchKernelGGL((bwd_fused_kernel<NP, CPLX, BCBF>), dim3(a.total), dim3(kBW * 64), 0, st, a);
+    return hipSuccess;
+}
+
+template <int NP>
+static hipError_t launch_fused(const BwdArgs &a, bool cplx, bool bcbf, hipStream_t st)
+{
+    if (cplx)
+        return bcbf ? launch_fused_t<NP, true, true>(a, st) : launch_fused_t<NP, true, false>(a, st);
+    return bcbf ? launch_fused_t<NP, false, true>(a, st) : launch_fused_t<NP, false, false>(a, st);
 }
 
 }  // namespace pdssm
@@ -808,7 +840,7 @@ extern "C" int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx
     a.N = N;
     a.K = K;
     a.sel_mode = flags & PDSSM_SEL_MASK;
-    a.det = (flags & PDSSM_DETERMINISTIC) ? 1 : 0;
+    a.strict = (flags & PDSSM_DETERMINISTIC) ? 1 : 0;   // launch_fused may set it too
     a.y_bf16 = (flags & PDSSM_Y_BF16) ? 1 : 0;
 
     // New epoch and ticket, the entry table; on first use every record is cleared.
@@ -817,10 +849,13 @@ extern "C" int pdssm_scan_bwd(const void *sel_or_logits, const int32_t *dict_idx
     if (rc != PDSSM_OK)
         return rc;
     const bool cplx = flags & PDSSM_COMPLEX, bcbf = flags & PDSSM_BC_BF16;
+    hipError_t e;
     switch (lo.NP) {
-    case 16: launch_fused<16>(a, cplx, bcbf, stream); break;
-    case 32: launch_fused<32>(a, cplx, bcbf, stream); break;
-    default: launch_fused<64>(a, cplx, bcbf, stream); break;
+    case 16: e = launch_fused<16>(a, cplx, bcbf, stream); break;
+    case 32: e = launch_fused<32>(a, cplx, bcbf, stream); break;
+    default: e = launch_fused<64>(a, cplx, bcbf, stream); break;
     }
+    if (e != hipSuccess)
+        return hip_status(e);
     return hip_status(hipGetLastError());
 }

@@ -62,7 +62,7 @@ struct ScanArgs {
     int N, K;
     uint32_t sel_mode;
     int y_bf16;
-    int det;        // PDSSM_DETERMINISTIC: the carry only from the tile just before
+    int strict;     // the carry only from the tile just before (no aggregate records)
     int dict_lds;   // the head's entry table fits in LDS
     const uint16_t *tab;   // [H][K][NP]: dict_entry() of every source (see prep_kernel)
 };
@@ -239,7 +239,7 @@ struct LookBack {
         if (done)
             return false;
         const bool act = lane < NP;
-        const bool has_agg = j > 0 && !a.det;   // tile 0 publishes no AGG (it knows its carry)
+        const bool has_agg = j > 0 && !a.strict;   // tile 0 publishes no AGG (it knows its carry)
         const int64_t rj = j * a.S + seq;
         const uint64_t *iw = a.incl + rj * IW;
         const uint64_t *aw = a.agg + rj * AW;
@@ -911,7 +911,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             // tile's carry is unknown, later tiles may need it: publish the
             // AGG record (its stores complete while this wave has nothing to
             // wait for).
-            if (pos == W - 1 && tile0 > 0 && tile0 + 1 < a.n_tiles && !a.det) {
+            if (pos == W - 1 && tile0 > 0 && tile0 + 1 < a.n_tiles && !a.strict) {
                 const uint32_t known = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile uint32_t *>(&s_known));
                 if (known != iter)
                     publish_agg<NP, CPLX>(a, tile0, seq0, epoch, q.i, q.g == G - 1, api, ad, ae);
@@ -1298,6 +1298,11 @@ int hip_status(hipError_t e)
 
 // Persistent grid: as many workgroups as the device holds at once (they
 // loop over the tiles), never more than there are tiles.
+#ifndef PDSSM_STRICT_WGS_PER_SEQ
+#define PDSSM_STRICT_WGS_PER_SEQ 12
+#endif
+constexpr int64_t kStrictWgsPerSeq = PDSSM_STRICT_WGS_PER_SEQ;
+
 template <int NP, bool CPLX, bool BCBF>
 static hipError_t launch_scan(const ScanArgs &a, hipStream_t st)
 {
@@ -1337,6 +1342,13 @@ static hipError_t launch_scan(const ScanArgs &a, hipStream_t st)
         b.ctr = nullptr;
         grid = (unsigned)((int64_t)a.total < c_wgs ? (int64_t)a.total : c_wgs);
     }
+    // Aggregate records let a tile's carry skip ahead of unfinished tiles;
+    // writing and polling them costs a few per cent of the call.  A tile
+    // whose predecessor has its carry gets its own about 1.1 us later, so
+    // with up to kStrictWgsPerSeq workgroups per sequence the plain chain
+    // keeps up with the tiles being worked on, and is used.
+    if ((int64_t)grid <= kStrictWgsPerSeq * a.S)
+        b.strict = 1;
     hipLaunchKernelGGL((scan_kernel<NP, CPLX, BCBF>), dim3(grid), dim3(block), dyn, st, b);
     return hipSuccess;
 }
@@ -1475,7 +1487,7 @@ static int scan_fwd(const void *sel_or_logits, const int32_t *dict_idx, const vo
     a.K = K;
     a.sel_mode = flags & PDSSM_SEL_MASK;
     a.y_bf16 = (flags & PDSSM_Y_BF16) ? 1 : 0;
-    a.det = (flags & PDSSM_DETERMINISTIC) ? 1 : 0;
+    a.strict = (flags & PDSSM_DETERMINISTIC) ? 1 : 0;   // launch_scan may set it too
     a.dict_lds = ((int64_t)K * lo.NP * 2 <= kDictLdsMax) ? 1 : 0;
 
     const int64_t rec_bytes = lo.agg_bytes + lo.incl_bytes;
