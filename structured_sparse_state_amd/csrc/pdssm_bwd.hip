@@ -514,9 +514,9 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
             const uint32_t slot = entry_slot(ent);
             *static_cast<float2 *>(__builtin_assume_aligned(regp + slot, 8)) = make_float2(vv.r, vv.i);
             lds_order();
-            if (__any(slot >= kSpareOff)) {
-                if (slot >= kSpareOff) {
-                    cf *o = reinterpret_cast<cf *>(regp + (slot - kSpareOff));
+            if (__any(slot_rank_ovf(slot))) {
+                if (slot_rank_ovf(slot)) {
+                    cf *o = reinterpret_cast<cf *>(regp + (slot - kRegionBytes));
                     lds_add(&o->r, vv.r);
                     if constexpr (CPLX)
                         lds_add(&o->i, vv.i);
@@ -530,6 +530,13 @@ __global__ void __launch_bounds__(kBW * 64) bwd_fused_kernel(BwdArgs a)
                 const float2 q = *static_cast<const float2 *>(__builtin_assume_aligned(rowp + r * kRegionBytes, 8));
                 sum.r += q.x;
                 sum.i += q.y;
+            }
+            if (__any(entry_deg_ovf(ent))) {
+                if (entry_deg_ovf(ent)) {
+                    const float2 q = *static_cast<const float2 *>(__builtin_assume_aligned(rowbase + kSpareOff, 8));
+                    sum.r += q.x;
+                    sum.i += q.y;
+                }
             }
             lds_order();
             x = sum;

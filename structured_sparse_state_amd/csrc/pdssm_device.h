@@ -644,12 +644,16 @@ __device__ __forceinline__ cf scatter_add(cf *scr, int lane, int base, int pi, c
 
 // ---------------------------------------------------------------------------
 // The collision-free scatter of one step.  A chunk wave's scatter area has
-// 2R + 1 blocks of 64 complex slots: blocks 0 .. R-1 hold regions R-1 .. 0
-// (region r at block R-1-r), R .. 2R-1 stay zero, 2R is the spare for
-// sources of rank >= R.  Source j stores into row pi(j) of the region of
-// its rank (rank = number of sources j' < j with the same destination), so
-// a region never has two sources on one row; row i reads the R blocks from
-// block R - min(deg(i), R) on: its deg(i) regions, then zero blocks.
+// 2R + 2 blocks of 64 complex slots: blocks 0 .. R-1 hold regions R-1 .. 0
+// (region r at block R-1-r), R .. 2R-1 stay zero, 2R is the spare region and
+// 2R+1 a trash block.  Source j stores into row pi(j) of the region of its
+// rank (rank = number of sources j' < j with the same destination), so a
+// region never has two sources on one row; row i reads the R blocks from
+// block R - min(deg(i), R) on: its deg(i) regions, then zero blocks.  The
+// source of rank R stores into row pi(j) of the spare region, and a row of
+// in-degree above R also reads its spare slot (a read under its own lane
+// mask).  Sources of rank above R (rare: a row with five or more sources)
+// store into the trash block and then add atomically into the spare slot.
 // ---------------------------------------------------------------------------
 // The forward scan can keep the state before every chunk of kCarryStride
 // steps; the backward scan works on chunks of the same length.
@@ -660,10 +664,13 @@ constexpr int kCarryStride = 16;
 #endif
 constexpr int kRegions = PDSSM_SCAN_REGIONS;   // collision-free regions (ranks 0..kRegions-1)
 constexpr int kRegionBytes = 64 * 8;           // one block: 64 complex slots
-constexpr int kBlocks = 2 * kRegions + 1;
-constexpr uint32_t kSpareOff = 2 * kRegions * kRegionBytes;
+constexpr int kBlocks = 2 * kRegions + 2;
+constexpr uint32_t kSpareOff = 2 * kRegions * kRegionBytes;         // the spare region
+constexpr uint32_t kTrashOff = (2 * kRegions + 1) * kRegionBytes;   // stores of sources of rank > R
 constexpr int kBlockBits = kBlocks <= 8 ? 3 : 4;   // bits of the scatter block field
+constexpr int kDegOvfBit = 6 + kBlockBits + 3;     // the row has more than R sources (top bit)
 static_assert(kRegions >= 1 && kRegions <= 4, "the entry's read-block field holds 0..kRegions in 3 bits");
+static_assert(kDegOvfBit < 16, "entries are 16 bits");
 
 // Byte offset of a source's scatter slot (block * 512 + pi * 8) and of the
 // first block its row reads, from its entry.
@@ -672,9 +679,13 @@ __device__ __forceinline__ uint32_t entry_row(uint32_t ent)
 {
     return ((ent >> (6 + kBlockBits)) & 7u) * (uint32_t)kRegionBytes;
 }
+// The row has more than R sources: it also reads its spare slot.
+__device__ __forceinline__ bool entry_deg_ovf(uint32_t ent) { return ent >= (1u << kDegOvfBit); }
+// The source has rank above R: it adds into the spare slot of its row.
+__device__ __forceinline__ bool slot_rank_ovf(uint32_t slot) { return slot >= kTrashOff; }
 
 // The 16-bit entry of source `lane` for the index map row[0..N):
-//   pi | scatter block << 6 | read block << (6 + kBlockBits).
+//   pi | scatter block << 6 | read block << (6 + kBlockBits) | (deg > R) << kDegOvfBit.
 // Called by a whole wave (lanes >= N are padding sources that map to
 // themselves with rank 0 and in-degree 1); entries outside [0,N) clamp.
 __device__ __forceinline__ uint16_t dict_entry(const int32_t *row, int N, int lane)
@@ -688,9 +699,9 @@ __device__ __forceinline__ uint16_t dict_entry(const int32_t *row, int N, int la
     }
     if (lane >= N)
         deg = 1;   // padding rows hold their own (zero) state
-    const int block = rank < kRegions ? kRegions - 1 - rank : 2 * kRegions;
+    const int block = rank < kRegions ? kRegions - 1 - rank : rank == kRegions ? 2 * kRegions : 2 * kRegions + 1;
     const int rblock = kRegions - min(deg, kRegions);
-    return (uint16_t)(pi | (block << 6) | (rblock << (6 + kBlockBits)));
+    return (uint16_t)(pi | (block << 6) | (rblock << (6 + kBlockBits)) | ((deg > kRegions ? 1 : 0) << kDegOvfBit));
 }
 
 // ---------------------------------------------------------------------------

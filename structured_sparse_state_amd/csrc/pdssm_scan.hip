@@ -385,10 +385,15 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
     // tile's entries, one row of NP 16-bit entries per (wave, step).
     extern __shared__ __attribute__((aligned(16))) uint32_t s_tab[];
     __shared__ int16_t s_sel[W][G * T];
-    __shared__ __attribute__((aligned(16))) cf s_reg[W][kBlocks][64];   // scatter regions, zero blocks, spare
+    // Scatter regions, zero blocks, spare region and trash block per chunk
+    // wave.  The trash block only takes stores during the wave's local pass;
+    // between local passes it holds the d part of the wave's chunk operators
+    // (slot wave * 64 + lane), which is written after the local pass and last
+    // read before (D).
+    __shared__ __attribute__((aligned(16))) cf s_reg[W][kBlocks][64];
     __shared__ cf s_cscr[64];   // the carry wave's scatter scratch
     __shared__ int s_pi[SLOTS];   // chunk operators, then their inclusive prefixes
-    __shared__ cf s_d[SLOTS];
+    auto s_d = [&](int slot) -> cf & { return s_reg[slot >> 6][kBlocks - 1][slot & 63]; };
     __shared__ cf s_e[SLOTS];
     __shared__ cf s_xin[64];
     __shared__ float s_y[TILE];   // a finished tile's outputs, stored by the carry wave
@@ -524,7 +529,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             if (act) {
                 const int as = wave_at(W - 1) * 64 + (G - 1) * NP + lane;
                 ppi = s_pi[as];
-                pd = s_d[as];
+                pd = s_d(as);
                 pe = s_e[as];
             }
             // Every chunk wave is past its local pass, the only reader of the
@@ -767,17 +772,19 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                 // x_t = P_t (d_t * x_{t-1}) + b_t.  Source j stores into the
                 // slot its entry names: region rank(j) at row pi(j), so within
                 // a region every row has at most one source and plain stores
-                // suffice.  Sources of rank >= kRegions (rare) go to the spare
-                // block and then add atomically into the last region.  Row i
-                // reads kRegions blocks from the offset its entry names: the
-                // in-degree(i) regions written in this step, then zero blocks.
+                // suffice (rank kRegions: the spare region).  Sources of
+                // higher rank (rare) store into the trash block and then add
+                // atomically into the spare slot of their row.  Row i reads
+                // kRegions blocks from the offset its entry names: the
+                // in-degree(i) regions written in this step, then zero
+                // blocks; a row with more sources also reads its spare slot.
                 const cf v = cmul(d, x);
                 const uint32_t slot = entry_slot(ent);   // block * 512 + pi * 8
                 *static_cast<float2 *>(__builtin_assume_aligned(regp + slot, 8)) = make_float2(v.r, v.i);
                 lds_order();
-                if (__any(slot >= kSpareOff)) {
-                    if (slot >= kSpareOff) {
-                        cf *o = reinterpret_cast<cf *>(regp + (slot - kSpareOff));
+                if (__any(slot_rank_ovf(slot))) {
+                    if (slot_rank_ovf(slot)) {
+                        cf *o = reinterpret_cast<cf *>(regp + (slot - kRegionBytes));
                         lds_add(&o->r, v.r);
                         if constexpr (CPLX)
                             lds_add(&o->i, v.i);
@@ -789,6 +796,13 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                 for (int r = 0; r < kRegions; ++r) {
                     const float2 u = *static_cast<const float2 *>(__builtin_assume_aligned(rowp + r * kRegionBytes, 8));
                     uu[r] = {u.x, u.y};
+                }
+                if (__any(entry_deg_ovf(ent))) {
+                    if (entry_deg_ovf(ent)) {
+                        const float2 u = *static_cast<const float2 *>(__builtin_assume_aligned(rowbase + kSpareOff, 8));
+                        uu[0].r += u.x;
+                        uu[0].i += u.y;
+                    }
                 }
                 lds_order();
             }
@@ -865,7 +879,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                     const uint32_t f = *reinterpret_cast<volatile uint32_t *>(&s_ready);
                     lds_order();
                     ppi = s_pi[ps];
-                    pd = s_d[ps];
+                    pd = s_d(ps);
                     pe = s_e[ps];
                     lds_order();
                     if (__builtin_amdgcn_readfirstlane(f) & need)
@@ -883,7 +897,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                     if (g > 0) {
                         const int ps = wave * 64 + (g - 1) * NP + q.i;
                         ppi = s_pi[ps];
-                        pd = s_d[ps];
+                        pd = s_d(ps);
                         pe = s_e[ps];
                     }
                     const int src = (q.gbase + ppi) * 4;
@@ -896,7 +910,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                 }
                 if (q.g == g) {
                     s_pi[slot] = rpi;
-                    s_d[slot] = rd;
+                    s_d(slot) = rd;
                     s_e[slot] = re;
                     api = rpi;
                     ad = rd;
@@ -942,7 +956,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             cf pd = {1.f, 0.f}, pe = {0.f, 0.f};
             if (chunk > 0) {
                 ppi = s_pi[pslot];
-                pd = s_d[pslot];
+                pd = s_d(pslot);
                 pe = s_e[pslot];
             }
             // The previous wave's slots are rewritten with its next operator
@@ -995,12 +1009,13 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
         }
         if (!more)
             return;
-        // The selection of the next tile (its scores have been in flight
-        // since (B)), then its first input steps: issued only now, they keep
-        // their registers free through the readout, and the selection's wait
-        // for the scores does not also wait for them.
-        select();
+        // The next tile's first input steps, then its selection (its scores
+        // have been in flight since (B)).  Issued only after the readout, the
+        // input loads keep their registers free through it; issued before
+        // the selection, their latency overlaps the selection's work (its
+        // wait for the scores, loaded earlier, does not wait for them).
         issue_inputs();
+        select();
         cur = nxt;
     }
 }
