@@ -174,12 +174,12 @@ def measure_aux(pk, gen, inp, stream):
 
     # Router scores + argmax from the step inputs (D = 2048 features per
     # token), only the int16 selections written; the fused kernel takes up
-    # to 64 scores per head.
+    # to 128 scores per head (heads padded to 64 or 128 score columns).
     D = ROUTER_D
-    if K > 64:
+    if K > 128:
         dec_bytes = sum(t.numel() * t.element_size() for t in (sel, d, b, c, y)) + 2 * x.numel() * 4
         print(f"[bench] dict hardmax {t_hm * 1e6:.1f} us ({hm_bytes / t_hm / 1e9:.0f} GB/s); decode step "
-              f"{t_dec * 1e6:.2f} us ({B * H / t_dec:.3g} tokens/s); router: K={K} > 64, not run",
+              f"{t_dec * 1e6:.2f} us ({B * H / t_dec:.3g} tokens/s); router: K={K} > 128, not run",
               file=sys.stderr, flush=True)
         return {
             "dict_hardmax": {"us_per_call": t_hm * 1e6, "shape": f"H={H} K={K} N={N} fp32",
@@ -202,7 +202,7 @@ def measure_aux(pk, gen, inp, stream):
         torch.cuda.synchronize()
     t_rt = _event_time(lambda: pk.router_select(ru, rw, out=rsel, stream=stream), 50, 3, stream)
     rt_flops = 2.0 * B * inp.L * H * K * D
-    rt_pad_flops = 2.0 * B * inp.L * H * 64 * D
+    rt_pad_flops = 2.0 * B * inp.L * H * (64 if K <= 64 else 128) * D
     del ru, rw, rsel
     dec_bytes = sum(t.numel() * t.element_size() for t in (sel, d, b, c, y)) + 2 * x.numel() * 4
     print(f"[bench] dict hardmax {t_hm * 1e6:.1f} us ({hm_bytes / t_hm / 1e9:.0f} GB/s); decode step "

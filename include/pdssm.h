@@ -274,7 +274,7 @@ int pdssm_decode_step(const void *sel_or_logits, const int32_t *dict_idx, const 
  *   u        bf16 [B,L,D] step inputs
  *   w        bf16 [H,K,D] router weights
  *   sel_out  int16 [B,H,L] output
- *   K in [1,64]; D a positive multiple of 32; flags must be 0.  B, L or H
+ *   K in [1,128]; D a positive multiple of 32; flags must be 0.  B, L or H
  *   may be 0: nothing is read or written then.
  * The scores are fp32 sums in an unspecified order: where two scores are
  * within their rounding error of each other, either index may be returned.

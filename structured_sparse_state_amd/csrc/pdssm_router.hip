@@ -7,17 +7,23 @@
 //     scores[b,h,t,k] = sum_d u[b,t,d] * w[h,k,d]        (no bias)
 //     sel[b,h,t]      = argmax_k scores[b,h,t,k]         (first maximum wins)
 //
-// As a matrix product: C[M, H*64] = U[M, D] * W^T with M = B*L tokens and each
-// head's K <= 64 weight rows padded to 64 columns.  It is a dense
+// As a matrix product: C[M, H*P] = U[M, D] * W^T with M = B*L tokens and each
+// head's K weight rows padded to P = 64 or 128 columns.  It is a dense
 // contraction, so it runs on the matrix cores: v_mfma_f32_32x32x16_bf16,
-// fp32 accumulation.  A workgroup computes a 256-token x 2-head tile; each of
-// its four waves owns 128 tokens x one head (4 x 2 MFMA tiles), so the argmax
-// over a head's scores stays inside one wave.  U and W tiles of 32 features
-// go straight from global memory into a three-stage LDS ring
-// (global_load_lds, 16 bytes per lane, chunks swizzled within each row so
-// fragment reads do not conflict); two stages are in flight while the third
-// is consumed.
+// fp32 accumulation.  A workgroup computes a 256-token x 256-column tile
+// (256/P heads); each of its four waves owns 128 tokens x 128 columns
+// (4 x 4 MFMA tiles, 256 accumulators, one wave per SIMD), so every head's
+// scores stay inside one wave and each fragment read from LDS feeds four
+// MFMAs.  U and W tiles of 32 features go straight from global memory into
+// a ring of LDS stages (global_load_lds, 16 bytes per lane, chunks swizzled
+// within each row so fragment reads do not conflict).  With one wave per
+// SIMD nothing else hides latency, so the loop is software-pipelined: the
+// fragments of the next 16 features are read while the MFMAs of the current
+// ones run, and every stage's loads are issued a whole ring ahead.
 #include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <type_traits>
 
 #include "pdssm.h"
 #include "pdssm_device.h"
@@ -29,41 +35,32 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-#ifndef PDSSM_ROUTER_HEADS
-#define PDSSM_ROUTER_HEADS 2
-#endif
-constexpr int kRM = 256;                  // tokens per workgroup tile
-constexpr int kRH = PDSSM_ROUTER_HEADS;   // heads per workgroup tile (2 or 4)
-constexpr int kWH = kRH / 2;              // heads per wave (waves are 2 x 2)
-constexpr int kNT = 2 * kWH;              // 32-column MFMA tiles per wave
-constexpr int kRN = kRH * 64;             // padded score columns per tile
-#ifndef PDSSM_ROUTER_BK
-#define PDSSM_ROUTER_BK 32
-#endif
-#ifndef PDSSM_ROUTER_STAGES
-#define PDSSM_ROUTER_STAGES 2
-#endif
-constexpr int kRK = PDSSM_ROUTER_BK;      // features per LDS stage (32 or 64)
-constexpr int kRStages = PDSSM_ROUTER_STAGES;
-constexpr int kRowBytes = kRK * 2;        // bytes of one row of a stage
-constexpr int kChunks = kRK / 8;          // 16-byte chunks per row
-constexpr int kRowsPerLoad = 64 / kChunks;   // rows one 64-lane 16-byte load fills
-constexpr int kABytes = kRM * kRowBytes;  // token rows per stage
-constexpr int kBBytes = kRN * kRowBytes;  // weight rows per stage
-constexpr int kStageBytes = kABytes + kBBytes;
+constexpr int kRM = 256;     // tokens per workgroup tile
+constexpr int kRN = 256;     // score columns per workgroup tile
 constexpr int kRThreads = 256;
-constexpr int kALoads = kRM / kRowsPerLoad / 4;   // direct-to-LDS loads per wave per stage
-constexpr int kBLoads = kRN / kRowsPerLoad / 4;
-constexpr int kLoadsPerStage = kALoads + kBLoads;
-// Workgroups per CU that the LDS allows (one wave of each per SIMD), at most
-// three with one head per wave (about 168 VGPRs, 128 of them accumulators)
-// and one with two (256 accumulators).
-constexpr int kRWaveCap = kWH == 1 ? 3 : 1;
-constexpr int kRWavesPerEU = (160 * 1024) / (kRStages * kStageBytes) < kRWaveCap
-                                 ? (160 * 1024) / (kRStages * kStageBytes) : kRWaveCap;
-static_assert(kRH == 2 || kRH == 4, "heads per tile");
-static_assert(kRK == 16 || kRK == 32 || kRK == 64, "stage depth");
-static_assert(kRStages >= 2 && kRStages * kStageBytes <= 160 * 1024, "stages fit in LDS");
+constexpr int kRingBytes = 128 * 1024;   // LDS ring of every stage depth
+
+// The LDS stage of BK features: 64 (two stages in the ring) when the feature
+// count allows it, else 32 (four stages).  Deeper stages mean fewer stage
+// hand-overs (barriers) per MFMA.
+template <int BK>
+struct StageGeom {
+    static constexpr int kRK = BK;                      // features per LDS stage
+    static constexpr int kRowBytes = BK * 2;            // bytes of one row of a stage
+    static constexpr int kChunks = BK / 8;              // 16-byte chunks per row
+    static constexpr int kRowsPerLoad = 64 / kChunks;   // rows one 64-lane 16-byte load fills
+    static constexpr int kABytes = kRM * kRowBytes;     // token rows per stage
+    static constexpr int kBBytes = kRN * kRowBytes;     // weight rows per stage
+    static constexpr int kStageBytes = kABytes + kBBytes;
+    static constexpr int kRStages = kRingBytes / kStageBytes;
+    static constexpr int kALoads = kRM / kRowsPerLoad / 4;   // direct-to-LDS loads per wave per stage
+    static constexpr int kBLoads = kRN / kRowsPerLoad / 4;
+    static constexpr int kLoadsPerStage = kALoads + kBLoads;
+    static_assert(BK == 32 || BK == 64, "stage depth");
+    static_assert(kRStages >= 2 && kRStages <= 4, "stage waits cover up to three younger stages");
+    static_assert((BK / 16) % 2 == 0, "the fragment double buffer alternates by step parity");
+    static_assert(kLoadsPerStage * 3 < 64, "vmcnt range");
+};
 
 struct RouterArgs {
     const uint16_t *u;   // [M][D] bf16
@@ -71,33 +68,54 @@ struct RouterArgs {
     int16_t *sel;        // [B][H][L]
     int64_t M, L, H;
     int K, D;
-    uint32_t m_tiles, h_tiles;
+    uint32_t m_tiles, n_tiles;
 };
 
 // Position of 16-byte chunk c of row r inside the row.  A fragment read
 // (ds_read_b128) has lane l read row l % 32 of a 32-row block; the chunks are
-// rotated from row to row so that both the 8 lanes of every 128-byte group
-// and the 16 lanes of every 256-byte group of the read land on distinct
-// 16-byte bank groups.  The rotation depends on r % 32 only: fragments
-// start at multiples of 32 rows.
+// rotated from row to row so that the reads do not conflict in the LDS banks
+// (for four chunks per row the rotation was chosen by measuring fragment-read
+// throughput: three of eight candidate rotations run 1.5 times faster than
+// the others and match the conflict-free eight-chunk rotation's rate).  The
+// rotation depends on r % 32 only: fragments start at multiples of 32 rows.
+template <int kChunks>
 __device__ __forceinline__ int chunk_pos(int r, int c)
 {
-    if constexpr (kChunks == 2)
-        return c ^ (((r >> 2) ^ (r >> 3)) & 1);
-    else if constexpr (kChunks == 4)
-        return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+    if constexpr (kChunks == 4)
+        return c ^ ((r ^ (r >> 2)) & 3);
     else
         return c ^ ((r ^ ((r >> 3) & 3)) & 7);
 }
 
-// better() of the selection (the score, then the lower index; a NaN above
-// every number, the first NaN winning) as one boolean expression, so that the
-// compiler selects instead of branching per comparison.
-__device__ __forceinline__ bool beats(float v2, int k2, float v1, int k1)
+// The selection's order (the score, then the lower index; -0 equal to +0; a
+// NaN above every number, the first NaN winning) as one signed 64-bit key:
+// the score's bits mapped to an int32 that orders like the value (negative
+// values have their magnitude bits flipped, -0 is made +0 first, every NaN
+// becomes INT32_MAX) in the high word, 255 - k in the low word.  The larger
+// key wins, so a max over keys is the argmax with ties to the lowest index.
+__device__ __forceinline__ int64_t score_key(float v, int k)
 {
-    const bool n1 = v1 != v1, n2 = v2 != v2;
-    const bool klt = k2 < k1;
-    return (n2 & (!n1 | klt)) | (!n2 & !n1 & ((v2 > v1) | ((v2 == v1) & klt)));
+    const float f = v + 0.0f;   // -0 + 0 = +0 (round to nearest); NaN stays NaN
+    const int32_t i = __float_as_int(f);
+    int32_t key = i ^ ((i >> 31) & 0x7fffffff);
+    key = (f != f) ? 0x7fffffff : key;
+    return (int64_t)(((uint64_t)(uint32_t)key << 32) | (uint32_t)(255 - k));
+}
+constexpr int64_t kNoKey = INT64_MIN;   // a padding column: below every score
+__device__ __forceinline__ int64_t kmax(int64_t a, int64_t b) { return a > b ? a : b; }
+
+// The partner's 64-bit value across lane bit BIT (0..3) inside a row of 16
+// lanes (DPP moves of both halves).  For bit 2 the partner is the mirror lane
+// 7-i, which differs in bit 2 and keeps bits >= 3: for a reduction that
+// later combines across bits 1 and 0, every lane still meets all eight.
+template <int BIT>
+__device__ __forceinline__ int64_t key_across(int64_t v)
+{
+    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)((uint64_t)v >> 32);
+    constexpr int CTRL = BIT == 3 ? 0x128 : BIT == 2 ? 0x141 : BIT == 1 ? 0x4E : 0xB1;
+    const int plo = __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xF, 0xF, false);
+    const int phi = __builtin_amdgcn_update_dpp(0, hi, CTRL, 0xF, 0xF, false);
+    return (int64_t)(((uint64_t)(uint32_t)phi << 32) | (uint32_t)plo);
 }
 
 // s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
@@ -108,21 +126,32 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-__global__ void __launch_bounds__(kRThreads, kRWavesPerEU) router_kernel(RouterArgs a)
+// P: padded score columns per head (64 or 128); a wave's 128 columns hold
+// 128 / P heads.
+template <int P, int BK>
+__global__ void __launch_bounds__(kRThreads, 1) router_kernel(RouterArgs a)
 {
-    __shared__ __attribute__((aligned(1024))) char smem[kRStages * kStageBytes];
+    using SG = StageGeom<BK>;
+    constexpr int kRK = SG::kRK, kRowBytes = SG::kRowBytes, kChunks = SG::kChunks,
+                  kRowsPerLoad = SG::kRowsPerLoad, kABytes = SG::kABytes, kStageBytes = SG::kStageBytes,
+                  kRStages = SG::kRStages, kALoads = SG::kALoads, kBLoads = SG::kBLoads,
+                  kLoadsPerStage = SG::kLoadsPerStage;
+    constexpr int HW = 128 / P;   // heads per wave
+    constexpr int NI = P / 32;    // 32-column MFMA tiles per head
+    __shared__ __attribute__((aligned(1024))) char smem[kRingBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     // Tile of this workgroup.  Consecutive workgroups go to different XCDs;
-    // the mapping gives each XCD a contiguous run of tiles, so the head tiles
-    // of one token tile (which read the same U rows) share that XCD's L2.
-    const uint32_t total = a.m_tiles * a.h_tiles, per = total / 8;
+    // the mapping gives each XCD a contiguous run of tiles, so the column
+    // tiles of one token tile (which read the same U rows) share that XCD's
+    // L2.
+    const uint32_t total = a.m_tiles * a.n_tiles, per = total / 8;
     const uint32_t bx = blockIdx.x;
     const uint32_t tile = (bx < per * 8) ? (bx % 8) * per + bx / 8 : bx;
-    const uint32_t mt = tile / a.h_tiles, ht = tile % a.h_tiles;
+    const uint32_t mt = tile / a.n_tiles, nt = tile % a.n_tiles;
     const int64_t m0 = (int64_t)mt * kRM;
-    const int64_t h0 = (int64_t)ht * kRH;
+    const int64_t h0 = (int64_t)nt * (kRN / P);
     const int D = a.D, K = a.K;
 
     // Direct-to-LDS loads: load j of this wave fills the kRowsPerLoad rows
@@ -136,25 +165,23 @@ __global__ void __launch_bounds__(kRThreads, kRWavesPerEU) router_kernel(RouterA
     for (int j = 0; j < kALoads; ++j) {
         const int r = kRowsPerLoad * (wave * kALoads + j) + lane / kChunks;
         const int64_t m = m0 + r;
-        asrc[j] = a.u + (m < a.M ? m : 0) * (int64_t)D + chunk_pos(r, lane % kChunks) * 8;
+        asrc[j] = a.u + (m < a.M ? m : 0) * (int64_t)D + chunk_pos<kChunks>(r, lane % kChunks) * 8;
     }
     const uint16_t *bsrc[kBLoads];
 #pragma unroll
     for (int j = 0; j < kBLoads; ++j) {
         const int col = kRowsPerLoad * (wave * kBLoads + j) + lane / kChunks;
-        const int64_t h = h0 + col / 64;
-        const int k = col % 64;
-        bsrc[j] = a.w + ((h < a.H && k < K) ? (h * K + k) : 0) * (int64_t)D + chunk_pos(col, lane % kChunks) * 8;
+        const int64_t h = h0 + col / P;
+        const int k = col % P;
+        bsrc[j] = a.w + ((h < a.H && k < K) ? (h * K + k) : 0) * (int64_t)D + chunk_pos<kChunks>(col, lane % kChunks) * 8;
     }
     // The loads are written in asm so that the compiler does not see them
     // as stores to LDS: it would otherwise make every fragment read wait
     // for all of them (it cannot tell the stages apart).  They write no
-    // registers; the stage waits below are explicit.
+    // registers; the stage waits below are explicit.  M0 carries the LDS
+    // address as an input operand.
     auto dma = [](const uint16_t *src, uint32_t lds) {
-        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                     :
-                     : "v"(src), "s"(lds)
-                     : "memory", "m0");
+        asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
     };
     auto issue = [&](char *buf, int k0) {
         const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(buf));
@@ -166,13 +193,13 @@ __global__ void __launch_bounds__(kRThreads, kRWavesPerEU) router_kernel(RouterA
             dma(bsrc[j] + k0, base + (uint32_t)(kABytes + (wave * kBLoads + j) * 1024));
     };
 
-    // This wave: tokens wm*128 .. +128 of the tile, heads wn*kWH .. +kWH.
+    // This wave: tokens wm*128 .. +128 of the tile, columns wn*128 .. +128.
     const int wm = wave >> 1, wn = wave & 1;
-    f32x16 acc[4][kNT];
+    f32x16 acc[4][4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < kNT; ++ni)
+        for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 acc[mi][ni][e] = 0.f;
@@ -180,102 +207,160 @@ __global__ void __launch_bounds__(kRThreads, kRWavesPerEU) router_kernel(RouterA
     // Fragments: row (lane % 32) of a 32-row block, features 16 ks + 8 (lane
     // / 32).  Blocks start at multiples of 32 rows, so the swizzled offset of
     // the lane inside a block depends on the lane and ks only.
-    uint32_t lane_off[kRK / 16];
+    constexpr int KS = kRK / 16;   // 16-feature MFMA steps per stage
+    uint32_t lane_off[KS];
 #pragma unroll
-    for (int ks = 0; ks < kRK / 16; ++ks)
-        lane_off[ks] = (uint32_t)((lane & 31) * kRowBytes + chunk_pos(lane & 31, ks * 2 + (lane >> 5)) * 16);
-    auto compute = [&](const char *base) {
-        const char *ab = base + wm * 128 * kRowBytes;
-        const char *bb = base + kABytes + wn * kWH * 64 * kRowBytes;
+    for (int ks = 0; ks < KS; ++ks)
+        lane_off[ks] = (uint32_t)((lane & 31) * kRowBytes + chunk_pos<kChunks>(lane & 31, ks * 2 + (lane >> 5)) * 16);
+    bf16x8 af[2][4], bf[2][4];
+    auto read_frags = [&](int buf, const char *base, int ks) {
+        const char *ab = base + wm * 128 * kRowBytes + lane_off[ks];
+        const char *bb = base + kABytes + wn * 128 * kRowBytes + lane_off[ks];
 #pragma unroll
-        for (int ks = 0; ks < kRK / 16; ++ks) {
-            bf16x8 af[4], bf[kNT];
+        for (int mi = 0; mi < 4; ++mi)
+            af[buf][mi] = *reinterpret_cast<const bf16x8 *>(ab + mi * 32 * kRowBytes);
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-                af[mi] = *reinterpret_cast<const bf16x8 *>(ab + mi * 32 * kRowBytes + lane_off[ks]);
-#pragma unroll
-            for (int ni = 0; ni < kNT; ++ni)
-                bf[ni] = *reinterpret_cast<const bf16x8 *>(bb + ni * 32 * kRowBytes + lane_off[ks]);
-#pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < kNT; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bf[ni], acc[mi][ni], 0, 0, 0);
-        }
+        for (int ni = 0; ni < 4; ++ni)
+            bf[buf][ni] = *reinterpret_cast<const bf16x8 *>(bb + ni * 32 * kRowBytes);
     };
-
-    // Ring of kRStages stages: stage s is consumed while the next
-    // kRStages - 1 load.  Before consuming s each wave waits for its own
-    // loads of s (those of the younger stages may stay in flight), then the
-    // barrier makes every wave's rows of s visible and frees the buffer of
-    // s - 1, which the loads of s + kRStages - 1 then refill.
-    const int stages = D / kRK;
+    auto mfmas = [&](int buf) {
 #pragma unroll
-    for (int p = 0; p < kRStages - 1; ++p)
-        if (p < stages)
-            issue(smem + p * kStageBytes, p * kRK);
-    for (int s = 0; s < stages; ++s) {
-        const int ahead = min(stages - 1 - s, kRStages - 2);   // younger stages already issued
-        if (ahead >= kRStages - 2)
-            wait_vm<kLoadsPerStage * (kRStages - 2)>();
-        else if (kRStages > 3 && ahead == 1)
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][mi], bf[buf][ni], acc[mi][ni], 0, 0, 0);
+    };
+    // The own loads of stage s have landed once at most `ahead` younger
+    // stages' loads are still in flight.
+    auto wait_stage = [&](int ahead) {
+        if (ahead >= 3)
+            wait_vm<kLoadsPerStage * 3>();
+        else if (ahead == 2)
+            wait_vm<kLoadsPerStage * 2>();
+        else if (ahead == 1)
             wait_vm<kLoadsPerStage>();
         else
             wait_vm<0>();
-        __builtin_amdgcn_s_barrier();
-        lds_order();   // no LDS access moves across the barrier
-        if (s + kRStages - 1 < stages)
-            issue(smem + ((s + kRStages - 1) % kRStages) * kStageBytes, (s + kRStages - 1) * kRK);
-        compute(smem + (s % kRStages) * kStageBytes);
+    };
+
+    // Software pipeline over 16-feature steps g = s * KS + ks: the fragments
+    // of step g + 1 are read from LDS while the MFMAs of step g run.  Ring of
+    // kRStages stages, all in flight: in the last step of stage s each wave
+    // has finished its reads of stage s (its fragments are in registers),
+    // waits for its own loads of stage s + 1, and the barrier makes every
+    // wave's rows of s + 1 visible and frees the buffer of stage s, which the
+    // loads of stage s + kRStages then refill.
+    const int stages = D / kRK;
+    char *const ring = smem;
+#pragma unroll
+    for (int p = 0; p < kRStages; ++p)
+        if (p < stages)
+            issue(ring + p * kStageBytes, p * kRK);
+    wait_stage(min(stages - 1, kRStages - 1));
+    __builtin_amdgcn_s_barrier();
+    lds_order();
+    read_frags(0, ring, 0);
+    // Every stage but the last hands over to the next one in its last step;
+    // the last stage is peeled off, so the loop body has one count of LDS
+    // operations in flight on every path (the compiler's waits then let the
+    // next fragments stay in flight under the MFMAs).
+    for (int s = 0; s + 1 < stages; ++s) {
+        const char *cur = ring + (s % kRStages) * kStageBytes;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int buf = ks & 1;   // KS is even: step parity
+            if (ks + 1 < KS) {
+                read_frags(buf ^ 1, cur, ks + 1);
+            } else {
+                // this wave's reads of stage s are done (its fragments of
+                // this step are waited for here), then stage s + 1
+                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+                wait_stage(min(stages - 2 - s, kRStages - 2));   // issued so far: stages up to s + kRStages - 1
+                __builtin_amdgcn_s_barrier();
+                lds_order();   // no LDS access moves across the barrier
+                if (s + kRStages < stages)
+                    issue(ring + (s % kRStages) * kStageBytes, (s + kRStages) * kRK);
+                read_frags(buf ^ 1, ring + ((s + 1) % kRStages) * kStageBytes, 0);
+            }
+            // Keep the next fragments' reads (and the stage hand-over) ahead
+            // of this step's MFMAs, so their latency runs under the MFMAs
+            // still queued from the step before.
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(buf);
+            // and keep the hand-over's wait for this wave's reads after the
+            // MFMAs that run while those reads land
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    {
+        const char *cur = ring + ((stages - 1) % kRStages) * kStageBytes;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS)
+                read_frags((ks & 1) ^ 1, cur, ks + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(ks & 1);
+        }
     }
 
     // Argmax per token over the head's K scores.  acc[mi][ni][e] is the
-    // score of token wm*128 + mi*32 + 8*(e/4) + 4*(lane/32) + e%4 and entry
-    // k = ni*32 + lane%32.  Each lane first keeps the better of its two
-    // entries for each of its 64 tokens (c = mi*16 + e); then the 32 lanes
-    // of each half-wave reduce by recursive halving: at the exchange with the
-    // lane 2^s apart, a lane keeps half of its tokens and hands the other
-    // half to its partner, so after five exchanges lane l holds the result of
-    // tokens c = 2 (l % 32) and 2 (l % 32) + 1 (62 values sent per lane
-    // instead of 5 per token).  better() orders by score, then by lower
-    // index, so the merge order does not matter.
+    // score of token wm*128 + mi*32 + 8*(e/4) + 4*(lane/32) + e%4 and column
+    // ni*32 + lane%32 of the wave, i.e. entry k = (ni % NI)*32 + lane%32 of
+    // head ni / NI.  Each lane first keeps the best key of its NI entries for
+    // each of its 64 tokens (c = mi*16 + e); then the 32 lanes of each
+    // half-wave reduce by recursive halving: at the exchange across lane bit
+    // b, a lane keeps the half of its tokens that its bit selects and takes
+    // its partner's keys of that half, so after five exchanges lane l holds
+    // the result of tokens c = 2 (l % 32) and 2 (l % 32) + 1.  The exchange
+    // across bit 4 is one v_permlane16_swap per register (odd and even rows
+    // trade halves), the others DPP moves; the max over keys is associative
+    // and commutative, so the pairing order does not matter.
 #pragma unroll
-    for (int hn = 0; hn < kWH; ++hn) {
-        const int64_t h = h0 + wn * kWH + hn;
-        float bv[64];
-        int bk[64];
+    for (int hn = 0; hn < HW; ++hn) {
+        const int64_t h = h0 + wn * HW + hn;
+        int64_t kv[64];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int c = mi * 16 + e;
-                const int k0 = lane & 31, k1 = 32 + (lane & 31);
-                bv[c] = (k0 < K) ? acc[mi][2 * hn][e] : __uint_as_float(0xFF800000u);   // -inf: beaten by any score
-                bk[c] = (k0 < K) ? k0 : 64;
-                const bool take = (k1 < K) & beats(acc[mi][2 * hn + 1][e], k1, bv[c], bk[c]);
-                bv[c] = take ? acc[mi][2 * hn + 1][e] : bv[c];
-                bk[c] = take ? k1 : bk[c];
+                int64_t best = kNoKey;
+#pragma unroll
+                for (int t = 0; t < NI; ++t) {
+                    const int kt = t * 32 + (lane & 31);
+                    best = kmax(best, kt < K ? score_key(acc[mi][hn * NI + t][e], kt) : kNoKey);
+                }
+                kv[mi * 16 + e] = best;
             }
         }
+        // bit 4: lanes l and l ^ 16 (odd and even rows)
 #pragma unroll
-        for (int st = 0; st < 5; ++st) {
-            const int m = 16 >> st;          // partner distance
-            const int n = 32 >> st;          // tokens kept after this exchange
-            const bool upper = (lane & m) != 0;
-#pragma unroll
-            for (int i = 0; i < n; ++i) {
-                // keep i (lower lane) or n + i (upper lane); send the other
-                const float sv = upper ? bv[i] : bv[n + i];
-                const int sk = upper ? bk[i] : bk[n + i];
-                float kv = upper ? bv[n + i] : bv[i];
-                int kk = upper ? bk[n + i] : bk[i];
-                const float ov = __shfl_xor(sv, m, 64);
-                const int ok = __shfl_xor(sk, m, 64);
-                const bool take = beats(ov, ok, kv, kk);
-                bv[i] = take ? ov : kv;
-                bk[i] = take ? ok : kk;
-            }
+        for (int i = 0; i < 32; ++i) {
+            uint32_t alo = (uint32_t)kv[i], ahi = (uint32_t)((uint64_t)kv[i] >> 32);
+            uint32_t blo = (uint32_t)kv[32 + i], bhi = (uint32_t)((uint64_t)kv[32 + i] >> 32);
+            // after the swap, lanes with bit 4 clear hold token i of both
+            // lanes, lanes with bit 4 set token 32 + i of both
+            const auto rl = __builtin_amdgcn_permlane16_swap(alo, blo, false, false);
+            const auto rh = __builtin_amdgcn_permlane16_swap(ahi, bhi, false, false);
+            const int64_t x = (int64_t)(((uint64_t)rh[0] << 32) | rl[0]);
+            const int64_t y = (int64_t)(((uint64_t)rh[1] << 32) | rl[1]);
+            kv[i] = kmax(x, y);
         }
+        auto level = [&](auto bitc, int n) {
+            constexpr int BIT = decltype(bitc)::value;
+            const bool up = (lane >> BIT) & 1;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (i < n) {
+                    const int64_t send = up ? kv[i] : kv[n + i];
+                    const int64_t keep = up ? kv[n + i] : kv[i];
+                    kv[i] = kmax(keep, key_across<BIT>(send));
+                }
+            }
+        };
+        level(std::integral_constant<int, 3>{}, 16);
+        level(std::integral_constant<int, 2>{}, 8);
+        level(std::integral_constant<int, 1>{}, 4);
+        level(std::integral_constant<int, 0>{}, 2);
         if (h < a.H) {
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
@@ -283,7 +368,7 @@ __global__ void __launch_bounds__(kRThreads, kRWavesPerEU) router_kernel(RouterA
                 const int64_t m = m0 + wm * 128 + mi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
                 if (m < a.M) {
                     const int64_t b = m / a.L, t = m - b * a.L;
-                    a.sel[(b * a.H + h) * a.L + t] = (int16_t)bk[r];
+                    a.sel[(b * a.H + h) * a.L + t] = (int16_t)(255 - (int)(uint32_t)kv[r]);
                 }
             }
         }
@@ -298,11 +383,12 @@ using namespace pdssm;
 extern "C" int pdssm_router_select(const void *u, const void *w, int16_t *sel_out, int64_t B, int64_t L,
                                    int64_t H, int32_t K, int32_t D, uint32_t flags, hipStream_t stream)
 {
-    if (B < 0 || L < 0 || H < 0 || K < 1 || K > 64 || D < kRK || (D % kRK) != 0)
+    if (B < 0 || L < 0 || H < 0 || K < 1 || K > 128 || D < 32 || (D % 32) != 0)
         return PDSSM_ERR_DIM;
+    const int P = K <= 64 ? 64 : 128;
     const double tokens = (double)B * (double)L;
-    const double m_tiles = (tokens + kRM - 1) / kRM, h_tiles = (double)((H + kRH - 1) / kRH);
-    if (tokens > 2.0e9 || m_tiles * h_tiles > 2.0e9 || (double)H * K * D > 4.0e18)
+    const double m_tiles = (tokens + kRM - 1) / kRM, n_tiles = (double)((H * P + kRN - 1) / kRN);
+    if (tokens > 2.0e9 || m_tiles * n_tiles > 2.0e9 || (double)H * K * D > 4.0e18)
         return PDSSM_ERR_DIM;
     if (flags != 0)
         return PDSSM_ERR_FLAGS;
@@ -322,7 +408,16 @@ extern "C" int pdssm_router_select(const void *u, const void *w, int16_t *sel_ou
     a.K = K;
     a.D = D;
     a.m_tiles = (uint32_t)((a.M + kRM - 1) / kRM);
-    a.h_tiles = (uint32_t)((H + kRH - 1) / kRH);
-    hipLaunchKernelGGL(router_kernel, dim3(a.m_tiles * a.h_tiles), dim3(kRThreads), 0, stream, a);
+    a.n_tiles = (uint32_t)((H * P + kRN - 1) / kRN);
+    const dim3 grid(a.m_tiles * a.n_tiles), block(kRThreads);
+    const bool deep = (D % 64) == 0;
+    if (P == 64 && deep)
+        router_kernel<64, 64><<<grid, block, 0, stream>>>(a);
+    else if (P == 64)
+        router_kernel<64, 32><<<grid, block, 0, stream>>>(a);
+    else if (deep)
+        router_kernel<128, 64><<<grid, block, 0, stream>>>(a);
+    else
+        router_kernel<128, 32><<<grid, block, 0, stream>>>(a);
     return hip_status(hipGetLastError());
 }

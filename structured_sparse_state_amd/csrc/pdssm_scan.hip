@@ -1658,7 +1658,7 @@ extern "C" const char *pdssm_strerror(int status)
     case PDSSM_OK: return "success";
     case PDSSM_ERR_NULL: return "a required pointer is NULL";
     case PDSSM_ERR_DIM:
-        return "invalid sizes (B, H, L >= 0; N in [1,64]; K in [1,32767], at most 64 for the router; "
+        return "invalid sizes (B, H, L >= 0; N in [1,64]; K in [1,32767], at most 128 for the router; "
                "router D a positive multiple of 32; or a size too large)";
     case PDSSM_ERR_FLAGS: return "invalid flags";
     case PDSSM_ERR_ALIGN: return "a pointer is not 16-byte aligned";

@@ -223,7 +223,7 @@ def test_router_argument_errors(lib):
     assert r(None, FAKE, FAKE, 2, 100, 3, 64, 256, 0, 0) == pk.PDSSM_ERR_NULL
     assert r(FAKE, FAKE, None, 2, 100, 3, 64, 256, 0, 0) == pk.PDSSM_ERR_NULL
     for B, L, H, K, D in ((-1, 100, 3, 64, 256), (2, -1, 3, 64, 256), (2, 100, -1, 64, 256),
-                          (2, 100, 3, 0, 256), (2, 100, 3, 65, 256), (2, 100, 3, 64, 0),
+                          (2, 100, 3, 0, 256), (2, 100, 3, 129, 256), (2, 100, 3, 64, 0),
                           (2, 100, 3, 64, 48), (2, 100, 3, 64, 16)):
         assert r(FAKE, FAKE, FAKE, B, L, H, K, D, 0, 0) == pk.PDSSM_ERR_DIM, (B, L, H, K, D)
     assert r(FAKE, FAKE, FAKE, 2, 100, 3, 64, 256, 1, 0) == pk.PDSSM_ERR_FLAGS

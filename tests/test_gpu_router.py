@@ -63,6 +63,10 @@ ROUTER_SHAPES = [
     (2, 257, 5, 33, 96),
     (1, 511, 4, 64, 2048),
     (3, 90, 1, 17, 160),
+    # heads padded to 128 score columns (64 < K <= 128)
+    (2, 300, 3, 100, 256),
+    (1, 257, 2, 128, 512),
+    (1, 513, 5, 65, 96),
 ]
 
 
@@ -77,7 +81,8 @@ def test_router_matches_oracle(orc, B, L, H, K, D):
     say(f"  {n} near-tie choices differ from the oracle's of {ref.size}")
 
 
-@pytest.mark.parametrize("B,L,H,K,D", [(1, 300, 3, 64, 64), (2, 129, 2, 7, 512), (1, 256, 2, 64, 2048)])
+@pytest.mark.parametrize("B,L,H,K,D", [(1, 300, 3, 64, 64), (2, 129, 2, 7, 512), (1, 256, 2, 64, 2048),
+                                       (1, 300, 3, 128, 64), (2, 129, 3, 97, 512)])
 def test_router_exact_integers(orc, B, L, H, K, D):
     """Exact sums: the kernel's index equals the oracle's everywhere (the
     first maximum on ties)."""
