@@ -351,9 +351,9 @@ __device__ void publish_incl(const ScanArgs &a, int64_t tile, int64_t seq, uint3
 // and runs the look-back while the chunk waves are busy (the carry into a
 // tile depends only on earlier tiles).  Per tile:
 //
-//   chunk waves:  local pass, chain prefixes      (B) next tile's scores          (C) readout (D) ... next inputs, selection
-//   carry wave:   next ticket, look-back          (B) next table, previous y,
-//                                                     publish                     (C)         (D)
+//   chunk waves:  local pass, chain prefixes      (B) next tile's scores     (C) prefixes (D) readout, next inputs, selection
+//   carry wave:   next ticket, look-back          (B) next table, carry,
+//                                                     publish                (C)          (D) previous y
 //
 // so the next tile's router scores and first input steps are in flight
 // while the carry of the current one is worked out.  The two roles run on
@@ -396,7 +396,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
     auto s_d = [&](int slot) -> cf & { return s_reg[slot >> 6][kBlocks - 1][slot & 63]; };
     __shared__ cf s_e[SLOTS];
     __shared__ cf s_xin[64];
-    __shared__ float s_y[TILE];   // a finished tile's outputs, stored by the carry wave
+    __shared__ float s_y[2][TILE];   // finished tiles' outputs by iteration parity, stored by the carry wave
     __shared__ float s_q[TILE];   // per step: sum_j Re(c_t[j] x_loc_t[j]), until the correction
     __shared__ uint32_t s_next;   // ticket published by the carry wave
     __shared__ uint32_t s_ready;  // bit w: chunk wave w has posted its inclusive prefixes
@@ -543,20 +543,23 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                 if (!lb.attempt(a, epoch, lane, scr))
                     __builtin_amdgcn_s_sleep(PDSSM_CARRY_NAP);
             // The next table has landed (it was staged before (B)), then the
-            // state after the tile goes out, then the previous tile's outputs
-            // (final in s_y since the chunk waves posted; rewritten only after
-            // (D)); the stores need not complete here.
+            // state after the tile goes out at once: the next tile of the
+            // sequence may be waiting for it.
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             publish_incl<NP, CPLX>(a, tile, seq, epoch, lane, ppi, pd, pe, lb.xin, scr);
+            s_xin[lane] = lb.xin;
+            __syncthreads();   // (C) carry ready, next table staged
+            __syncthreads();   // (D) chunk waves have read the prefixes and the carry
+            // While the chunk waves run the readout: the previous tile's
+            // outputs, from the other s_y buffer (the chunk waves rewrite it
+            // only in the next iteration, after the next (D)); the stores
+            // need not complete here.
             if (have_prev)
                 for (int w = 0; w < W; ++w)
 #pragma unroll
                     for (int j = 0; j < YR; ++j)
                         if (j * 64 + lane < G * T)
-                            store_y(w, j, s_y[w * G * T + j * 64 + lane]);
-            s_xin[lane] = lb.xin;
-            __syncthreads();   // (C) carry ready, next table staged
-            __syncthreads();   // (D) chunk waves have read the prefixes and the carry
+                            store_y(w, j, s_y[(iter - 1) & 1][w * G * T + j * 64 + lane]);
             if (!more)
                 return;
             pt0 = (int64_t)tile * TILE;
@@ -997,7 +1000,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                     const int tt = r.g * T + GB::step_of(rr, r.i);   // step within the wave
                     const float yv = s_q[wave * G * T + tt] + wc[rr];
                     if (more) {
-                        s_y[wave * G * T + tt] = yv;
+                        s_y[iter & 1][wave * G * T + tt] = yv;
                     } else if (cw0 + tt < L) {
                         if (a.y_bf16)
                             (reinterpret_cast<uint16_t *>(a.y) + y0)[tt] = f32_to_bf16_rne(yv);
