@@ -147,7 +147,7 @@ def measure_hbm_practical(nbytes: int, stream):
                     "as one scan call; the practical streaming rate on this GPU, for context"}
 
 
-def measure_aux(pk, gen, inp, stream):
+def measure_aux(pk, gen, inp, stream, workload):
     """The dictionary pre-compute and one decode step at the workload's
     shape, HIP events on the launch stream."""
     import torch
@@ -171,6 +171,46 @@ def measure_aux(pk, gen, inp, stream):
                        bc_bf16=inp.bc_bf16, y_bf16=inp.y_bf16, y=y, stream=stream)
 
     t_dec = _event_time(dec, 200, 20, stream)
+
+    # The same step as a decoding window: 64 consecutive steps captured in
+    # one HIP graph (the state stays in place, every step's inputs at fixed
+    # addresses), so the window costs one launch instead of 64.
+    T_win = min(64, inp.L)
+    win = []
+    for t in range(T_win):
+        ws_ = (inp.sel_or_logits[:, :, t].contiguous() if inp.sel_mode.startswith("sel")
+               else inp.sel_or_logits[:, :, t, :].contiguous())
+        win.append((ws_, inp.diag[:, :, t].contiguous(), inp.b[:, :, t].contiguous(),
+                    inp.c[:, :, t].contiguous(), torch.empty_like(y)))
+    xw = x.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+
+    def window():
+        for (s_, d_, b_, c_, y_) in win:
+            pk.decode_step(s_, inp.dict_idx, d_, b_, c_, xw, sel_mode=inp.sel_mode, complex=inp.complex,
+                           bc_bf16=inp.bc_bf16, y_bf16=inp.y_bf16, y=y_)
+
+    with torch.cuda.stream(side):
+        window()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        window()
+    t_win = _event_time(lambda: graph.replay(), 50, 5, stream)
+    del graph, win, xw
+    # A window of known steps can also run as one scan call of L = 64 that
+    # starts from the carried state (x0) and hands its state on (x_final):
+    # the steps then overlap inside the kernel instead of following each
+    # other's memory latencies.
+    wl_inp = gen.make_inputs(workload, device=dev, L=T_win, with_x0=True)
+    wl_ws = pk.workspace_for(wl_inp)
+    wl_y = torch.empty((B, H, T_win), device=dev, dtype=torch.bfloat16 if inp.y_bf16 else torch.float32)
+    wl_xf = torch.empty_like(wl_inp.x0)
+    t_swin = _event_time(lambda: pk.scan(wl_inp, workspace=wl_ws, y=wl_y, x_final=wl_xf, stream=stream),
+                         50, 5, stream)
+    del wl_inp, wl_ws, wl_y, wl_xf
 
     # Router scores + argmax from the step inputs (D = 2048 features per
     # token), only the int16 selections written; the fused kernel takes up
@@ -206,7 +246,9 @@ def measure_aux(pk, gen, inp, stream):
     del ru, rw, rsel
     dec_bytes = sum(t.numel() * t.element_size() for t in (sel, d, b, c, y)) + 2 * x.numel() * 4
     print(f"[bench] dict hardmax {t_hm * 1e6:.1f} us ({hm_bytes / t_hm / 1e9:.0f} GB/s); decode step "
-          f"{t_dec * 1e6:.2f} us ({B * H / t_dec:.3g} tokens/s); router D={D} {t_rt * 1e6:.1f} us "
+          f"{t_dec * 1e6:.2f} us ({B * H / t_dec:.3g} tokens/s), in a {T_win}-step graph "
+          f"{t_win / T_win * 1e6:.2f} us per step, as one scan call {t_swin / T_win * 1e6:.2f} us per step; "
+          f"router D={D} {t_rt * 1e6:.1f} us "
           f"({rt_flops / t_rt / 1e12:.0f} TFLOP/s)", file=sys.stderr, flush=True)
     return {
         "dict_hardmax": {"us_per_call": t_hm * 1e6, "shape": f"H={H} K={K} N={N} fp32",
@@ -217,7 +259,15 @@ def measure_aux(pk, gen, inp, stream):
                         "shape": f"B={B} H={H} N={N} K={K}, one step per sequence",
                         "algorithmic_bytes_per_call": dec_bytes,
                         "note": "launch- and latency-bound: one step reads and writes "
-                                f"{dec_bytes} bytes"},
+                                f"{dec_bytes} bytes",
+                        "graph_window": {"steps": T_win, "us_per_step": t_win / T_win * 1e6,
+                                         "tokens_per_s": B * H * T_win / t_win,
+                                         "note": "the same step, a window of consecutive steps "
+                                                 "captured in one HIP graph and replayed"},
+                        "scan_window": {"steps": T_win, "us_per_step": t_swin / T_win * 1e6,
+                                        "tokens_per_s": B * H * T_win / t_swin,
+                                        "note": "the window as one pdssm_scan_fwd call from the carried "
+                                                "state (x0) to the handed-on state (x_final)"}},
         "router_select": {"us_per_call": t_rt * 1e6, "tokens_per_s": B * inp.L * H / t_rt,
                           "shape": f"B={B} L={inp.L} H={H} K={K} D={D}, bf16 inputs, fp32 sums",
                           "roofline": {"bound": "mfma", "achieved": rt_flops / t_rt / 1e12,
@@ -370,7 +420,7 @@ def main() -> int:
         det["bwd_us_per_call"] = bwd["us_per_call"]
         det["bwd_deterministic_us_per_call"] = bwd["deterministic_us_per_call"]
         det["bwd_cost"] = bwd["deterministic_us_per_call"] / bwd["us_per_call"] - 1.0
-    aux = None if args.no_backward else measure_aux(pk, gen, inp, stream)
+    aux = None if args.no_backward else measure_aux(pk, gen, inp, stream, args.workload)
     hbm = None if args.no_backward else measure_hbm_practical(alg_bytes, stream)
     if hbm:
         print(f"[bench] practical HBM: read {hbm['read_GBps']:.0f} GB/s, read+write "
