@@ -28,7 +28,10 @@ namespace {
 // a time so that several loads are in flight per wave.
 // ---------------------------------------------------------------------------
 constexpr int kHmWaves = 4;
-constexpr int kHmRows = 8;
+#ifndef PDSSM_HM_ROWS
+#define PDSSM_HM_ROWS 16
+#endif
+constexpr int kHmRows = PDSSM_HM_ROWS;
 
 template <bool BF16>
 __global__ void __launch_bounds__(kHmWaves * 64) hardmax_kernel(const void *__restrict__ m,
