@@ -547,6 +547,51 @@ __device__ __forceinline__ ScoreSlice<NV> select_issue(const void *__restrict__ 
     return s;
 }
 
+// Score i of a lane's slice (bf16 pairs or fp32 words, in index order).
+template <bool BF, int NV>
+__device__ __forceinline__ float slice_score(const ScoreSlice<NV> &s, int i)
+{
+    constexpr int PER = BF ? 8 : 4;
+    const uint4 &v = s.v[i / PER];
+    const int m = i % PER;
+    const uint32_t w = (BF ? m >> 1 : m) == 0 ? v.x : (BF ? m >> 1 : m) == 1 ? v.y : (BF ? m >> 1 : m) == 2 ? v.z : v.w;
+    if constexpr (BF)
+        return (m & 1) ? bf16_hi(w) : bf16_lo(w);
+    else
+        return __uint_as_float(w);
+}
+
+// Argmax of the first n scores of a lane's slice, scanned in index order.
+// Without NaN a strict comparison is the whole rule: among equal scores
+// (+0 and -0 included) the first one stays.  Returns the position in the
+// slice (0 for an empty one) and flags a slice whose scores may hold a NaN
+// (their sum is NaN), for which the caller takes the exact comparison.
+// MASKED: positions n and on are read as -inf.
+template <bool BF, bool MASKED, int NV>
+__device__ __forceinline__ int slice_argmax(const ScoreSlice<NV> &s, int n, float &bv, bool &nan)
+{
+    constexpr int CNT = (BF ? 8 : 4) * NV;
+    const float ninf = __int_as_float((int)0xFF800000u);
+    float acc = 0.f;
+    int bi = 0;
+#pragma unroll
+    for (int i = 0; i < CNT; ++i) {
+        float v = slice_score<BF, NV>(s, i);
+        if constexpr (MASKED)
+            v = (i < n) ? v : ninf;
+        acc += v;
+        if (i == 0) {
+            bv = v;
+        } else {
+            const bool t = v > bv;
+            bv = t ? v : bv;
+            bi = t ? i : bi;
+        }
+    }
+    nan = acc != acc;
+    return bi;
+}
+
 template <int SPW, int NV>
 __device__ __forceinline__ void select_finish(const ScoreSlice<NV> &s, uint32_t mode, int K, int64_t L,
                                               int64_t t_first, int16_t *out, int lane)
@@ -560,20 +605,43 @@ __device__ __forceinline__ void select_finish(const ScoreSlice<NV> &s, uint32_t 
     } else {
         int k0, k1;
         select_slice<SPW>(mode, K, lane, k0, k1);
-        float bv = __int_as_float(opaque((int)0xFF800000u));   // -inf, made here
-        int bk = K;
         const bool bf = (mode == PDSSM_LOGITS_BF16);
+        const int n = k1 - k0;
+        float bv = __int_as_float((int)0xFF800000u);
+        bool nan = true;
+        int bk = K;
+        // Slices of up to two vectors (one chunk per wave): one wave-uniform
+        // branch picks the unpacking and whether any lane's slice is short
+        // (its tail then reads as -inf).  Longer slices go the exact way.
+        if constexpr (NV <= 2) {
+            int bi;
+            if (bf)
+                bi = __all(n >= 8 * NV) ? slice_argmax<true, false, NV>(s, n, bv, nan)
+                                        : slice_argmax<true, true, NV>(s, n, bv, nan);
+            else
+                bi = __all(n >= 4 * NV) ? slice_argmax<false, false, NV>(s, n, bv, nan)
+                                        : slice_argmax<false, true, NV>(s, n, bv, nan);
+            bk = (n > 0) ? k0 + bi : K;   // an empty slice offers K, below every index
+        }
+        if (__any(nan)) {
+            // A NaN (or +inf and -inf) in the slice: the exact rule, NaN
+            // above every number and the first NaN winning.
+            if (nan) {
+                bv = __int_as_float((int)0xFF800000u);
+                bk = K;
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const uint32_t w[4] = {s.v[v].x, s.v[v].y, s.v[v].z, s.v[v].w};
+                for (int v = 0; v < NV; ++v) {
+                    const uint32_t w[4] = {s.v[v].x, s.v[v].y, s.v[v].z, s.v[v].w};
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int kk = bf ? k0 + v * 8 + m : k0 + v * 4 + (m & 3);
-                if (!bf && m >= 4)
-                    continue;
-                const float val = bf ? ((m & 1) ? bf16_hi(w[m >> 1]) : bf16_lo(w[m >> 1]))
-                                     : __uint_as_float(w[m]);
-                take_better(val, kk, kk < k1, bv, bk);
+                    for (int m = 0; m < 8; ++m) {
+                        const int kk = bf ? k0 + v * 8 + m : k0 + v * 4 + (m & 3);
+                        if (!bf && m >= 4)
+                            continue;
+                        const float val = bf ? ((m & 1) ? bf16_hi(w[m >> 1]) : bf16_lo(w[m >> 1]))
+                                             : __uint_as_float(w[m]);
+                        take_better(val, kk, kk < k1, bv, bk);
+                    }
+                }
             }
         }
 #pragma unroll

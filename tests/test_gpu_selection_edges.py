@@ -59,6 +59,10 @@ def per_seq_err(got: np.ndarray, ref: np.ndarray) -> float:
 CASES = [
     # N, K, mode, complex, bc_bf16, y_bf16, L
     (64, 64, gen.LOGITS_BF16, True, True, True, 700),      # cooperative, one chunk per wave
+    (64, 40, gen.LOGITS_BF16, True, True, True, 300),      # one chunk per wave, short and empty slices
+    (64, 8, gen.LOGITS_BF16, False, True, False, 300),     # one lane holds every score
+    (64, 32, gen.LOGITS_F32, False, False, False, 300),    # one chunk per wave, fp32 slices
+    (64, 20, gen.LOGITS_F32, True, False, False, 300),     # fp32, short and empty slices
     (16, 16, gen.LOGITS_F32, False, False, False, 900),    # cooperative, four chunks per wave
     (64, 200, gen.LOGITS_BF16, True, True, True, 500),     # per-slice selection
     (32, 3000, gen.LOGITS_F32, False, False, False, 300),  # per-slice, entry table beyond LDS
