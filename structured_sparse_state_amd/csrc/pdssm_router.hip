@@ -93,15 +93,20 @@ __device__ __forceinline__ int chunk_pos(int r, int c)
 // values have their magnitude bits flipped, -0 is made +0 first, every NaN
 // becomes INT32_MAX) in the high word, 255 - k in the low word.  The larger
 // key wins, so a max over keys is the argmax with ties to the lowest index.
-__device__ __forceinline__ int64_t score_key(float v, int k)
+__device__ __forceinline__ int32_t value_key(float v)
 {
     const float f = v + 0.0f;   // -0 + 0 = +0 (round to nearest); NaN stays NaN
     const int32_t i = __float_as_int(f);
-    int32_t key = i ^ ((i >> 31) & 0x7fffffff);
-    key = (f != f) ? 0x7fffffff : key;
-    return (int64_t)(((uint64_t)(uint32_t)key << 32) | (uint32_t)(255 - k));
+    const int32_t key = i ^ ((i >> 31) & 0x7fffffff);
+    return (f != f) ? 0x7fffffff : key;
 }
-constexpr int64_t kNoKey = INT64_MIN;   // a padding column: below every score
+// A padding column's value key: below the key of every score (-inf's is
+// INT32_MIN + 0x7fffff).
+constexpr int32_t kNoValue = INT32_MIN;
+__device__ __forceinline__ int64_t join_key(int32_t vkey, int k)
+{
+    return (int64_t)(((uint64_t)(uint32_t)vkey << 32) | (uint32_t)(255 - k));
+}
 __device__ __forceinline__ int64_t kmax(int64_t a, int64_t b) { return a > b ? a : b; }
 
 // The partner's 64-bit value across lane bit BIT (0..3) inside a row of 16
@@ -306,8 +311,10 @@ __global__ void __launch_bounds__(kRThreads, 1) router_kernel(RouterArgs a)
     // Argmax per token over the head's K scores.  acc[mi][ni][e] is the
     // score of token wm*128 + mi*32 + 8*(e/4) + 4*(lane/32) + e%4 and column
     // ni*32 + lane%32 of the wave, i.e. entry k = (ni % NI)*32 + lane%32 of
-    // head ni / NI.  Each lane first keeps the best key of its NI entries for
-    // each of its 64 tokens (c = mi*16 + e); then the 32 lanes of each
+    // head ni / NI.  Each lane first keeps the best of its NI entries for
+    // each of its 64 tokens (c = mi*16 + e), comparing value keys in index
+    // order with a strict comparison (the lower index stays on a tie), and
+    // joins the winner's index into a 64-bit key; then the 32 lanes of each
     // half-wave reduce by recursive halving: at the exchange across lane bit
     // b, a lane keeps the half of its tokens that its bit selects and takes
     // its partner's keys of that half, so after five exchanges lane l holds
@@ -315,23 +322,44 @@ __global__ void __launch_bounds__(kRThreads, 1) router_kernel(RouterArgs a)
     // across bit 4 is one v_permlane16_swap per register (odd and even rows
     // trade halves), the others DPP moves; the max over keys is associative
     // and commutative, so the pairing order does not matter.
+    // Padding columns (entry k >= K) exist only when K < P (one wave-uniform
+    // branch); their scores are then replaced by kNoValue.
+    const bool padded = K < P;
+    bool col_ok[NI];
+#pragma unroll
+    for (int t = 0; t < NI; ++t)
+        col_ok[t] = t * 32 + (lane & 31) < K;
 #pragma unroll
     for (int hn = 0; hn < HW; ++hn) {
         const int64_t h = h0 + wn * HW + hn;
         int64_t kv[64];
+        auto in_lane = [&](auto padc) {
+            constexpr bool PAD = decltype(padc)::value;
 #pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
+            for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                int64_t best = kNoKey;
+                for (int e = 0; e < 16; ++e) {
+                    int32_t best = value_key(acc[mi][hn * NI][e]);
+                    if constexpr (PAD)
+                        best = col_ok[0] ? best : kNoValue;
+                    int bt = 0;
 #pragma unroll
-                for (int t = 0; t < NI; ++t) {
-                    const int kt = t * 32 + (lane & 31);
-                    best = kmax(best, kt < K ? score_key(acc[mi][hn * NI + t][e], kt) : kNoKey);
+                    for (int t = 1; t < NI; ++t) {
+                        int32_t v = value_key(acc[mi][hn * NI + t][e]);
+                        if constexpr (PAD)
+                            v = col_ok[t] ? v : kNoValue;
+                        const bool take = v > best;
+                        best = take ? v : best;
+                        bt = take ? t : bt;
+                    }
+                    kv[mi * 16 + e] = join_key(best, bt * 32 + (lane & 31));
                 }
-                kv[mi * 16 + e] = best;
             }
-        }
+        };
+        if (padded)
+            in_lane(std::true_type{});
+        else
+            in_lane(std::false_type{});
         // bit 4: lanes l and l ^ 16 (odd and even rows)
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
