@@ -94,6 +94,39 @@ def test_router_exact_integers(orc, B, L, H, K, D):
     assert np.array_equal(got.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("B,L,H,K,D", [(1, 300, 3, 64, 64), (2, 129, 3, 40, 96), (1, 200, 2, 100, 128),
+                                       (1, 256, 2, 128, 64)])
+def test_router_special_scores(orc, B, L, H, K, D):
+    """Scores that are +-inf, NaN or all zero reach the argmax's rule (NaN
+    above every number and the first NaN winning, -0 equal to +0, the first
+    maximum on ties): small-integer inputs, with some tokens holding an inf
+    (inf * 0 gives NaN), a NaN, both infinities, or nothing but zeros.  Every
+    finite sum is exact and inf/NaN arithmetic does not depend on the order
+    of the sum, so the index must equal the oracle's everywhere."""
+    say(f"[case] router special scores B={B} L={L} H={H} K={K} D={D}")
+    u, w = gen.make_router_inputs(B, L, H, K, D, seed=11 + K + D, integers=True)
+    u = u.float()
+    g = torch.Generator().manual_seed(5 + K)
+    d0 = torch.randint(0, D, (B, L), generator=g)
+    d1 = (d0 + 1 + torch.randint(0, D - 1, (B, L), generator=g)) % D
+    kind = torch.arange(L).view(1, L).expand(B, L) % 7
+    rows = torch.arange(B).view(B, 1).expand(B, L)
+    cols = torch.arange(L).view(1, L).expand(B, L)
+    for k, val in ((1, float("inf")), (2, float("nan")), (4, float("-inf"))):
+        m = kind == k
+        u[rows[m], cols[m], d0[m]] = val
+    m = kind == 4
+    u[rows[m], cols[m], d1[m]] = float("inf")
+    u[kind == 3] = 0.0
+    u = u.to(torch.bfloat16)
+    ref = orc.router_select(u, w, nthreads=8)
+    got = pk.router_select(u.to(DEV), w.to(DEV))
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, f"{bad.shape[0]} choices differ, first at {tuple(bad[0])}"
+
+
 def test_router_lm_full_size_sampled(orc):
     """The LM-layer router at full size (B=8 L=4096 H=32 K=64, D=2048): sampled
     tokens against the oracle, including the first and last of several
