@@ -857,27 +857,56 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             for (int rr = 0; rr < GB::RF; ++rr)
                 s_q[wave * G * T + q.g * T + GB::step_of(rr, q.i)] = w[rr];
         }
-        // ---- a3: the prefix operators of the tile's chunks, chained in time
-        // order across the chunk waves: this wave waits for the prefix of the
-        // chunks before its own, composes its operator(s) onto it, and posts
-        // the inclusive prefix (slot wave * 64 + g * NP + i) for the next.
-        // Lanes of other groups run along and write nothing.  The chain is
-        // on the tile's critical path, so it runs at raised priority, and
-        // its hand-offs rely on the LDS executing each wave's operations in
-        // order: a prefix is written before its flag, and read after it.
+        // ---- a3: the prefix operators of the tile's chunks, in time order.
+        // A wave's G chunks first combine among themselves by an inclusive
+        // scan over its lane groups in log2(G) rounds (group g composes its
+        // value onto that of group g - s), which needs nothing from the
+        // other waves.  Then the wave waits for the prefix of the chunks
+        // before its own, composes it under all of its groups at once, and
+        // posts the inclusive prefixes (slot wave * 64 + g * NP + i) for the
+        // next wave: one composition per wave on the chain across the
+        // waves.  The chain is on the tile's critical path, so it runs at
+        // raised priority, and its hand-offs rely on the LDS executing each
+        // wave's operations in order: a prefix is written before its flag,
+        // and read after it.
+        //   (later o earlier): pi[j] = pi_l[pi_e[j]], d[j] = d_l[pi_e[j]] * d_e[j],
+        //                      e = scatter(pi_l, d_l * e_e) + e_l.
         {
-            const int opi = (pa4 >> 2) - q.gbase;
             const int pos = chunk_pos(wave);
             const int slot = wave * 64 + q.ln;
             cf *scr = &s_reg[wave][0][0];   // scatter scratch: a region the next local pass rewrites
             __builtin_amdgcn_s_setprio(PDSSM_CARRY_PRIO);
-            int ppi = 0;
-            cf pd = {1.f, 0.f}, pe = {0.f, 0.f};
-            int api = opi;   // this lane's posted prefix (its group's last)
+            int api = (pa4 >> 2) - q.gbase;   // this lane's prefix: first the chunk's own operator
             cf ad = dacc, ae = x;
+#pragma unroll
+            for (int s = 1; s < G; s <<= 1) {
+                // Group g - s's value, from the lane s groups down (lanes of
+                // groups g < s fetch another group's value and discard the
+                // result; every index stays inside the group).
+                const int from = (q.ln - s * NP) & 63;
+                const int epi = (int)bperm((uint32_t)api, from);
+                cf ed, ee;
+                ed.r = bperm(ad.r, from);
+                ed.i = CPLX ? bperm(ad.i, from) : 0.f;
+                ee.r = bperm(ae.r, from);
+                ee.i = CPLX ? bperm(ae.i, from) : 0.f;
+                const int src = (q.gbase + epi) * 4;
+                const int npi = (int)bperm_a((uint32_t)api, src);
+                cf gd;
+                gd.r = bperm_a(ad.r, src);
+                gd.i = CPLX ? bperm_a(ad.i, src) : 0.f;
+                const cf ne = scatter_add<CPLX>(scr, q.ln, q.gbase, api, cmul(ad, ee), ae);
+                if (q.g >= s) {
+                    api = npi;
+                    ad = cmul(gd, ed);
+                    ae = ne;
+                }
+            }
             if (pos > 0) {
                 const uint32_t need = 1u << wave_at(pos - 1);
                 const int ps = wave_at(pos - 1) * 64 + (G - 1) * NP + q.i;
+                int ppi;
+                cf pd, pe;
                 while (true) {
                     const uint32_t f = *reinterpret_cast<volatile uint32_t *>(&s_ready);
                     lds_order();
@@ -889,38 +918,19 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
                         break;
                     __builtin_amdgcn_s_sleep(1);
                 }
+                const int src = (q.gbase + ppi) * 4;
+                const int rpi = (int)bperm_a((uint32_t)api, src);
+                cf gd;
+                gd.r = bperm_a(ad.r, src);
+                gd.i = CPLX ? bperm_a(ad.i, src) : 0.f;
+                ae = scatter_add<CPLX>(scr, q.ln, q.gbase, api, cmul(ad, pe), ae);
+                api = rpi;
+                ad = cmul(gd, pd);
             }
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                int rpi = opi;
-                cf rd = dacc, re = x;
-                if (pos > 0 || g > 0) {
-                    // (op o prefix): pi[j] = opi[ppi[j]], d[j] = dacc[ppi[j]] * pd[j],
-                    // e = P D pe + x.
-                    if (g > 0) {
-                        const int ps = wave * 64 + (g - 1) * NP + q.i;
-                        ppi = s_pi[ps];
-                        pd = s_d(ps);
-                        pe = s_e[ps];
-                    }
-                    const int src = (q.gbase + ppi) * 4;
-                    rpi = (int)bperm_a((uint32_t)opi, src);
-                    cf gd;
-                    gd.r = bperm_a(dacc.r, src);
-                    gd.i = CPLX ? bperm_a(dacc.i, src) : 0.f;
-                    re = scatter_add<CPLX>(scr, q.ln, q.gbase, opi, cmul(dacc, pe), x);
-                    rd = cmul(gd, pd);
-                }
-                if (q.g == g) {
-                    s_pi[slot] = rpi;
-                    s_d(slot) = rd;
-                    s_e[slot] = re;
-                    api = rpi;
-                    ad = rd;
-                    ae = re;
-                }
-                lds_order();
-            }
+            s_pi[slot] = api;
+            s_d(slot) = ad;
+            s_e[slot] = ae;
+            lds_order();
             if (q.ln == 0)
                 __hip_atomic_fetch_or(&s_ready, 1u << wave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             __builtin_amdgcn_s_setprio(0);
