@@ -554,7 +554,8 @@ __device__ __forceinline__ float slice_score(const ScoreSlice<NV> &s, int i)
     constexpr int PER = BF ? 8 : 4;
     const uint4 &v = s.v[i / PER];
     const int m = i % PER;
-    const uint32_t w = (BF ? m >> 1 : m) == 0 ? v.x : (BF ? m >> 1 : m) == 1 ? v.y : (BF ? m >> 1 : m) == 2 ? v.z : v.w;
+    const int wi = BF ? m >> 1 : m;   // the 32-bit word of the vector
+    const uint32_t w = wi == 0 ? v.x : wi == 1 ? v.y : wi == 2 ? v.z : v.w;
     if constexpr (BF)
         return (m & 1) ? bf16_hi(w) : bf16_lo(w);
     else
