@@ -88,11 +88,12 @@ __device__ __forceinline__ int chunk_pos(int r, int c)
 }
 
 // The selection's order (the score, then the lower index; -0 equal to +0; a
-// NaN above every number, the first NaN winning) as one signed 64-bit key:
-// the score's bits mapped to an int32 that orders like the value (negative
-// values have their magnitude bits flipped, -0 is made +0 first, every NaN
-// becomes INT32_MAX) in the high word, 255 - k in the low word.  The larger
-// key wins, so a max over keys is the argmax with ties to the lowest index.
+// NaN above every number, the first NaN winning) in integers.  value_key maps
+// the score's bits to an int32 that orders like the value (negative values
+// have their magnitude bits flipped, -0 is made +0 first, every NaN becomes
+// INT32_MAX); join_key puts it in the high word of a signed 64-bit key and
+// 255 - k in the low word.  The larger key wins, so a max over joined keys
+// is the argmax with ties to the lowest index.
 __device__ __forceinline__ int32_t value_key(float v)
 {
     const float f = v + 0.0f;   // -0 + 0 = +0 (round to nearest); NaN stays NaN
