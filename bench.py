@@ -232,24 +232,30 @@ def measure_aux(pk, gen, inp, stream, workload):
             "router_select": None,
         }
     ru, rw = gen.make_router_inputs(B, inp.L, H, K, D, seed=4, device=dev)
-    rsel = pk.router_select(ru, rw, stream=stream)
+    rwp = pk.router_pack_weights(rw, stream=stream)
+    rsel = pk.router_select(ru, rwp, stream=stream)
     # The matrix cores reach their sustained clock only after a while of
     # load: warm up for about a second before timing.
     t_end = time.perf_counter() + 1.0
     while time.perf_counter() < t_end:
         for _ in range(10):
-            pk.router_select(ru, rw, out=rsel, stream=stream)
+            pk.router_select(ru, rwp, out=rsel, stream=stream)
         torch.cuda.synchronize()
-    t_rt = _event_time(lambda: pk.router_select(ru, rw, out=rsel, stream=stream), 50, 3, stream)
+    # Packed weights (the layout of router_pack_weights, packed once per
+    # weight update) and the [H,K,D] layout as given; the packing itself.
+    t_rt = _event_time(lambda: pk.router_select(ru, rwp, out=rsel, stream=stream), 50, 3, stream)
+    t_rt_plain = _event_time(lambda: pk.router_select(ru, rw, out=rsel, stream=stream), 50, 3, stream)
+    t_pack = _event_time(lambda: pk.router_pack_weights(rw, stream=stream), 20, 3, stream)
     rt_flops = 2.0 * B * inp.L * H * K * D
     rt_pad_flops = 2.0 * B * inp.L * H * (64 if K <= 64 else 128) * D
-    del ru, rw, rsel
+    del ru, rw, rwp, rsel
     dec_bytes = sum(t.numel() * t.element_size() for t in (sel, d, b, c, y)) + 2 * x.numel() * 4
     print(f"[bench] dict hardmax {t_hm * 1e6:.1f} us ({hm_bytes / t_hm / 1e9:.0f} GB/s); decode step "
           f"{t_dec * 1e6:.2f} us ({B * H / t_dec:.3g} tokens/s), in a {T_win}-step graph "
           f"{t_win / T_win * 1e6:.2f} us per step, as one scan call {t_swin / T_win * 1e6:.2f} us per step; "
-          f"router D={D} {t_rt * 1e6:.1f} us "
-          f"({rt_flops / t_rt / 1e12:.0f} TFLOP/s)", file=sys.stderr, flush=True)
+          f"router D={D} {t_rt * 1e6:.1f} us ({rt_flops / t_rt / 1e12:.0f} TFLOP/s), "
+          f"weights as [H,K,D] {t_rt_plain * 1e6:.1f} us, packing {t_pack * 1e6:.1f} us",
+          file=sys.stderr, flush=True)
     return {
         "dict_hardmax": {"us_per_call": t_hm * 1e6, "shape": f"H={H} K={K} N={N} fp32",
                          "algorithmic_bytes_per_call": hm_bytes,
@@ -270,6 +276,9 @@ def measure_aux(pk, gen, inp, stream, workload):
                                                 "state (x0) to the handed-on state (x_final)"}},
         "router_select": {"us_per_call": t_rt * 1e6, "tokens_per_s": B * inp.L * H / t_rt,
                           "shape": f"B={B} L={inp.L} H={H} K={K} D={D}, bf16 inputs, fp32 sums",
+                          "weights": "packed (pdssm_router_pack_weights, once per weight update)",
+                          "us_per_call_weights_hkd": t_rt_plain * 1e6,
+                          "us_per_pack": t_pack * 1e6,
                           "roofline": {"bound": "mfma", "achieved": rt_flops / t_rt / 1e12,
                                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                        "frac": rt_flops / t_rt / 1e12 / MFMA_BF16_PEAK_TFLOPS,

@@ -102,6 +102,10 @@ extern "C" {
 #define PDSSM_DETERMINISTIC 0x20u
 #define PDSSM_FLAGS_ALL 0x3Fu
 
+/* pdssm_router_select only: w is in the packed layout that
+ * pdssm_router_pack_weights writes. */
+#define PDSSM_ROUTER_W_PACKED 0x1u
+
 /* status codes */
 #define PDSSM_OK 0
 #define PDSSM_ERR_NULL -1      /* a required pointer is NULL */
@@ -272,18 +276,38 @@ int pdssm_decode_step(const void *sel_or_logits, const int32_t *dict_idx, const 
  *     sel_out[b,h,t]  = argmax_k scores[b,h,t,k]       (first maximum wins)
  * The result feeds pdssm_scan_fwd with PDSSM_SEL_I16.
  *   u        bf16 [B,L,D] step inputs
- *   w        bf16 [H,K,D] router weights
+ *   w        bf16 router weights: [H,K,D] (flags 0), or, with
+ *            PDSSM_ROUTER_W_PACKED, the packed layout [H][D/8][P][8] of
+ *            pdssm_router_pack_weights (P = 64 for K <= 64, else 128), which
+ *            the faster of the two kernels reads
  *   sel_out  int16 [B,H,L] output
- *   K in [1,128]; D a positive multiple of 32; flags must be 0.  B, L or H
- *   may be 0: nothing is read or written then.
+ *   K in [1,128]; D a positive multiple of 32; flags 0 or
+ *   PDSSM_ROUTER_W_PACKED (then H*P*D*2 bytes must stay below 4 GB).  B, L
+ *   or H may be 0: nothing is read or written then.
  * The scores are fp32 sums in an unspecified order: where two scores are
- * within their rounding error of each other, either index may be returned.
+ * within their rounding error of each other, either index may be returned
+ * (the two layouts may differ there).
  * All pointers are device pointers, 16-byte aligned.  Errors:
  * PDSSM_ERR_NULL, PDSSM_ERR_DIM, PDSSM_ERR_FLAGS, PDSSM_ERR_ALIGN,
  * PDSSM_ERR_HIP.  Asynchronous on stream; allocates nothing.
  */
 int pdssm_router_select(const void *u, const void *w, int16_t *sel_out, int64_t B, int64_t L,
                         int64_t H, int32_t K, int32_t D, uint32_t flags, hipStream_t stream);
+
+/*
+ * The router weights in the packed layout of pdssm_router_select with
+ * PDSSM_ROUTER_W_PACKED: w_packed[h][d/8][k][d%8] = w[h][k][d] for k < K and
+ * 0 for K <= k < P (P = 64 for K <= 64, else 128), so the 32 score columns
+ * of an 8-feature block are 512 contiguous bytes.  It depends on the
+ * weights only: pack once per weight update.
+ *   w         bf16 [H,K,D]
+ *   w_packed  bf16 [H, D/8, P, 8] output (H*P*D*2 bytes, below 4 GB)
+ *   K in [1,128]; D a positive multiple of 32; H = 0 writes nothing.
+ * Device pointers, 16-byte aligned.  Errors: PDSSM_ERR_NULL, PDSSM_ERR_DIM,
+ * PDSSM_ERR_ALIGN, PDSSM_ERR_HIP.  Asynchronous on stream; allocates nothing.
+ */
+int pdssm_router_pack_weights(const void *w, void *w_packed, int64_t H, int32_t K, int32_t D,
+                              hipStream_t stream);
 
 /*
  * The selection step alone: sel_out[b,h,t] = the dictionary entry step t

@@ -9,7 +9,8 @@ library raises.
 
 Higher-level helpers allocate outputs (and workspaces) with torch and call
 the C entry points: ``scan`` and ``scan_save`` (forward), ``scan_bwd``
-(gradients), ``router_select`` (router scores and their argmax),
+(gradients), ``router_select`` (router scores and their argmax) with
+``router_pack_weights`` (the weights in the faster kernel's layout),
 ``dict_hardmax`` (index maps from dense matrices), ``decode_step`` (one
 recurrent step), ``select`` and ``compose`` (test exports).
 """
@@ -19,7 +20,7 @@ import contextlib
 import ctypes
 import os
 import re
-from typing import Optional
+from typing import NamedTuple, Optional
 
 import torch
 
@@ -38,6 +39,7 @@ PDSSM_BC_BF16 = 0x8
 PDSSM_Y_BF16 = 0x10
 PDSSM_DETERMINISTIC = 0x20
 PDSSM_FLAGS_ALL = 0x3F
+PDSSM_ROUTER_W_PACKED = 0x1
 
 PDSSM_OK = 0
 PDSSM_ERR_NULL = -1
@@ -93,6 +95,8 @@ def _load(path: str) -> ctypes.CDLL:
     lib.pdssm_decode_step.restype = ctypes.c_int
     lib.pdssm_router_select.argtypes = [P, P, P, I64, I64, I64, I32, I32, U32, P]
     lib.pdssm_router_select.restype = ctypes.c_int
+    lib.pdssm_router_pack_weights.argtypes = [P, P, I64, I32, I32, P]
+    lib.pdssm_router_pack_weights.restype = ctypes.c_int
     return lib
 
 
@@ -214,6 +218,10 @@ def pdssm_decode_step(sel_or_logits, dict_idx, diag, b, c, y, x, B, H, N, K, fla
 def pdssm_router_select(u, w, sel_out, B, L, H, K, D, flags, stream=None) -> int:
     return library().pdssm_router_select(_ptr(u), _ptr(w), _ptr(sel_out), B, L, H, K, D, flags,
                                          _stream(stream))
+
+
+def pdssm_router_pack_weights(w, w_packed, H, K, D, stream=None) -> int:
+    return library().pdssm_router_pack_weights(_ptr(w), _ptr(w_packed), H, K, D, _stream(stream))
 
 
 def pdssm_strerror(status: int) -> str:
@@ -402,16 +410,41 @@ def decode_step(sel_or_logits, dict_idx, diag, b, c, x, *, sel_mode: str, comple
     return y
 
 
-def router_select(u: torch.Tensor, w: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+class PackedRouterWeights(NamedTuple):
+    """Router weights in the packed layout (bf16 [H, D/8, P, 8]) with the
+    dictionary size K they were packed for."""
+    data: torch.Tensor
+    K: int
+
+
+def router_pack_weights(w: torch.Tensor, *, stream=None) -> PackedRouterWeights:
+    """The packed layout of router weights w [H,K,D] bf16 (pack once per
+    weight update; router_select then runs its faster kernel)."""
+    H, K, D = w.shape
+    if w.dtype != torch.bfloat16:
+        raise ValueError("w [H,K,D] must be bf16")
+    P = 64 if K <= 64 else 128
+    out = torch.empty((H, D // 8, P, 8), dtype=torch.bfloat16, device=w.device)
+    check(pdssm_router_pack_weights(w, out, H, K, D, stream))
+    return PackedRouterWeights(out, K)
+
+
+def router_select(u: torch.Tensor, w, *, out: Optional[torch.Tensor] = None,
                   stream=None) -> torch.Tensor:
     """sel int16 [B,H,L] from bf16 step inputs u [B,L,D] and router weights
-    w [H,K,D]: the argmax of each head's K scores, computed on the matrix
-    cores without writing the scores."""
+    w (bf16 [H,K,D], or PackedRouterWeights from router_pack_weights): the
+    argmax of each head's K scores, computed on the matrix cores without
+    writing the scores."""
     B, L, D = u.shape
-    H, K, D2 = w.shape
-    if D != D2 or u.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
-        raise ValueError("u [B,L,D] and w [H,K,D] must be bf16 with the same D")
+    if isinstance(w, PackedRouterWeights):
+        H, D8, P, _ = w.data.shape
+        K, D2, wt, flags = w.K, D8 * 8, w.data, PDSSM_ROUTER_W_PACKED
+    else:
+        H, K, D2 = w.shape
+        wt, flags = w, 0
+    if D != D2 or u.dtype != torch.bfloat16 or wt.dtype != torch.bfloat16:
+        raise ValueError("u [B,L,D] and the weights must be bf16 with the same D")
     if out is None:
         out = torch.empty((B, H, L), dtype=torch.int16, device=u.device)
-    check(pdssm_router_select(u, w, out, B, L, H, K, D, 0, stream))
+    check(pdssm_router_select(u, wt, out, B, L, H, K, D, flags, stream))
     return out

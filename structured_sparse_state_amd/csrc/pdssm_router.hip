@@ -13,13 +13,23 @@
 // fp32 accumulation.  A workgroup computes a 256-token x 256-column tile
 // (256/P heads); each of its four waves owns 128 tokens x 128 columns
 // (4 x 4 MFMA tiles, 256 accumulators, one wave per SIMD), so every head's
-// scores stay inside one wave and each fragment read from LDS feeds four
-// MFMAs.  U and W tiles of 32 features go straight from global memory into
-// a ring of LDS stages (global_load_lds, 16 bytes per lane, chunks swizzled
-// within each row so fragment reads do not conflict).  With one wave per
-// SIMD nothing else hides latency, so the loop is software-pipelined: the
-// fragments of the next 16 features are read while the MFMAs of the current
-// ones run, and every stage's loads are issued a whole ring ahead.
+// scores stay inside one wave and each fragment feeds four MFMAs.  With one
+// wave per SIMD nothing else hides latency, so the loops are
+// software-pipelined: the fragments of the next 16 features are read while
+// the MFMAs of the current ones run.
+//
+// Two kernels, by the layout of the weights:
+//   * [H][K][D] (router_lds_kernel): token rows and weight rows both go
+//     straight from global memory into a ring of LDS stages
+//     (global_load_lds, 16 bytes per lane, whole 128-byte lines per load).
+//     Per 16 features a CU then writes 16 KB and reads 32 KB of LDS, more
+//     than the LDS delivers in the MFMAs' time, which bounds this kernel.
+//   * packed, [H][D/8][P][8] (router_wreg_kernel; pdssm_router_pack_weights
+//     writes it): token rows go through LDS as above, the weight fragments
+//     straight into a ring of registers.  In this layout the 32 columns of a
+//     fragment are 512 contiguous bytes per 8 features, so a fragment load
+//     touches whole lines (in [H][K][D] it would touch 32 rows), and the LDS
+//     carries 8 KB of writes and 16 KB of reads per 16 features.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -40,11 +50,12 @@ constexpr int kRN = 256;     // score columns per workgroup tile
 constexpr int kRThreads = 256;
 constexpr int kRingBytes = 128 * 1024;   // LDS ring of every stage depth
 
-// The LDS stage of BK features: 64 (two stages in the ring) when the feature
+// router_lds_kernel's LDS stage of BK features of token and weight rows: 64
+// (two stages in the ring) when the feature
 // count allows it, else 32 (four stages).  Deeper stages mean fewer stage
 // hand-overs (barriers) per MFMA.
 template <int BK>
-struct StageGeom {
+struct PairStage {
     static constexpr int kRK = BK;                      // features per LDS stage
     static constexpr int kRowBytes = BK * 2;            // bytes of one row of a stage
     static constexpr int kChunks = BK / 8;              // 16-byte chunks per row
@@ -62,9 +73,26 @@ struct StageGeom {
     static_assert(kLoadsPerStage * 3 < 64, "vmcnt range");
 };
 
+// router_wreg_kernel's LDS stage of BK features of the token rows: 64 when
+// the feature count allows it, else 32.  The weight rows do not pass through
+// LDS (each wave loads its own fragments into registers), so the ring holds
+// token rows only: four 64-feature stages or eight 32-feature ones.
+template <int BK>
+struct TokenStage {
+    static constexpr int kRK = BK;                      // features per LDS stage
+    static constexpr int kRowBytes = BK * 2;            // bytes of one row of a stage
+    static constexpr int kChunks = BK / 8;              // 16-byte chunks per row
+    static constexpr int kRowsPerLoad = 64 / kChunks;   // rows one 64-lane 16-byte load fills
+    static constexpr int kStageBytes = kRM * kRowBytes;   // token rows per stage
+    static constexpr int kRStages = kRingBytes / kStageBytes;
+    static constexpr int kALoads = kRM / kRowsPerLoad / 4;   // direct-to-LDS loads per wave per stage
+    static_assert(BK == 32 || BK == 64, "stage depth");
+    static_assert(kRStages >= 3, "the hand-over wait assumes at least three stages in the ring");
+};
+
 struct RouterArgs {
     const uint16_t *u;   // [M][D] bf16
-    const uint16_t *w;   // [H][K][D] bf16
+    const uint16_t *w;   // [H][K][D] bf16, or packed [H][D/8][P][8] (P = 64 or 128)
     int16_t *sel;        // [B][H][L]
     int64_t M, L, H;
     int K, D;
@@ -132,18 +160,121 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// P: padded score columns per head (64 or 128); a wave's 128 columns hold
-// 128 / P heads.
-template <int P, int BK>
-__global__ void __launch_bounds__(kRThreads, 1) router_kernel(RouterArgs a)
+// The selection of every token of a wave's 128 x 128 score tile, stored to
+// sel.  acc[mi][ni][e] is the score of token wm*128 + mi*32 + 8*(e/4) +
+// 4*(lane/32) + e%4 and column ni*32 + lane%32 of the wave, i.e. entry k =
+// (ni % NI)*32 + lane%32 of head ni / NI (NI = P / 32).
+template <int P>
+__device__ __forceinline__ void select_store(const f32x16 (&acc)[4][4], const RouterArgs &a, int64_t m0,
+                                             int64_t h0, int wm, int wn, int lane)
 {
-    using SG = StageGeom<BK>;
+    constexpr int HW = 128 / P;   // heads per wave
+    constexpr int NI = P / 32;    // 32-column MFMA tiles per head
+    const int K = a.K;
+    // Argmax per token over the head's K scores.  Each lane first keeps the
+    // best of its NI entries for
+    // each of its 64 tokens (c = mi*16 + e), comparing value keys in index
+    // order with a strict comparison (the lower index stays on a tie), and
+    // joins the winner's index into a 64-bit key; then the 32 lanes of each
+    // half-wave reduce by recursive halving: at the exchange across lane bit
+    // b, a lane keeps the half of its tokens that its bit selects and takes
+    // its partner's keys of that half, so after five exchanges lane l holds
+    // the result of tokens c = 2 (l % 32) and 2 (l % 32) + 1.  The exchange
+    // across bit 4 is one v_permlane16_swap per register (odd and even rows
+    // trade halves), the others DPP moves; the max over keys is associative
+    // and commutative, so the pairing order does not matter.
+    // Padding columns (entry k >= K) exist only when K < P (one wave-uniform
+    // branch); their scores are then replaced by kNoValue.
+    const bool padded = K < P;
+    bool col_ok[NI];
+#pragma unroll
+    for (int t = 0; t < NI; ++t)
+        col_ok[t] = t * 32 + (lane & 31) < K;
+#pragma unroll
+    for (int hn = 0; hn < HW; ++hn) {
+        const int64_t h = h0 + wn * HW + hn;
+        int64_t kv[64];
+        auto in_lane = [&](auto padc) {
+            constexpr bool PAD = decltype(padc)::value;
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    int32_t best = value_key(acc[mi][hn * NI][e]);
+                    if constexpr (PAD)
+                        best = col_ok[0] ? best : kNoValue;
+                    int bt = 0;
+#pragma unroll
+                    for (int t = 1; t < NI; ++t) {
+                        int32_t v = value_key(acc[mi][hn * NI + t][e]);
+                        if constexpr (PAD)
+                            v = col_ok[t] ? v : kNoValue;
+                        const bool take = v > best;
+                        best = take ? v : best;
+                        bt = take ? t : bt;
+                    }
+                    kv[mi * 16 + e] = join_key(best, bt * 32 + (lane & 31));
+                }
+            }
+        };
+        if (padded)
+            in_lane(std::true_type{});
+        else
+            in_lane(std::false_type{});
+        // bit 4: lanes l and l ^ 16 (odd and even rows)
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            uint32_t alo = (uint32_t)kv[i], ahi = (uint32_t)((uint64_t)kv[i] >> 32);
+            uint32_t blo = (uint32_t)kv[32 + i], bhi = (uint32_t)((uint64_t)kv[32 + i] >> 32);
+            // after the swap, lanes with bit 4 clear hold token i of both
+            // lanes, lanes with bit 4 set token 32 + i of both
+            const auto rl = __builtin_amdgcn_permlane16_swap(alo, blo, false, false);
+            const auto rh = __builtin_amdgcn_permlane16_swap(ahi, bhi, false, false);
+            const int64_t x = (int64_t)(((uint64_t)rh[0] << 32) | rl[0]);
+            const int64_t y = (int64_t)(((uint64_t)rh[1] << 32) | rl[1]);
+            kv[i] = kmax(x, y);
+        }
+        auto level = [&](auto bitc, int n) {
+            constexpr int BIT = decltype(bitc)::value;
+            const bool up = (lane >> BIT) & 1;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (i < n) {
+                    const int64_t send = up ? kv[i] : kv[n + i];
+                    const int64_t keep = up ? kv[n + i] : kv[i];
+                    kv[i] = kmax(keep, key_across<BIT>(send));
+                }
+            }
+        };
+        level(std::integral_constant<int, 3>{}, 16);
+        level(std::integral_constant<int, 2>{}, 8);
+        level(std::integral_constant<int, 1>{}, 4);
+        level(std::integral_constant<int, 0>{}, 2);
+        if (h < a.H) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int c = 2 * (lane & 31) + r, mi = c >> 4, e = c & 15;
+                const int64_t m = m0 + wm * 128 + mi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (m < a.M) {
+                    const int64_t b = m / a.L, t = m - b * a.L;
+                    a.sel[(b * a.H + h) * a.L + t] = (int16_t)(255 - (int)(uint32_t)kv[r]);
+                }
+            }
+        }
+    }
+}
+
+
+// Weights [H][K][D].  P: padded score columns per head (64 or 128); a
+// wave's 128 columns hold 128 / P heads.
+template <int P, int BK>
+__global__ void __launch_bounds__(kRThreads, 1) router_lds_kernel(RouterArgs a)
+{
+    using SG = PairStage<BK>;
     constexpr int kRK = SG::kRK, kRowBytes = SG::kRowBytes, kChunks = SG::kChunks,
                   kRowsPerLoad = SG::kRowsPerLoad, kABytes = SG::kABytes, kStageBytes = SG::kStageBytes,
                   kRStages = SG::kRStages, kALoads = SG::kALoads, kBLoads = SG::kBLoads,
                   kLoadsPerStage = SG::kLoadsPerStage;
-    constexpr int HW = 128 / P;   // heads per wave
-    constexpr int NI = P / 32;    // 32-column MFMA tiles per head
     __shared__ __attribute__((aligned(1024))) char smem[kRingBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -236,6 +367,16 @@ __global__ void __launch_bounds__(kRThreads, 1) router_kernel(RouterArgs a)
             for (int ni = 0; ni < 4; ++ni)
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][mi], bf[buf][ni], acc[mi][ni], 0, 0, 0);
     };
+    // One MFMA, then one LDS read, eight times, then the other eight MFMAs.
+    auto interleave_reads = []() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
     // The own loads of stage s have landed once at most `ahead` younger
     // stages' loads are still in flight.
     auto wait_stage = [&](int ahead) {
@@ -288,14 +429,23 @@ __global__ void __launch_bounds__(kRThreads, 1) router_kernel(RouterArgs a)
                     issue(ring + (s % kRStages) * kStageBytes, (s + kRStages) * kRK);
                 read_frags(buf ^ 1, ring + ((s + 1) % kRStages) * kStageBytes, 0);
             }
-            // Keep the next fragments' reads (and the stage hand-over) ahead
-            // of this step's MFMAs, so their latency runs under the MFMAs
-            // still queued from the step before.
-            __builtin_amdgcn_sched_barrier(0);
-            mfmas(buf);
-            // and keep the hand-over's wait for this wave's reads after the
-            // MFMAs that run while those reads land
-            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (P == 64) {
+                // The next fragments' reads go out between this step's
+                // MFMAs (clustered, they would leave the matrix core idle
+                // while they issue).  With 128 columns per head the
+                // epilogue's registers do not leave room for it.
+                mfmas(buf);
+                interleave_reads();
+            } else {
+                // Keep the next fragments' reads (and the stage hand-over)
+                // ahead of this step's MFMAs, so their latency runs under
+                // the MFMAs still queued from the step before.
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas(buf);
+                // and keep the hand-over's wait for this wave's reads after
+                // the MFMAs that run while those reads land
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     }
     {
@@ -304,103 +454,251 @@ __global__ void __launch_bounds__(kRThreads, 1) router_kernel(RouterArgs a)
         for (int ks = 0; ks < KS; ++ks) {
             if (ks + 1 < KS)
                 read_frags((ks & 1) ^ 1, cur, ks + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            mfmas(ks & 1);
+            if constexpr (P == 64) {
+                mfmas(ks & 1);
+                interleave_reads();
+            } else {
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas(ks & 1);
+            }
         }
     }
+    select_store<P>(acc, a, m0, h0, wm, wn, lane);
+}
 
-    // Argmax per token over the head's K scores.  acc[mi][ni][e] is the
-    // score of token wm*128 + mi*32 + 8*(e/4) + 4*(lane/32) + e%4 and column
-    // ni*32 + lane%32 of the wave, i.e. entry k = (ni % NI)*32 + lane%32 of
-    // head ni / NI.  Each lane first keeps the best of its NI entries for
-    // each of its 64 tokens (c = mi*16 + e), comparing value keys in index
-    // order with a strict comparison (the lower index stays on a tie), and
-    // joins the winner's index into a 64-bit key; then the 32 lanes of each
-    // half-wave reduce by recursive halving: at the exchange across lane bit
-    // b, a lane keeps the half of its tokens that its bit selects and takes
-    // its partner's keys of that half, so after five exchanges lane l holds
-    // the result of tokens c = 2 (l % 32) and 2 (l % 32) + 1.  The exchange
-    // across bit 4 is one v_permlane16_swap per register (odd and even rows
-    // trade halves), the others DPP moves; the max over keys is associative
-    // and commutative, so the pairing order does not matter.
-    // Padding columns (entry k >= K) exist only when K < P (one wave-uniform
-    // branch); their scores are then replaced by kNoValue.
-    const bool padded = K < P;
-    bool col_ok[NI];
+// Packed weights [H][D/8][P][8].  P: score columns per head (64 or 128); a
+// wave's 128 columns hold 128 / P heads.
+template <int P, int BK>
+__global__ void __launch_bounds__(kRThreads, 1) router_wreg_kernel(RouterArgs a)
+{
+    using SG = TokenStage<BK>;
+    constexpr int kRK = SG::kRK, kRowBytes = SG::kRowBytes, kChunks = SG::kChunks,
+                  kRowsPerLoad = SG::kRowsPerLoad, kStageBytes = SG::kStageBytes, kRStages = SG::kRStages,
+                  kALoads = SG::kALoads;
+    __shared__ __attribute__((aligned(1024))) char smem[kRingBytes];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // Tile of this workgroup.  Consecutive workgroups go to different XCDs;
+    // the mapping gives each XCD a contiguous run of tiles, so the column
+    // tiles of one token tile (which read the same U rows) share that XCD's
+    // L2.
+    const uint32_t total = a.m_tiles * a.n_tiles, per = total / 8;
+    const uint32_t bx = blockIdx.x;
+    const uint32_t tile = (bx < per * 8) ? (bx % 8) * per + bx / 8 : bx;
+    const uint32_t mt = tile / a.n_tiles, nt = tile % a.n_tiles;
+    const int64_t m0 = (int64_t)mt * kRM;
+    const int64_t h0 = (int64_t)nt * (kRN / P);
+    const int D = a.D;
+
+    // Token rows go straight from global memory into LDS (global_load_lds):
+    // load j of this wave fills the kRowsPerLoad rows from R g on (g = wave
+    // * loads + j, R = kRowsPerLoad), lane i writing the 16-byte slot i, i.e.
+    // row R g + i / kChunks at position i % kChunks, which holds the chunk
+    // chunk_pos(row, i % kChunks) (the swizzle is its own inverse).  Rows
+    // past the token count read row 0 instead: their results are never used.
+    const uint16_t *asrc[kALoads];
 #pragma unroll
-    for (int t = 0; t < NI; ++t)
-        col_ok[t] = t * 32 + (lane & 31) < K;
+    for (int j = 0; j < kALoads; ++j) {
+        const int r = kRowsPerLoad * (wave * kALoads + j) + lane / kChunks;
+        const int64_t m = m0 + r;
+        asrc[j] = a.u + (m < a.M ? m : 0) * (int64_t)D + chunk_pos<kChunks>(r, lane % kChunks) * 8;
+    }
+    // The loads are written in asm so that the compiler does not see them
+    // as stores to LDS: it would otherwise make every fragment read wait
+    // for all of them (it cannot tell the stages apart).  They write no
+    // registers; the stage waits below are explicit.  M0 carries the LDS
+    // address as an input operand.
+    auto dma = [](const uint16_t *src, uint32_t lds) {
+        asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(lds) : "memory");
+    };
+    // Stage s of the token rows into ring slot s % kRStages.  Stages past
+    // the last one reload the last one into a slot nobody reads any more, so
+    // every hand-over sees the same count of loads in flight.
+    const int stages = D / kRK;
+    auto issue_a = [&](int s) {
+        char *buf = smem + (s % kRStages) * kStageBytes;
+        const int k0 = min(s, stages - 1) * kRK;
+        const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(buf));
 #pragma unroll
-    for (int hn = 0; hn < HW; ++hn) {
-        const int64_t h = h0 + wn * HW + hn;
-        int64_t kv[64];
-        auto in_lane = [&](auto padc) {
-            constexpr bool PAD = decltype(padc)::value;
+        for (int j = 0; j < kALoads; ++j)
+            dma(asrc[j] + k0, base + (uint32_t)((wave * kALoads + j) * 1024));
+    };
+
+    // This wave: tokens wm*128 .. +128 of the tile, columns wn*128 .. +128.
+    const int wm = wave >> 1, wn = wave & 1;
+    f32x16 acc[4][4];
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    int32_t best = value_key(acc[mi][hn * NI][e]);
-                    if constexpr (PAD)
-                        best = col_ok[0] ? best : kNoValue;
-                    int bt = 0;
+        for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-                    for (int t = 1; t < NI; ++t) {
-                        int32_t v = value_key(acc[mi][hn * NI + t][e]);
-                        if constexpr (PAD)
-                            v = col_ok[t] ? v : kNoValue;
-                        const bool take = v > best;
-                        best = take ? v : best;
-                        bt = take ? t : bt;
-                    }
-                    kv[mi * 16 + e] = join_key(best, bt * 32 + (lane & 31));
-                }
-            }
-        };
-        if (padded)
-            in_lane(std::true_type{});
-        else
-            in_lane(std::false_type{});
-        // bit 4: lanes l and l ^ 16 (odd and even rows)
+            for (int e = 0; e < 16; ++e)
+                acc[mi][ni][e] = 0.f;
+
+    // Fragments of 16-feature step g: row (lane % 32) of a 32-row block,
+    // features 16 g + 8 (lane / 32) .. + 8.  Token fragments come from the
+    // LDS stage; blocks start at multiples of 32 rows, so the swizzled
+    // offset of the lane inside a block depends on the lane and the step
+    // within the stage only.
+    constexpr int KS = kRK / 16;   // 16-feature steps per stage
+    uint32_t lane_off[KS];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            uint32_t alo = (uint32_t)kv[i], ahi = (uint32_t)((uint64_t)kv[i] >> 32);
-            uint32_t blo = (uint32_t)kv[32 + i], bhi = (uint32_t)((uint64_t)kv[32 + i] >> 32);
-            // after the swap, lanes with bit 4 clear hold token i of both
-            // lanes, lanes with bit 4 set token 32 + i of both
-            const auto rl = __builtin_amdgcn_permlane16_swap(alo, blo, false, false);
-            const auto rh = __builtin_amdgcn_permlane16_swap(ahi, bhi, false, false);
-            const int64_t x = (int64_t)(((uint64_t)rh[0] << 32) | rl[0]);
-            const int64_t y = (int64_t)(((uint64_t)rh[1] << 32) | rl[1]);
-            kv[i] = kmax(x, y);
+    for (int ks = 0; ks < KS; ++ks)
+        lane_off[ks] = (uint32_t)((lane & 31) * kRowBytes + chunk_pos<kChunks>(lane & 31, ks * 2 + (lane >> 5)) * 16);
+    bf16x8 af[2][4];
+    auto read_a = [&](int buf, int g) {
+        const char *ab = smem + ((g / KS) % kRStages) * kStageBytes + wm * 128 * kRowBytes + lane_off[g % KS];
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+            af[buf][mi] = *reinterpret_cast<const bf16x8 *>(ab + mi * 32 * kRowBytes);
+    };
+    // Weight fragments go from global memory straight into a ring of kNB
+    // register slots, kNB - 1 steps ahead of their MFMAs: 4 x 16 bytes per
+    // lane per step, one 16-byte load per 32-column block.  The two waves of
+    // a column half load the same rows at about the same time, so the second
+    // load mostly hits the cache.  Padding columns and heads past H read row
+    // 0 (their scores are never used); steps past the last one reload the
+    // last one, so the loads issued never depend on the step count.
+    constexpr int kNB = 8;
+    const int G = D / 16;
+    // One buffer resource over the weights; lane offsets per 32-column
+    // block (column k of head h at ((h * D/8 + lane / 32) * P + k) * 16
+    // bytes), the step's offset in a scalar register (no address arithmetic
+    // per load).  The host keeps the weights below 4 GB.
+    uint32_t boff[4];
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, (uint64_t)a.H * (uint64_t)P * (uint64_t)D * 2u);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+        const int col = wn * 128 + ni * 32 + (lane & 31);
+        const int64_t h = h0 + col / P;
+        const int k = col % P;
+        boff[ni] = (uint32_t)((((h < a.H ? h : 0) * (int64_t)(D / 8) + (lane >> 5)) * P + k) * 16);
+    }
+    constexpr uint32_t kStepBytes = 2u * P * 16u;
+    bf16x8 bq[kNB][4];
+    auto issue_b = [&](int slot, int g) {
+        const uint32_t soff = (uint32_t)min(g, G - 1) * kStepBytes;
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, boff[ni], soff, 0);
+            __builtin_memcpy(&bq[slot][ni], &v, 16);
         }
-        auto level = [&](auto bitc, int n) {
-            constexpr int BIT = decltype(bitc)::value;
-            const bool up = (lane >> BIT) & 1;
+    };
+    auto mfmas = [&](int buf, int slot) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (i < n) {
-                    const int64_t send = up ? kv[i] : kv[n + i];
-                    const int64_t keep = up ? kv[n + i] : kv[i];
-                    kv[i] = kmax(keep, key_across<BIT>(send));
-                }
-            }
-        };
-        level(std::integral_constant<int, 3>{}, 16);
-        level(std::integral_constant<int, 2>{}, 8);
-        level(std::integral_constant<int, 1>{}, 4);
-        level(std::integral_constant<int, 0>{}, 2);
-        if (h < a.H) {
+        for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int c = 2 * (lane & 31) + r, mi = c >> 4, e = c & 15;
-                const int64_t m = m0 + wm * 128 + mi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                if (m < a.M) {
-                    const int64_t b = m / a.L, t = m - b * a.L;
-                    a.sel[(b * a.H + h) * a.L + t] = (int16_t)(255 - (int)(uint32_t)kv[r]);
-                }
+            for (int ni = 0; ni < 4; ++ni)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][mi], bq[slot][ni], acc[mi][ni], 0, 0, 0);
+    };
+
+    // Vector-memory loads of this wave, in issue order: token stages 0 ..
+    // kRStages - 1, weight steps 0 .. kNB - 2, then per step g: in the last
+    // step of stage s (the hand-over) token stage s + kRStages, then the
+    // weights of step g + kNB - 1.  At the hand-over of stage s, token stage
+    // s + 1 has landed once at most kHandWait younger loads are in flight:
+    // at least (R - 2) A + 4 (KS + kNB - 2) loads were issued after it
+    // (s = 0, stage 1 issued before the loop) and 4 (R - 1) KS + (R - 2) A
+    // in the steady state (A = kALoads, R = kRStages); vmcnt counts 63 at
+    // most.  The compiler's own waits before each step's MFMAs count the
+    // weight loads only, which makes them stricter than needed, never
+    // laxer.
+    constexpr int kHandPro = (kRStages - 2) * kALoads + 4 * (KS + kNB - 2);
+    constexpr int kHandSteady = 4 * (kRStages - 1) * KS + (kRStages - 2) * kALoads;
+    constexpr int kHandWait = kHandPro < kHandSteady ? (kHandPro < 63 ? kHandPro : 63)
+                                                     : (kHandSteady < 63 ? kHandSteady : 63);
+    constexpr int kFirstWait = (kRStages - 1) * kALoads + 4 * (kNB - 1);
+    static_assert(kFirstWait < 64, "vmcnt range");
+    // (The scheduling barriers keep the loads in this order: the loop's
+    // waits hold on every path into it only if each slot's loads are as old
+    // on entry as in the steady state.)
+#pragma unroll
+    for (int s = 0; s < kRStages; ++s)
+        issue_a(s);
+#pragma unroll
+    for (int g = 0; g + 1 < kNB; ++g) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_b(g, g);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<kFirstWait>();   // token stage 0
+    __builtin_amdgcn_s_barrier();
+    lds_order();
+    read_a(0, 0);
+
+    // Steps g0 .. g0 + kNB - 1 per group, so that every weight slot has a
+    // fixed register home.  Per step: the weights of step g + kNB - 1 go out,
+    // the token fragments of step g + 1 are read from LDS (after the
+    // hand-over when g + 1 starts a stage), then the MFMAs of step g run.
+    // Only the MFMAs of steps past the last one are skipped (in the one
+    // partial group at the end): every load, read and hand-over is issued on
+    // every path, at clamped addresses, so the compiler's waits count the
+    // loads exactly and never fall back to waiting for all of them.
+    auto group = [&](int g0, auto tailc) {
+        constexpr bool TAIL = decltype(tailc)::value;
+#pragma unroll
+        for (int j = 0; j < kNB; ++j) {
+            const int g = g0 + j;
+            if ((j + 1) % KS == 0) {
+                // Hand-over from stage s = g / KS to stage s + 1: this wave's
+                // reads of stage s are done, stage s + 1 has landed (every
+                // wave's rows of it, after the barrier), and the slot of
+                // stage s is refilled with stage s + R.
+                __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+                wait_vm<kHandWait>();
+                __builtin_amdgcn_s_barrier();
+                lds_order();   // no LDS access moves across the barrier
+                issue_a(g / KS + kRStages);
             }
+            issue_b((j + kNB - 1) % kNB, g + kNB - 1);
+            read_a((j + 1) & 1, g + 1);
+            if (!TAIL || g < G)
+                mfmas(j & 1, j);
+            // The loads and fragment reads go out between the MFMAs (one
+            // wave per SIMD issues everything: clustered, they would leave
+            // the matrix core idle while they issue).
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // vector memory read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    const int g_full = G & ~(kNB - 1);
+    for (int g0 = 0; g0 < g_full; g0 += kNB)
+        group(g0, std::false_type{});
+    if (g_full < G)
+        group(g_full, std::true_type{});
+    // Every load has landed before the epilogue: the weight slots loaded
+    // past the last step are consumed here (so no load is dropped or moved,
+    // and the counts above hold), and the token stages past the last one
+    // finish writing LDS before the workgroup ends.
+#pragma unroll
+    for (int j = 0; j < kNB; ++j)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+            asm volatile("" : : "v"(bq[j][ni]));
+    wait_vm<0>();
+    select_store<P>(acc, a, m0, h0, wm, wn, lane);
+}
+
+// The packed weight layout: wp[h][d/8][k][d%8] = w[h][k][d] for k < K, zero
+// for K <= k < P.  One thread per 16-byte chunk of the output.
+__global__ void __launch_bounds__(256) pack_kernel(const uint4 *__restrict__ w, uint4 *__restrict__ wp, int64_t H,
+                                                   int K, int D, int P)
+{
+    const int64_t n = H * (int64_t)(D / 8) * P;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int k = (int)(i % P);
+        const int64_t r = i / P;
+        const int d8 = (int)(r % (D / 8));
+        const int64_t h = r / (D / 8);
+        wp[i] = k < K ? w[(h * K + k) * (D / 8) + d8] : make_uint4(0u, 0u, 0u, 0u);
     }
 }
 
@@ -419,8 +717,12 @@ extern "C" int pdssm_router_select(const void *u, const void *w, int16_t *sel_ou
     const double m_tiles = (tokens + kRM - 1) / kRM, n_tiles = (double)((H * P + kRN - 1) / kRN);
     if (tokens > 2.0e9 || m_tiles * n_tiles > 2.0e9 || (double)H * K * D > 4.0e18)
         return PDSSM_ERR_DIM;
-    if (flags != 0)
+    if ((flags & ~PDSSM_ROUTER_W_PACKED) != 0)
         return PDSSM_ERR_FLAGS;
+    const bool packed = (flags & PDSSM_ROUTER_W_PACKED) != 0;
+    // Packed weights are addressed by 32-bit byte offsets.
+    if (packed && (double)H * P * D * 2.0 > 4294967295.0)
+        return PDSSM_ERR_DIM;
     if (B == 0 || L == 0 || H == 0)
         return PDSSM_OK;   // no tokens or no heads: nothing to write
     if (!u || !w || !sel_out)
@@ -440,13 +742,44 @@ extern "C" int pdssm_router_select(const void *u, const void *w, int16_t *sel_ou
     a.n_tiles = (uint32_t)((H * P + kRN - 1) / kRN);
     const dim3 grid(a.m_tiles * a.n_tiles), block(kRThreads);
     const bool deep = (D % 64) == 0;
-    if (P == 64 && deep)
-        router_kernel<64, 64><<<grid, block, 0, stream>>>(a);
-    else if (P == 64)
-        router_kernel<64, 32><<<grid, block, 0, stream>>>(a);
-    else if (deep)
-        router_kernel<128, 64><<<grid, block, 0, stream>>>(a);
-    else
-        router_kernel<128, 32><<<grid, block, 0, stream>>>(a);
+    if (packed) {
+        if (P == 64 && deep)
+            router_wreg_kernel<64, 64><<<grid, block, 0, stream>>>(a);
+        else if (P == 64)
+            router_wreg_kernel<64, 32><<<grid, block, 0, stream>>>(a);
+        else if (deep)
+            router_wreg_kernel<128, 64><<<grid, block, 0, stream>>>(a);
+        else
+            router_wreg_kernel<128, 32><<<grid, block, 0, stream>>>(a);
+    } else {
+        if (P == 64 && deep)
+            router_lds_kernel<64, 64><<<grid, block, 0, stream>>>(a);
+        else if (P == 64)
+            router_lds_kernel<64, 32><<<grid, block, 0, stream>>>(a);
+        else if (deep)
+            router_lds_kernel<128, 64><<<grid, block, 0, stream>>>(a);
+        else
+            router_lds_kernel<128, 32><<<grid, block, 0, stream>>>(a);
+    }
+    return hip_status(hipGetLastError());
+}
+
+extern "C" int pdssm_router_pack_weights(const void *w, void *w_packed, int64_t H, int32_t K, int32_t D,
+                                         hipStream_t stream)
+{
+    if (H < 0 || K < 1 || K > 128 || D < 32 || (D % 32) != 0)
+        return PDSSM_ERR_DIM;
+    const int P = K <= 64 ? 64 : 128;
+    if ((double)H * P * D * 2.0 > 4294967295.0)
+        return PDSSM_ERR_DIM;
+    if (H == 0)
+        return PDSSM_OK;
+    if (!w || !w_packed)
+        return PDSSM_ERR_NULL;
+    if (!aligned16(w) || !aligned16(w_packed))
+        return PDSSM_ERR_ALIGN;
+    const int64_t n = H * (int64_t)(D / 8) * P;
+    const unsigned blocks = (unsigned)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
+    pack_kernel<<<blocks, 256, 0, stream>>>(static_cast<const uint4 *>(w), static_cast<uint4 *>(w_packed), H, K, D, P);
     return hip_status(hipGetLastError());
 }

@@ -20,7 +20,8 @@ def test_exports_every_declared_function(lib):
     assert set(names) == {"pdssm_scan_fwd", "pdssm_scan_workspace_bytes", "pdssm_select",
                           "pdssm_compose", "pdssm_strerror", "pdssm_scan_fwd_save",
                           "pdssm_scan_bwd", "pdssm_scan_bwd_workspace_bytes", "pdssm_dict_hardmax",
-                          "pdssm_decode_step", "pdssm_router_select", "pdssm_scan_fwd_noalloc"}
+                          "pdssm_decode_step", "pdssm_router_select", "pdssm_scan_fwd_noalloc",
+                          "pdssm_router_pack_weights"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -226,9 +227,27 @@ def test_router_argument_errors(lib):
                           (2, 100, 3, 0, 256), (2, 100, 3, 129, 256), (2, 100, 3, 64, 0),
                           (2, 100, 3, 64, 48), (2, 100, 3, 64, 16)):
         assert r(FAKE, FAKE, FAKE, B, L, H, K, D, 0, 0) == pk.PDSSM_ERR_DIM, (B, L, H, K, D)
-    assert r(FAKE, FAKE, FAKE, 2, 100, 3, 64, 256, 1, 0) == pk.PDSSM_ERR_FLAGS
+    for flags in (2, 4, 0x80000000, pk.PDSSM_ROUTER_W_PACKED | 2):
+        assert r(FAKE, FAKE, FAKE, 2, 100, 3, 64, 256, flags, 0) == pk.PDSSM_ERR_FLAGS, flags
+    packed = pk.PDSSM_ROUTER_W_PACKED
+    assert r(None, FAKE, FAKE, 2, 100, 3, 64, 256, packed, 0) == pk.PDSSM_ERR_NULL
+    assert r(FAKE, FAKE + 2, FAKE, 2, 100, 3, 64, 256, packed, 0) == pk.PDSSM_ERR_ALIGN
+    # packed weights are addressed by 32-bit offsets: H*P*D*2 bytes below 4 GB
+    assert r(FAKE, FAKE, FAKE, 2, 100, 1024, 128, 16384, packed, 0) == pk.PDSSM_ERR_DIM
     assert r(FAKE + 2, FAKE, FAKE, 2, 100, 3, 64, 256, 0, 0) == pk.PDSSM_ERR_ALIGN
     assert r(FAKE, FAKE, FAKE + 2, 2, 100, 3, 64, 256, 0, 0) == pk.PDSSM_ERR_ALIGN
+
+
+def test_router_pack_argument_errors(lib):
+    p = pk.pdssm_router_pack_weights
+    assert p(None, None, 0, 64, 256, 0) == pk.PDSSM_OK   # no heads: nothing read or written
+    assert p(None, FAKE, 3, 64, 256, 0) == pk.PDSSM_ERR_NULL
+    assert p(FAKE, None, 3, 64, 256, 0) == pk.PDSSM_ERR_NULL
+    for H, K, D in ((-1, 64, 256), (3, 0, 256), (3, 129, 256), (3, 64, 0), (3, 64, 48),
+                    (1024, 128, 16384)):
+        assert p(FAKE, FAKE, H, K, D, 0) == pk.PDSSM_ERR_DIM, (H, K, D)
+    assert p(FAKE + 2, FAKE, 3, 64, 256, 0) == pk.PDSSM_ERR_ALIGN
+    assert p(FAKE, FAKE + 2, 3, 64, 256, 0) == pk.PDSSM_ERR_ALIGN
 
 
 def test_noalloc_rejects_sizes_beyond_its_scratch(lib):

@@ -38,6 +38,15 @@ def orc():
     return oracle.get()
 
 
+# Both weight layouts: [H,K,D] as given, and the packed layout of
+# router_pack_weights (another kernel, the same contract).
+LAYOUTS = ["plain", "packed"]
+
+
+def weights_for(w, layout):
+    return w if layout == "plain" else pk.router_pack_weights(w)
+
+
 def check_choice(u, w, got, ref, lg):
     """got/ref int [B,H,L], lg fp64 scores [B,H,L,K] for the same tokens."""
     uf = u.double().abs().numpy()
@@ -71,11 +80,12 @@ ROUTER_SHAPES = [
 
 
 @pytest.mark.parametrize("B,L,H,K,D", ROUTER_SHAPES)
-def test_router_matches_oracle(orc, B, L, H, K, D):
-    say(f"[case] router B={B} L={L} H={H} K={K} D={D}")
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_router_matches_oracle(orc, layout, B, L, H, K, D):
+    say(f"[case] router {layout} B={B} L={L} H={H} K={K} D={D}")
     u, w = gen.make_router_inputs(B, L, H, K, D, seed=B * 1000 + L + K)
     ref, lg = orc.router_select(u, w, want_logits=True, nthreads=8)
-    got = pk.router_select(u.to(DEV), w.to(DEV))
+    got = pk.router_select(u.to(DEV), weights_for(w.to(DEV), layout))
     torch.cuda.synchronize()
     n = check_choice(u, w, got.cpu().numpy(), ref, lg)
     say(f"  {n} near-tie choices differ from the oracle's of {ref.size}")
@@ -83,27 +93,29 @@ def test_router_matches_oracle(orc, B, L, H, K, D):
 
 @pytest.mark.parametrize("B,L,H,K,D", [(1, 300, 3, 64, 64), (2, 129, 2, 7, 512), (1, 256, 2, 64, 2048),
                                        (1, 300, 3, 128, 64), (2, 129, 3, 97, 512)])
-def test_router_exact_integers(orc, B, L, H, K, D):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_router_exact_integers(orc, layout, B, L, H, K, D):
     """Exact sums: the kernel's index equals the oracle's everywhere (the
     first maximum on ties)."""
-    say(f"[case] router exact B={B} L={L} H={H} K={K} D={D}")
+    say(f"[case] router exact {layout} B={B} L={L} H={H} K={K} D={D}")
     u, w = gen.make_router_inputs(B, L, H, K, D, seed=7 + D, integers=True)
     ref = orc.router_select(u, w, nthreads=8)
-    got = pk.router_select(u.to(DEV), w.to(DEV))
+    got = pk.router_select(u.to(DEV), weights_for(w.to(DEV), layout))
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy(), ref)
 
 
 @pytest.mark.parametrize("B,L,H,K,D", [(1, 300, 3, 64, 64), (2, 129, 3, 40, 96), (1, 200, 2, 100, 128),
                                        (1, 256, 2, 128, 64)])
-def test_router_special_scores(orc, B, L, H, K, D):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_router_special_scores(orc, layout, B, L, H, K, D):
     """Scores that are +-inf, NaN or all zero reach the argmax's rule (NaN
     above every number and the first NaN winning, -0 equal to +0, the first
     maximum on ties): small-integer inputs, with some tokens holding an inf
     (inf * 0 gives NaN), a NaN, both infinities, or nothing but zeros.  Every
     finite sum is exact and inf/NaN arithmetic does not depend on the order
     of the sum, so the index must equal the oracle's everywhere."""
-    say(f"[case] router special scores B={B} L={L} H={H} K={K} D={D}")
+    say(f"[case] router special scores {layout} B={B} L={L} H={H} K={K} D={D}")
     u, w = gen.make_router_inputs(B, L, H, K, D, seed=11 + K + D, integers=True)
     u = u.float()
     g = torch.Generator().manual_seed(5 + K)
@@ -120,21 +132,22 @@ def test_router_special_scores(orc, B, L, H, K, D):
     u[kind == 3] = 0.0
     u = u.to(torch.bfloat16)
     ref = orc.router_select(u, w, nthreads=8)
-    got = pk.router_select(u.to(DEV), w.to(DEV))
+    got = pk.router_select(u.to(DEV), weights_for(w.to(DEV), layout))
     torch.cuda.synchronize()
     got = got.cpu().numpy()
     bad = np.argwhere(got != ref)
     assert bad.size == 0, f"{bad.shape[0]} choices differ, first at {tuple(bad[0])}"
 
 
-def test_router_lm_full_size_sampled(orc):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_router_lm_full_size_sampled(orc, layout):
     """The LM-layer router at full size (B=8 L=4096 H=32 K=64, D=2048): sampled
     tokens against the oracle, including the first and last of several
     256-token tiles."""
     B, L, H, K, D = 8, 4096, 32, 64, 2048
-    say(f"[case] router lm full size B={B} L={L} H={H} K={K} D={D}")
+    say(f"[case] router lm full size {layout} B={B} L={L} H={H} K={K} D={D}")
     u, w = gen.make_router_inputs(B, L, H, K, D, seed=4, device=DEV)
-    got = pk.router_select(u, w)
+    got = pk.router_select(u, weights_for(w, layout))
     torch.cuda.synchronize()
     ts = sorted({0, 1, 255, 256, 257, 511, 1000, 2047, 2048, 3071, 4094, 4095})
     for bi in (0, 5, B - 1):
@@ -143,14 +156,15 @@ def test_router_lm_full_size_sampled(orc):
         check_choice(us, w.cpu(), got[bi:bi + 1][:, :, ts].cpu().numpy(), ref, lg)
 
 
-def test_router_feeds_scan(orc):
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_router_feeds_scan(orc, layout):
     """Router selections drive the scan exactly like the oracle's."""
     inp = gen.make_inputs("lm", B=1, H=4, L=300, seed=91)
     u, w = gen.make_router_inputs(1, 300, 4, 64, 128, seed=92, integers=True)
     inp.sel_or_logits = torch.from_numpy(orc.router_select(u, w)).to(torch.int16)
     inp.sel_mode = gen.SEL_I16
     g = inp.to(DEV)
-    g.sel_or_logits = pk.router_select(u.to(DEV), w.to(DEV))
+    g.sel_or_logits = pk.router_select(u.to(DEV), weights_for(w.to(DEV), layout))
     assert torch.equal(g.sel_or_logits.cpu(), inp.sel_or_logits)
     y, _ = pk.scan(g)
     y_ref, _ = pk.scan(inp.to(DEV))
@@ -158,3 +172,18 @@ def test_router_feeds_scan(orc):
     # the same selections give the same scan, to rounding (the tiles'
     # carries may compose in another order from call to call)
     assert seq_rel_err(y_to_np(y), y_to_np(y_ref)) <= 2.0 ** -7
+
+
+@pytest.mark.parametrize("H,K,D", [(1, 1, 32), (3, 64, 96), (2, 40, 256), (2, 65, 64), (3, 128, 160)])
+def test_router_pack_layout(H, K, D):
+    """The packed layout holds w[h][k][d] at [h][d/8][k][d%8] and zeros in the
+    padding columns K <= k < P, bit for bit (a pure rearrangement)."""
+    say(f"[case] router pack H={H} K={K} D={D}")
+    _, w = gen.make_router_inputs(1, 1, H, K, D, seed=H + K + D)
+    P = 64 if K <= 64 else 128
+    got = pk.router_pack_weights(w.to(DEV))
+    torch.cuda.synchronize()
+    assert got.K == K and tuple(got.data.shape) == (H, D // 8, P, 8)
+    want = torch.zeros(H, D // 8, P, 8, dtype=torch.bfloat16)
+    want[:, :, :K, :] = w.view(H, K, D // 8, 8).permute(0, 2, 1, 3)
+    assert torch.equal(got.data.cpu().view(torch.int16), want.view(torch.int16))
