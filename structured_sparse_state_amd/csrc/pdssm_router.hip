@@ -87,7 +87,8 @@ struct TokenStage {
     static constexpr int kRStages = kRingBytes / kStageBytes;
     static constexpr int kALoads = kRM / kRowsPerLoad / 4;   // direct-to-LDS loads per wave per stage
     static_assert(BK == 32 || BK == 64, "stage depth");
-    static_assert(kRStages >= 3, "the hand-over wait assumes at least three stages in the ring");
+    static constexpr int kGroupStages = 128 / BK;   // stages of 128 features (one hand-over each)
+    static_assert(kRStages == 2 * kGroupStages, "the ring holds two groups of 128 features");
 };
 
 struct RouterArgs {
@@ -593,23 +594,22 @@ __global__ void __launch_bounds__(kRThreads, 1) router_wreg_kernel(RouterArgs a)
                 acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][mi], bq[slot][ni], acc[mi][ni], 0, 0, 0);
     };
 
-    // Vector-memory loads of this wave, in issue order: token stages 0 ..
-    // kRStages - 1, weight steps 0 .. kNB - 2, then per step g: in the last
-    // step of stage s (the hand-over) token stage s + kRStages, then the
-    // weights of step g + kNB - 1.  At the hand-over of stage s, token stage
-    // s + 1 has landed once at most kHandWait younger loads are in flight:
-    // at least (R - 2) A + 4 (KS + kNB - 2) loads were issued after it
-    // (s = 0, stage 1 issued before the loop) and 4 (R - 1) KS + (R - 2) A
-    // in the steady state (A = kALoads, R = kRStages); vmcnt counts 63 at
-    // most.  The compiler's own waits before each step's MFMAs count the
-    // weight loads only, which makes them stricter than needed, never
-    // laxer.
-    constexpr int kHandPro = (kRStages - 2) * kALoads + 4 * (KS + kNB - 2);
-    constexpr int kHandSteady = 4 * (kRStages - 1) * KS + (kRStages - 2) * kALoads;
-    constexpr int kHandWait = kHandPro < kHandSteady ? (kHandPro < 63 ? kHandPro : 63)
-                                                     : (kHandSteady < 63 ? kHandSteady : 63);
-    constexpr int kFirstWait = (kRStages - 1) * kALoads + 4 * (kNB - 1);
-    static_assert(kFirstWait < 64, "vmcnt range");
+    // The token ring holds two groups of 128 features (kNB steps, HS =
+    // kGroupStages stages each); the waves hand over once per group.
+    // Vector-memory loads of this wave, in issue order: groups 0 and 1 of
+    // the token stages, weight steps 0 .. kNB - 2, then per step g: in the
+    // last step of group q (the hand-over) the token stages of group q + 2,
+    // then the weights of step g + kNB - 1.  At the hand-over of group q,
+    // group q + 1 has landed once at most 4 kNB loads are in flight: the
+    // weights of kNB steps were issued after it (q >= 1; for q = 0, 2 kNB - 2
+    // steps' weights).  The compiler's own waits before each step's MFMAs
+    // count the weight loads only, which makes them stricter than needed,
+    // never laxer.
+    constexpr int HS = SG::kGroupStages;
+    static_assert(HS * KS == kNB, "a group of stages is a group of weight slots");
+    constexpr int kHandWait = 4 * kNB;
+    constexpr int kFirstWait = HS * kALoads + 4 * (kNB - 1);   // group 0 landed
+    static_assert(kFirstWait < 64 && kHandWait < 64, "vmcnt range");
     // (The scheduling barriers keep the loads in this order: the loop's
     // waits hold on every path into it only if each slot's loads are as old
     // on entry as in the steady state.)
@@ -622,7 +622,7 @@ __global__ void __launch_bounds__(kRThreads, 1) router_wreg_kernel(RouterArgs a)
         issue_b(g, g);
     }
     __builtin_amdgcn_sched_barrier(0);
-    wait_vm<kFirstWait>();   // token stage 0
+    wait_vm<kFirstWait>();
     __builtin_amdgcn_s_barrier();
     lds_order();
     read_a(0, 0);
@@ -630,7 +630,7 @@ __global__ void __launch_bounds__(kRThreads, 1) router_wreg_kernel(RouterArgs a)
     // Steps g0 .. g0 + kNB - 1 per group, so that every weight slot has a
     // fixed register home.  Per step: the weights of step g + kNB - 1 go out,
     // the token fragments of step g + 1 are read from LDS (after the
-    // hand-over when g + 1 starts a stage), then the MFMAs of step g run.
+    // hand-over when g + 1 starts a group), then the MFMAs of step g run.
     // Only the MFMAs of steps past the last one are skipped (in the one
     // partial group at the end): every load, read and hand-over is issued on
     // every path, at clamped addresses, so the compiler's waits count the
@@ -640,16 +640,18 @@ __global__ void __launch_bounds__(kRThreads, 1) router_wreg_kernel(RouterArgs a)
 #pragma unroll
         for (int j = 0; j < kNB; ++j) {
             const int g = g0 + j;
-            if ((j + 1) % KS == 0) {
-                // Hand-over from stage s = g / KS to stage s + 1: this wave's
-                // reads of stage s are done, stage s + 1 has landed (every
-                // wave's rows of it, after the barrier), and the slot of
-                // stage s is refilled with stage s + R.
+            if (j == kNB - 1) {
+                // Hand-over from group q = g0 / kNB to group q + 1: this
+                // wave's reads of group q are done, group q + 1 has landed
+                // (every wave's rows of it, after the barrier), and the
+                // slots of group q are refilled with group q + 2.
                 __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
                 wait_vm<kHandWait>();
                 __builtin_amdgcn_s_barrier();
                 lds_order();   // no LDS access moves across the barrier
-                issue_a(g / KS + kRStages);
+#pragma unroll
+                for (int t = 0; t < HS; ++t)
+                    issue_a(g0 / KS + t + kRStages);
             }
             issue_b((j + kNB - 1) % kNB, g + kNB - 1);
             read_a((j + 1) & 1, g + 1);
