@@ -161,110 +161,105 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// The epilogue's LDS: per wave, 64 score columns of its 128 tokens, each
+// column 512 bytes plus 16 of padding (so that the 32 columns a store
+// instruction writes fall in different banks).
+constexpr int kEpiColBytes = 128 * 4 + 16;
+constexpr int kEpiWaveBytes = 64 * kEpiColBytes;
+constexpr int kSmemBytes = kRingBytes > 4 * kEpiWaveBytes ? kRingBytes : 4 * kEpiWaveBytes;
+
 // The selection of every token of a wave's 128 x 128 score tile, stored to
 // sel.  acc[mi][ni][e] is the score of token wm*128 + mi*32 + 8*(e/4) +
 // 4*(lane/32) + e%4 and column ni*32 + lane%32 of the wave, i.e. entry k =
-// (ni % NI)*32 + lane%32 of head ni / NI (NI = P / 32).
+// (ni % NI)*32 + lane%32 of head ni / NI (NI = P / 32).  Blocks of 64
+// columns of a head go through the wave's LDS area transposed, so that lane
+// l holds tokens 2l and 2l+1 and scans their scores in index order: a later
+// score replaces the best only when it is larger (the first maximum stays;
+// -0 and +0 compare equal).  A token whose block holds a NaN (its sum is
+// then NaN, as it is with +inf beside -inf) has the block scanned again by
+// value keys, which put a NaN above every number (the first NaN winning);
+// later blocks win over earlier ones only with a larger key.  The caller
+// has finished every other use of smem.
 template <int P>
 __device__ __forceinline__ void select_store(const f32x16 (&acc)[4][4], const RouterArgs &a, int64_t m0,
-                                             int64_t h0, int wm, int wn, int lane)
+                                             int64_t h0, int wm, int wn, int wave, int lane, char *smem)
 {
     constexpr int HW = 128 / P;   // heads per wave
     constexpr int NI = P / 32;    // 32-column MFMA tiles per head
     const int K = a.K;
-    // Argmax per token over the head's K scores.  Each lane first keeps the
-    // best of its NI entries for
-    // each of its 64 tokens (c = mi*16 + e), comparing value keys in index
-    // order with a strict comparison (the lower index stays on a tie), and
-    // joins the winner's index into a 64-bit key; then the 32 lanes of each
-    // half-wave reduce by recursive halving: at the exchange across lane bit
-    // b, a lane keeps the half of its tokens that its bit selects and takes
-    // its partner's keys of that half, so after five exchanges lane l holds
-    // the result of tokens c = 2 (l % 32) and 2 (l % 32) + 1.  The exchange
-    // across bit 4 is one v_permlane16_swap per register (odd and even rows
-    // trade halves), the others DPP moves; the max over keys is associative
-    // and commutative, so the pairing order does not matter.
-    // Padding columns (entry k >= K) exist only when K < P (one wave-uniform
-    // branch); their scores are then replaced by kNoValue.
-    const bool padded = K < P;
-    bool col_ok[NI];
-#pragma unroll
-    for (int t = 0; t < NI; ++t)
-        col_ok[t] = t * 32 + (lane & 31) < K;
+    char *const wb = smem + wave * kEpiWaveBytes;
+    const int wr = (lane & 31) * kEpiColBytes + 16 * (lane >> 5);   // column lane%32, tokens 4 (lane/32) + ...
+    const int rd = 8 * lane;                                        // tokens 2 lane, 2 lane + 1
 #pragma unroll
     for (int hn = 0; hn < HW; ++hn) {
         const int64_t h = h0 + wn * HW + hn;
-        int64_t kv[64];
-        auto in_lane = [&](auto padc) {
-            constexpr bool PAD = decltype(padc)::value;
+        int32_t best_key[2] = {0, 0};
+        int best_k[2] = {0, 0};
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi) {
+        for (int ps = 0; ps < P / 64; ++ps) {
+            // columns (2 ps + t2) * 32 + lane % 32 of the head, t2 = 0, 1
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    int32_t best = value_key(acc[mi][hn * NI][e]);
-                    if constexpr (PAD)
-                        best = col_ok[0] ? best : kNoValue;
-                    int bt = 0;
+            for (int t2 = 0; t2 < 2; ++t2) {
+                const int ni = hn * NI + 2 * ps + t2;
 #pragma unroll
-                    for (int t = 1; t < NI; ++t) {
-                        int32_t v = value_key(acc[mi][hn * NI + t][e]);
-                        if constexpr (PAD)
-                            v = col_ok[t] ? v : kNoValue;
-                        const bool take = v > best;
-                        best = take ? v : best;
-                        bt = take ? t : bt;
+                for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 v = make_float4(acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2],
+                                                     acc[mi][ni][4 * q + 3]);
+                        *reinterpret_cast<float4 *>(wb + t2 * 32 * kEpiColBytes + wr + (mi * 32 + 8 * q) * 4) = v;
                     }
-                    kv[mi * 16 + e] = join_key(best, bt * 32 + (lane & 31));
-                }
             }
-        };
-        if (padded)
-            in_lane(std::true_type{});
-        else
-            in_lane(std::false_type{});
-        // bit 4: lanes l and l ^ 16 (odd and even rows)
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            uint32_t alo = (uint32_t)kv[i], ahi = (uint32_t)((uint64_t)kv[i] >> 32);
-            uint32_t blo = (uint32_t)kv[32 + i], bhi = (uint32_t)((uint64_t)kv[32 + i] >> 32);
-            // after the swap, lanes with bit 4 clear hold token i of both
-            // lanes, lanes with bit 4 set token 32 + i of both
-            const auto rl = __builtin_amdgcn_permlane16_swap(alo, blo, false, false);
-            const auto rh = __builtin_amdgcn_permlane16_swap(ahi, bhi, false, false);
-            const int64_t x = (int64_t)(((uint64_t)rh[0] << 32) | rl[0]);
-            const int64_t y = (int64_t)(((uint64_t)rh[1] << 32) | rl[1]);
-            kv[i] = kmax(x, y);
+            const int k0 = ps * 64;
+            const int nk = min(K - k0, 64);   // >= 1: P = 128 only when K > 64
+            float bv0 = -__builtin_inff(), bv1 = -__builtin_inff(), s0 = 0.f, s1 = 0.f;
+            int bk0 = k0, bk1 = k0;
+#pragma unroll 8
+            for (int c = 0; c < nk; ++c) {
+                const float2 v = *reinterpret_cast<const float2 *>(wb + c * kEpiColBytes + rd);
+                const bool t0 = v.x > bv0, t1 = v.y > bv1;
+                bv0 = t0 ? v.x : bv0;
+                bk0 = t0 ? k0 + c : bk0;
+                bv1 = t1 ? v.y : bv1;
+                bk1 = t1 ? k0 + c : bk1;
+                s0 += v.x;
+                s1 += v.y;
+            }
+            int32_t key0 = value_key(bv0), key1 = value_key(bv1);
+            if (__builtin_amdgcn_ballot_w64(s0 != s0 || s1 != s1) != 0) {
+                int32_t q0 = kNoValue, q1 = kNoValue;
+                for (int c = 0; c < nk; ++c) {
+                    const float2 v = *reinterpret_cast<const float2 *>(wb + c * kEpiColBytes + rd);
+                    const int32_t v0 = value_key(v.x), v1 = value_key(v.y);
+                    bk0 = v0 > q0 ? k0 + c : bk0;
+                    q0 = v0 > q0 ? v0 : q0;
+                    bk1 = v1 > q1 ? k0 + c : bk1;
+                    q1 = v1 > q1 ? v1 : q1;
+                }
+                key0 = q0;
+                key1 = q1;
+            }
+            if (ps == 0 || key0 > best_key[0]) {
+                best_key[0] = key0;
+                best_k[0] = bk0;
+            }
+            if (ps == 0 || key1 > best_key[1]) {
+                best_key[1] = key1;
+                best_k[1] = bk1;
+            }
         }
-        auto level = [&](auto bitc, int n) {
-            constexpr int BIT = decltype(bitc)::value;
-            const bool up = (lane >> BIT) & 1;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (i < n) {
-                    const int64_t send = up ? kv[i] : kv[n + i];
-                    const int64_t keep = up ? kv[n + i] : kv[i];
-                    kv[i] = kmax(keep, key_across<BIT>(send));
-                }
-            }
-        };
-        level(std::integral_constant<int, 3>{}, 16);
-        level(std::integral_constant<int, 2>{}, 8);
-        level(std::integral_constant<int, 1>{}, 4);
-        level(std::integral_constant<int, 0>{}, 2);
         if (h < a.H) {
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
-                const int c = 2 * (lane & 31) + r, mi = c >> 4, e = c & 15;
-                const int64_t m = m0 + wm * 128 + mi * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int64_t m = m0 + wm * 128 + 2 * lane + r;
                 if (m < a.M) {
                     const int64_t b = m / a.L, t = m - b * a.L;
-                    a.sel[(b * a.H + h) * a.L + t] = (int16_t)(255 - (int)(uint32_t)kv[r]);
+                    a.sel[(b * a.H + h) * a.L + t] = (int16_t)best_k[r];
                 }
             }
         }
     }
 }
-
 
 // Weights [H][K][D].  P: padded score columns per head (64 or 128); a
 // wave's 128 columns hold 128 / P heads.
@@ -276,7 +271,7 @@ __global__ void __launch_bounds__(kRThreads, 1) router_lds_kernel(RouterArgs a)
                   kRowsPerLoad = SG::kRowsPerLoad, kABytes = SG::kABytes, kStageBytes = SG::kStageBytes,
                   kRStages = SG::kRStages, kALoads = SG::kALoads, kBLoads = SG::kBLoads,
                   kLoadsPerStage = SG::kLoadsPerStage;
-    __shared__ __attribute__((aligned(1024))) char smem[kRingBytes];
+    __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
@@ -464,7 +459,12 @@ __global__ void __launch_bounds__(kRThreads, 1) router_lds_kernel(RouterArgs a)
             }
         }
     }
-    select_store<P>(acc, a, m0, h0, wm, wn, lane);
+    // Every wave is past its last fragment read before the epilogue reuses
+    // the ring.
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    lds_order();
+    select_store<P>(acc, a, m0, h0, wm, wn, wave, lane, smem);
 }
 
 // Packed weights [H][D/8][P][8].  P: score columns per head (64 or 128); a
@@ -476,7 +476,7 @@ __global__ void __launch_bounds__(kRThreads, 1) router_wreg_kernel(RouterArgs a)
     constexpr int kRK = SG::kRK, kRowBytes = SG::kRowBytes, kChunks = SG::kChunks,
                   kRowsPerLoad = SG::kRowsPerLoad, kStageBytes = SG::kStageBytes, kRStages = SG::kRStages,
                   kALoads = SG::kALoads;
-    __shared__ __attribute__((aligned(1024))) char smem[kRingBytes];
+    __shared__ __attribute__((aligned(1024))) char smem[kSmemBytes];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
@@ -686,7 +686,12 @@ __global__ void __launch_bounds__(kRThreads, 1) router_wreg_kernel(RouterArgs a)
         for (int ni = 0; ni < 4; ++ni)
             asm volatile("" : : "v"(bq[j][ni]));
     wait_vm<0>();
-    select_store<P>(acc, a, m0, h0, wm, wn, lane);
+    // Every wave's loads into the ring have landed and every wave is past
+    // its last fragment read before the epilogue reuses the ring.
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    lds_order();
+    select_store<P>(acc, a, m0, h0, wm, wn, wave, lane, smem);
 }
 
 // The packed weight layout: wp[h][d/8][k][d%8] = w[h][k][d] for k < K, zero
