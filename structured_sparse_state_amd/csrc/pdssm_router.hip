@@ -51,9 +51,8 @@ constexpr int kRThreads = 256;
 constexpr int kRingBytes = 128 * 1024;   // LDS ring of every stage depth
 
 // router_lds_kernel's LDS stage of BK features of token and weight rows: 64
-// (two stages in the ring) when the feature
-// count allows it, else 32 (four stages).  Deeper stages mean fewer stage
-// hand-overs (barriers) per MFMA.
+// (two stages in the ring) when the feature count allows it, else 32 (four
+// stages).  Deeper stages mean fewer stage hand-overs (barriers) per MFMA.
 template <int BK>
 struct PairStage {
     static constexpr int kRK = BK;                      // features per LDS stage
