@@ -424,23 +424,11 @@ __global__ void __launch_bounds__(kRThreads, 1) router_lds_kernel(RouterArgs a)
                     issue(ring + (s % kRStages) * kStageBytes, (s + kRStages) * kRK);
                 read_frags(buf ^ 1, ring + ((s + 1) % kRStages) * kStageBytes, 0);
             }
-            if constexpr (P == 64) {
-                // The next fragments' reads go out between this step's
-                // MFMAs (clustered, they would leave the matrix core idle
-                // while they issue).  With 128 columns per head the
-                // epilogue's registers do not leave room for it.
-                mfmas(buf);
-                interleave_reads();
-            } else {
-                // Keep the next fragments' reads (and the stage hand-over)
-                // ahead of this step's MFMAs, so their latency runs under
-                // the MFMAs still queued from the step before.
-                __builtin_amdgcn_sched_barrier(0);
-                mfmas(buf);
-                // and keep the hand-over's wait for this wave's reads after
-                // the MFMAs that run while those reads land
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            // The next fragments' reads go out between this step's MFMAs
+            // (clustered, they would leave the matrix core idle while they
+            // issue).
+            mfmas(buf);
+            interleave_reads();
         }
     }
     {
@@ -449,13 +437,8 @@ __global__ void __launch_bounds__(kRThreads, 1) router_lds_kernel(RouterArgs a)
         for (int ks = 0; ks < KS; ++ks) {
             if (ks + 1 < KS)
                 read_frags((ks & 1) ^ 1, cur, ks + 1);
-            if constexpr (P == 64) {
-                mfmas(ks & 1);
-                interleave_reads();
-            } else {
-                __builtin_amdgcn_sched_barrier(0);
-                mfmas(ks & 1);
-            }
+            mfmas(ks & 1);
+            interleave_reads();
         }
     }
     // Every wave is past its last fragment read before the epilogue reuses
