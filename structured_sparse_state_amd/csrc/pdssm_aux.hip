@@ -21,50 +21,67 @@ namespace pdssm {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Column-wise hardmax.  One wave per matrix, lane j = column j: rows are read
-// in order (a row of N values is contiguous, so each read is one coalesced
-// row), every lane keeping its column's running argmax under the selection's
-// rule (first maximum, NaN above every number).  Rows are fetched kHmRows at
-// a time so that several loads are in flight per wave.
+// Column-wise hardmax.  One workgroup per matrix, lane j = column j; the
+// kHmWaves waves take consecutive blocks of at most kHmRows rows (a row of N
+// values is contiguous, so each read is one coalesced row) and issue all of
+// their rows' loads at once.  Each wave keeps its columns' running argmax
+// over its rows in order under the selection's rule (first maximum, NaN
+// above every number); the first wave then merges the waves' results in
+// row order under the same rule, which keeps the first maximum over the
+// whole column.
 // ---------------------------------------------------------------------------
 constexpr int kHmWaves = 4;
-#ifndef PDSSM_HM_ROWS
-#define PDSSM_HM_ROWS 16
-#endif
-constexpr int kHmRows = PDSSM_HM_ROWS;
+constexpr int kHmRows = 16;   // rows per wave: N <= 64
+static_assert(kHmWaves * kHmRows >= 64, "the waves cover every row");
 
 template <bool BF16>
 __global__ void __launch_bounds__(kHmWaves * 64) hardmax_kernel(const void *__restrict__ m,
                                                                int32_t *__restrict__ out, int64_t mats,
                                                                int N)
 {
+    __shared__ float s_v[kHmWaves][64];
+    __shared__ int s_k[kHmWaves][64];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t mat = (int64_t)blockIdx.x * kHmWaves + wave;
-    if (mat >= mats)
-        return;
     const int col = min(lane, N - 1);
-    const int64_t base = mat * (int64_t)N * N + col;
-    auto value = [&](int r) -> float {
-        const int64_t e = base + (int64_t)r * N;
-        if constexpr (BF16)
-            return bf16_lo(reinterpret_cast<const uint16_t *>(m)[e]);
-        else
-            return reinterpret_cast<const float *>(m)[e];
-    };
-    float bv = value(0);
-    int bk = 0;
-    for (int r0 = 1; r0 < N; r0 += kHmRows) {
-        float v[kHmRows];
+    const int rows = (N + kHmWaves - 1) / kHmWaves;   // <= kHmRows
+    const int r0 = wave * rows, r1 = min(N, r0 + rows);
+    // Matrices blockIdx.x, + gridDim.x, ... (the whole workgroup loops).
+    for (int64_t mat = blockIdx.x; mat < mats; mat += gridDim.x) {
+        const int64_t base = mat * (int64_t)N * N + col;
+        auto value = [&](int r) -> float {
+            const int64_t e = base + (int64_t)r * N;
+            if constexpr (BF16)
+                return bf16_lo(reinterpret_cast<const uint16_t *>(m)[e]);
+            else
+                return reinterpret_cast<const float *>(m)[e];
+        };
+        float bv = 0.f;
+        int bk = -1;   // no rows in this wave's block
+        if (r0 < r1) {
+            float v[kHmRows];
 #pragma unroll
-        for (int u = 0; u < kHmRows; ++u)
-            v[u] = value(min(r0 + u, N - 1));
+            for (int u = 0; u < kHmRows; ++u)
+                v[u] = value(min(r0 + u, r1 - 1));
+            bv = v[0];
+            bk = r0;
 #pragma unroll
-        for (int u = 0; u < kHmRows; ++u)
-            if (r0 + u < N)
-                argmax_take(v[u], r0 + u, bv, bk);
+            for (int u = 1; u < kHmRows; ++u)
+                if (r0 + u < r1)
+                    argmax_take(v[u], r0 + u, bv, bk);
+        }
+        s_v[wave][lane] = bv;
+        s_k[wave][lane] = bk;
+        __syncthreads();
+        if (wave == 0) {
+#pragma unroll
+            for (int w = 1; w < kHmWaves; ++w)
+                if (s_k[w][lane] >= 0)
+                    argmax_take(s_v[w][lane], s_k[w][lane], bv, bk);
+            if (lane < N)
+                out[mat * N + lane] = bk;
+        }
+        __syncthreads();   // the merge has read s_v, s_k before the next matrix
     }
-    if (lane < N)
-        out[mat * N + lane] = bk;
 }
 
 // ---------------------------------------------------------------------------
@@ -170,7 +187,9 @@ extern "C" int pdssm_dict_hardmax(const void *m, int32_t *dict_idx, int64_t H, i
     if (!aligned16(m) || !aligned16(dict_idx))
         return PDSSM_ERR_ALIGN;
     const int64_t mats = H * (int64_t)K;
-    const dim3 grid((unsigned)((mats + kHmWaves - 1) / kHmWaves)), block(kHmWaves * 64);
+    // One workgroup per matrix (at most 2^20 workgroups, each then taking
+    // several matrices).
+    const dim3 grid((unsigned)(mats < (1 << 20) ? mats : (1 << 20))), block(kHmWaves * 64);
     if (mode == PDSSM_LOGITS_BF16)
         hipLaunchKernelGGL(hardmax_kernel<true>, grid, block, 0, stream, m, dict_idx, mats, (int)N);
     else

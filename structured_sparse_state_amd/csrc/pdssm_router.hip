@@ -115,13 +115,11 @@ __device__ __forceinline__ int chunk_pos(int r, int c)
         return c ^ ((r ^ ((r >> 3) & 3)) & 7);
 }
 
-// The selection's order (the score, then the lower index; -0 equal to +0; a
-// NaN above every number, the first NaN winning) in integers.  value_key maps
-// the score's bits to an int32 that orders like the value (negative values
-// have their magnitude bits flipped, -0 is made +0 first, every NaN becomes
-// INT32_MAX); join_key puts it in the high word of a signed 64-bit key and
-// 255 - k in the low word.  The larger key wins, so a max over joined keys
-// is the argmax with ties to the lowest index.
+// The selection's order on values (-0 equal to +0; a NaN above every number)
+// in integers: value_key maps the score's bits to an int32 that orders like
+// the value (negative values have their magnitude bits flipped, -0 is made
+// +0 first, every NaN becomes INT32_MAX).  A strict comparison of keys in
+// index order then keeps the first maximum, and the first NaN.
 __device__ __forceinline__ int32_t value_key(float v)
 {
     const float f = v + 0.0f;   // -0 + 0 = +0 (round to nearest); NaN stays NaN
@@ -129,28 +127,8 @@ __device__ __forceinline__ int32_t value_key(float v)
     const int32_t key = i ^ ((i >> 31) & 0x7fffffff);
     return (f != f) ? 0x7fffffff : key;
 }
-// A padding column's value key: below the key of every score (-inf's is
-// INT32_MIN + 0x7fffff).
+// Below the key of every score (-inf's is INT32_MIN + 0x7fffff).
 constexpr int32_t kNoValue = INT32_MIN;
-__device__ __forceinline__ int64_t join_key(int32_t vkey, int k)
-{
-    return (int64_t)(((uint64_t)(uint32_t)vkey << 32) | (uint32_t)(255 - k));
-}
-__device__ __forceinline__ int64_t kmax(int64_t a, int64_t b) { return a > b ? a : b; }
-
-// The partner's 64-bit value across lane bit BIT (0..3) inside a row of 16
-// lanes (DPP moves of both halves).  For bit 2 the partner is the mirror lane
-// 7-i, which differs in bit 2 and keeps bits >= 3: for a reduction that
-// later combines across bits 1 and 0, every lane still meets all eight.
-template <int BIT>
-__device__ __forceinline__ int64_t key_across(int64_t v)
-{
-    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)((uint64_t)v >> 32);
-    constexpr int CTRL = BIT == 3 ? 0x128 : BIT == 2 ? 0x141 : BIT == 1 ? 0x4E : 0xB1;
-    const int plo = __builtin_amdgcn_update_dpp(0, lo, CTRL, 0xF, 0xF, false);
-    const int phi = __builtin_amdgcn_update_dpp(0, hi, CTRL, 0xF, 0xF, false);
-    return (int64_t)(((uint64_t)(uint32_t)phi << 32) | (uint32_t)plo);
-}
 
 // s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
 template <int N>
