@@ -76,6 +76,13 @@ ROUTER_SHAPES = [
     (2, 300, 3, 100, 256),
     (1, 257, 2, 128, 512),
     (1, 513, 5, 65, 96),
+    # feature counts that leave a partial last group of 128 features (8
+    # steps), wrap the two-group token ring many times, or take 32-feature
+    # stages
+    (1, 260, 3, 64, 224),
+    (1, 130, 2, 40, 4064),
+    (2, 70, 2, 128, 4096),
+    (1, 300, 9, 16, 1056),
 ]
 
 
