@@ -158,11 +158,14 @@ def measure_aux(pk, gen, inp, stream, workload):
     t_hm = _event_time(lambda: pk.dict_hardmax(m, stream=stream, out=dct), 50, 5, stream)
     hm_bytes = m.numel() * m.element_size() + dct.numel() * dct.element_size()
 
+    # Copies (clone), not views: with B = H = 1 a step's slice is already
+    # contiguous, and its address would be that of the step inside the
+    # sequence, which the library's 16-byte alignment rule rejects.
     if inp.sel_mode.startswith("sel"):
-        sel = inp.sel_or_logits[:, :, 0].contiguous()
+        sel = inp.sel_or_logits[:, :, 0].clone()
     else:
-        sel = inp.sel_or_logits[:, :, 0, :].contiguous()
-    d, b, c = (t[:, :, 0].contiguous() for t in (inp.diag, inp.b, inp.c))
+        sel = inp.sel_or_logits[:, :, 0, :].clone()
+    d, b, c = (t[:, :, 0].clone() for t in (inp.diag, inp.b, inp.c))
     x = torch.zeros((B, H, N, 2) if inp.complex else (B, H, N), device=dev, dtype=torch.float32)
     y = torch.empty((B, H), device=dev, dtype=torch.bfloat16 if inp.y_bf16 else torch.float32)
 
@@ -178,10 +181,10 @@ def measure_aux(pk, gen, inp, stream, workload):
     T_win = min(64, inp.L)
     win = []
     for t in range(T_win):
-        ws_ = (inp.sel_or_logits[:, :, t].contiguous() if inp.sel_mode.startswith("sel")
-               else inp.sel_or_logits[:, :, t, :].contiguous())
-        win.append((ws_, inp.diag[:, :, t].contiguous(), inp.b[:, :, t].contiguous(),
-                    inp.c[:, :, t].contiguous(), torch.empty_like(y)))
+        ws_ = (inp.sel_or_logits[:, :, t].clone() if inp.sel_mode.startswith("sel")
+               else inp.sel_or_logits[:, :, t, :].clone())
+        win.append((ws_, inp.diag[:, :, t].clone(), inp.b[:, :, t].clone(),
+                    inp.c[:, :, t].clone(), torch.empty_like(y)))
     xw = x.clone()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
