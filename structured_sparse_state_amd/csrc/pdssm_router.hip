@@ -10,26 +10,28 @@
 // As a matrix product: C[M, H*P] = U[M, D] * W^T with M = B*L tokens and each
 // head's K weight rows padded to P = 64 or 128 columns.  It is a dense
 // contraction, so it runs on the matrix cores: v_mfma_f32_32x32x16_bf16,
-// fp32 accumulation.  A workgroup computes a 256-token x 256-column tile
-// (256/P heads); each of its four waves owns 128 tokens x 128 columns
-// (4 x 4 MFMA tiles, 256 accumulators, one wave per SIMD), so every head's
-// scores stay inside one wave and each fragment feeds four MFMAs.  With one
-// wave per SIMD nothing else hides latency, so the loops are
+// fp32 accumulation.  Each of a workgroup's four waves owns 128 tokens x 128
+// columns (4 x 4 MFMA tiles, 256 accumulators, one wave per SIMD), so every
+// head's scores stay inside one wave and each fragment feeds four MFMAs.
+// With one wave per SIMD nothing else hides latency, so the loops are
 // software-pipelined: the fragments of the next 16 features are read while
 // the MFMAs of the current ones run.
 //
 // Two kernels, by the layout of the weights:
-//   * [H][K][D] (router_lds_kernel): token rows and weight rows both go
-//     straight from global memory into a ring of LDS stages
-//     (global_load_lds, 16 bytes per lane, whole 128-byte lines per load).
-//     Per 16 features a CU then writes 16 KB and reads 32 KB of LDS, more
-//     than the LDS delivers in the MFMAs' time, which bounds this kernel.
+//   * [H][K][D] (router_lds_kernel): a workgroup tile of 256 tokens x 256
+//     columns, waves 2 x 2.  Token rows and weight rows both go straight
+//     from global memory into a ring of LDS stages (global_load_lds, 16
+//     bytes per lane, whole 128-byte lines per load).  Per 16 features a CU
+//     then writes 16 KB and reads 32 KB of LDS, more than the LDS delivers
+//     in the MFMAs' time, which bounds this kernel.
 //   * packed, [H][D/8][P][8] (router_wreg_kernel; pdssm_router_pack_weights
-//     writes it): token rows go through LDS as above, the weight fragments
-//     straight into a ring of registers.  In this layout the 32 columns of a
-//     fragment are 512 contiguous bytes per 8 features, so a fragment load
-//     touches whole lines (in [H][K][D] it would touch 32 rows), and the LDS
-//     carries 8 KB of writes and 16 KB of reads per 16 features.
+//     writes it): a workgroup tile of 128 tokens x 512 columns, so the four
+//     waves share one set of token rows, which go through LDS as above, and
+//     each loads its own weight fragments straight into a ring of
+//     registers.  In this layout the 32 columns of a fragment are 512
+//     contiguous bytes per 8 features, so a fragment load touches whole
+//     lines (in [H][K][D] it would touch 32 rows).  Per 16 features a CU
+//     then writes 4 KB and reads 16 KB of LDS and loads 16 KB of weights.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -45,8 +47,10 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kRM = 256;     // tokens per workgroup tile
-constexpr int kRN = 256;     // score columns per workgroup tile
+constexpr int kRM = 256;     // router_lds_kernel: tokens per workgroup tile
+constexpr int kRN = 256;     // and score columns (waves 2 x 2)
+constexpr int kWM = 128;     // router_wreg_kernel: tokens per workgroup tile
+constexpr int kWN = 512;     // and score columns (waves 1 x 4)
 constexpr int kRThreads = 256;
 constexpr int kRingBytes = 128 * 1024;   // LDS ring of every stage depth
 
@@ -72,19 +76,20 @@ struct PairStage {
     static_assert(kLoadsPerStage * 3 < 64, "vmcnt range");
 };
 
-// router_wreg_kernel's LDS stage of BK features of the token rows: 64 when
-// the feature count allows it, else 32.  The weight rows do not pass through
-// LDS (each wave loads its own fragments into registers), so the ring holds
-// token rows only: four 64-feature stages or eight 32-feature ones.
+// router_wreg_kernel's LDS stage of BK features of its 128 token rows: 64
+// when the feature count allows it, else 32.  The weight rows do not pass
+// through LDS (each wave loads its own fragments into registers), so the
+// ring holds token rows only: two groups of 128 features, four 64-feature
+// stages or eight 32-feature ones (64 KB).
 template <int BK>
 struct TokenStage {
     static constexpr int kRK = BK;                      // features per LDS stage
     static constexpr int kRowBytes = BK * 2;            // bytes of one row of a stage
     static constexpr int kChunks = BK / 8;              // 16-byte chunks per row
     static constexpr int kRowsPerLoad = 64 / kChunks;   // rows one 64-lane 16-byte load fills
-    static constexpr int kStageBytes = kRM * kRowBytes;   // token rows per stage
-    static constexpr int kRStages = kRingBytes / kStageBytes;
-    static constexpr int kALoads = kRM / kRowsPerLoad / 4;   // direct-to-LDS loads per wave per stage
+    static constexpr int kStageBytes = kWM * kRowBytes;   // token rows per stage
+    static constexpr int kRStages = 2 * (128 / BK);      // two groups of 128 features
+    static constexpr int kALoads = kWM / kRowsPerLoad / 4;   // direct-to-LDS loads per wave per stage
     static_assert(BK == 32 || BK == 64, "stage depth");
     static constexpr int kGroupStages = 128 / BK;   // stages of 128 features (one hand-over each)
     static_assert(kRStages == 2 * kGroupStages, "the ring holds two groups of 128 features");
@@ -448,8 +453,8 @@ __global__ void __launch_bounds__(kRThreads, 1) router_wreg_kernel(RouterArgs a)
     const uint32_t bx = blockIdx.x;
     const uint32_t tile = (bx < per * 8) ? (bx % 8) * per + bx / 8 : bx;
     const uint32_t mt = tile / a.n_tiles, nt = tile % a.n_tiles;
-    const int64_t m0 = (int64_t)mt * kRM;
-    const int64_t h0 = (int64_t)nt * (kRN / P);
+    const int64_t m0 = (int64_t)mt * kWM;
+    const int64_t h0 = (int64_t)nt * (kWN / P);
     const int D = a.D;
 
     // Token rows go straight from global memory into LDS (global_load_lds):
@@ -486,8 +491,9 @@ __global__ void __launch_bounds__(kRThreads, 1) router_wreg_kernel(RouterArgs a)
             dma(asrc[j] + k0, base + (uint32_t)((wave * kALoads + j) * 1024));
     };
 
-    // This wave: tokens wm*128 .. +128 of the tile, columns wn*128 .. +128.
-    const int wm = wave >> 1, wn = wave & 1;
+    // This wave: the tile's 128 tokens (all four waves), columns wn*128 ..
+    // +128.
+    const int wm = 0, wn = wave;
     f32x16 acc[4][4];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
@@ -516,11 +522,10 @@ __global__ void __launch_bounds__(kRThreads, 1) router_wreg_kernel(RouterArgs a)
     };
     // Weight fragments go from global memory straight into a ring of kNB
     // register slots, kNB - 1 steps ahead of their MFMAs: 4 x 16 bytes per
-    // lane per step, one 16-byte load per 32-column block.  The two waves of
-    // a column half load the same rows at about the same time, so the second
-    // load mostly hits the cache.  Padding columns and heads past H read row
-    // 0 (their scores are never used); steps past the last one reload the
-    // last one, so the loads issued never depend on the step count.
+    // lane per step, one 16-byte load per 32-column block; the four waves
+    // load disjoint columns.  Padding columns and heads past H read row 0
+    // (their scores are never used); steps past the last one reload the last
+    // one, so the loads issued never depend on the step count.
     constexpr int kNB = 8;
     const int G = D / 16;
     // One buffer resource over the weights; lane offsets per 32-column
@@ -707,9 +712,13 @@ extern "C" int pdssm_router_select(const void *u, const void *w, int16_t *sel_ou
     a.D = D;
     a.m_tiles = (uint32_t)((a.M + kRM - 1) / kRM);
     a.n_tiles = (uint32_t)((H * P + kRN - 1) / kRN);
-    const dim3 grid(a.m_tiles * a.n_tiles), block(kRThreads);
+    dim3 grid(a.m_tiles * a.n_tiles), block(kRThreads);
     const bool deep = (D % 64) == 0;
     if (packed) {
+        // tiles of 128 tokens x 512 columns
+        a.m_tiles = (uint32_t)((a.M + kWM - 1) / kWM);
+        a.n_tiles = (uint32_t)((H * P + kWN - 1) / kWN);
+        grid = dim3(a.m_tiles * a.n_tiles);
         if (P == 64 && deep)
             router_wreg_kernel<64, 64><<<grid, block, 0, stream>>>(a);
         else if (P == 64)
