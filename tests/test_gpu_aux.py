@@ -59,6 +59,18 @@ def test_dict_hardmax(orc, H, K, N, bf16, ties, specials):
     assert np.array_equal(got.cpu().numpy(), ref)
 
 
+def test_dict_hardmax_many_matrices(orc):
+    """More matrices than the kernel's 2^20 workgroups: each workgroup takes
+    several (2M matrices of 8 x 8, ties and -0/+0/NaN entries)."""
+    H, K, N = 2048, 1024, 8
+    say(f"[case] hardmax many matrices H={H} K={K} N={N}")
+    m = oracle_pins.hardmax_matrices(H, K, N, bf16=False, seed=4242, ties=True, specials=True)
+    ref = orc.dict_hardmax(m)
+    got = pk.dict_hardmax(m.to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
 def test_dict_hardmax_drives_scan(orc):
     """Maps from the GPU hardmax run the scan like the oracle's maps."""
     inp = gen.make_inputs("tiny", B=2, H=3, L=200, N=16, K=6, seed=77)
