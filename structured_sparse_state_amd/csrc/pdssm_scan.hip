@@ -90,7 +90,13 @@ constexpr int kDictLdsMax = 32768;   // bytes of the head's entry table kept in 
 #define PDSSM_CARRY_NAP 4
 #endif
 #ifndef PDSSM_CARRY_PRIO
-#define PDSSM_CARRY_PRIO 2   // s_setprio level of the carry wave (chunk waves stay at 0)
+#define PDSSM_CARRY_PRIO 2   // s_setprio level of the carry wave and of the chunk waves' chain
+#endif
+// The chunk waves' s_setprio level during their local pass (0 in the other
+// phases): the waves of a CU's workgroups are in different phases at any
+// time, and those in the local pass, which saturates the LDS, go first.
+#ifndef PDSSM_LOCAL_PRIO
+#define PDSSM_LOCAL_PRIO 1
 #endif
 
 __host__ __device__ constexpr int scan_tile_steps(int NP) { return kScanW * (64 / NP) * kScanT; }
@@ -744,6 +750,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             return *reinterpret_cast<const uint16_t *>(tbp + tt * NP * 2);
         };
         uint32_t ent_next = entry(0);
+        __builtin_amdgcn_s_setprio(PDSSM_LOCAL_PRIO);
 #pragma unroll
         for (int tt = 0; tt < T; ++tt) {
             const uint32_t ent = ent_next;
@@ -847,6 +854,7 @@ __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<NP, CPLX, BCBF>()))) scan_k
             keep_here(gr[T - 1], gi[T - 1]);
         }
 
+        __builtin_amdgcn_s_setprio(0);
         // ---- The chunk's operator (pi, d, e) = (pacc, dacc, x) for the carry wave.
         // The local part of the readout, summed over the group's rows now
         // (the sum is linear, so the carry's part is summed on its own).
