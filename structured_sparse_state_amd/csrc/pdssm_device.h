@@ -755,17 +755,26 @@ __device__ __forceinline__ bool slot_rank_ovf(uint32_t slot) { return slot >= kT
 
 // The 16-bit entry of source `lane` for the index map row[0..N):
 //   pi | scatter block << 6 | read block << (6 + kBlockBits) | (deg > R) << kDegOvfBit.
-// Called by a whole wave (lanes >= N are padding sources that map to
-// themselves with rank 0 and in-degree 1); entries outside [0,N) clamp.
+// Called by a wave whose lanes [0, N) are all active (lanes >= N are padding
+// sources that map to themselves with rank 0 and in-degree 1); entries
+// outside [0,N) clamp.  The rank is the number of lower sources with the same
+// destination, the in-degree the number of sources whose destination is this
+// lane.  Both come from six ballots, one per bit of a destination: the lanes
+// that agree with a value on every bit are the AND, over the bits, of the
+// ballot or its complement.
 __device__ __forceinline__ uint16_t dict_entry(const int32_t *row, int N, int lane)
 {
     const int pi = lane < N ? (int)min((unsigned)row[lane], (unsigned)(N - 1)) : lane;
-    int rank = 0, deg = 0;
-    for (int jj = 0; jj < N; ++jj) {
-        const int pj = __builtin_amdgcn_readlane(pi, jj);
-        rank += (jj < lane && pj == pi) ? 1 : 0;
-        deg += (pj == lane) ? 1 : 0;
+    const uint64_t real = N >= 64 ? ~0ull : ((1ull << N) - 1ull);
+    uint64_t same = real, into = real;
+#pragma unroll
+    for (int bit = 0; bit < 6; ++bit) {
+        const uint64_t m = __ballot((pi >> bit) & 1);
+        same &= ((pi >> bit) & 1) ? m : ~m;
+        into &= ((lane >> bit) & 1) ? m : ~m;
     }
+    const int rank = __popcll(same & ((1ull << lane) - 1ull));
+    int deg = __popcll(into);
     if (lane >= N)
         deg = 1;   // padding rows hold their own (zero) state
     const int block = rank < kRegions ? kRegions - 1 - rank : rank == kRegions ? 2 * kRegions : 2 * kRegions + 1;
