@@ -132,6 +132,22 @@ def test_shapes(orc, N, L, K, mode, cplx, bcbf, ybf):
         run_and_compare(orc, inp, f"shape N={N} L={L} K={K} x0={with_x0}")
 
 
+@pytest.mark.parametrize("N", [8, 20, 64])
+def test_dictionary_collisions(orc, N):
+    """Index maps at the extremes of the scatter entries: every source into
+    state 0 (in-degree N, ranks 0..N-1), every source into the last state,
+    half of them into one state beside a fixed half, and an iid map."""
+    inp = gen.make_inputs("tiny", B=2, H=3, L=900, N=N, K=4, sel_mode=gen.SEL_I32, complex=True,
+                          dmin=0.5, dmax=0.7, seed=77 + N)
+    d = inp.dict_idx
+    half = N // 2
+    d[:, 0, :] = 0
+    d[:, 1, :] = N - 1
+    d[:, 2, :] = torch.arange(N, dtype=torch.int32)
+    d[:, 2, :half] = half
+    run_and_compare(orc, inp, f"collisions N={N}")
+
+
 @pytest.mark.parametrize("N,mode", [(5, gen.LOGITS_F32), (8, gen.SEL_I32), (16, gen.LOGITS_BF16)])
 def test_many_tiles_per_workgroup(orc, N, mode):
     """Several times more tiles than resident workgroups, so every workgroup
